@@ -1,0 +1,43 @@
+"""CPU oracle for heavy-hitter KV-cache eviction fused into decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+CPU-baseline leg may import or run anything in this package.  The GPU library
+never imports it, links it or falls back to it, and this package imports
+nothing from the GPU library: the two share no code.  Both sides take their
+inputs from the seeded generators in ``workloads``, which hold none of the
+method's arithmetic.
+
+Everything here is plain numpy in float64 on the exact storage-dtype input
+values (upcast), written step by step in the order the pages state the
+method:
+
+* ``attention`` - softmax attention (textbook definition).
+* ``h2o``       - H2O heavy-hitter scoring, prefill selection and the greedy
+                  per-step eviction with a recent window; also the
+                  Scissorhands fixed-budget reading (same loop).
+* ``fastgen``   - FastGen's per-head policies: full cache, local window,
+                  special+punctuation tokens, frequency (H2O) + local.
+* ``hashevict`` - HashEvict's sign sketches, Hamming ranking, prompt replay
+                  and pre-attention replacement.
+* ``lockstep``  - replays a unit against a GPU run's logs with the near-tie
+                  acceptance band, and measures the score and output errors.
+
+Sources (cited per function):
+  [H2O]  review page of "H2O: Heavy-Hitter Oracle for Efficient Generative
+         Inference of Large Language Models" (nubint.ai), sections
+         "研究の動機と目的" (motivation), "提案手法" (proposed method).
+  [FG]   review page of "Model Tells You What to Discard: Adaptive KV Cache
+         Compression for LLMs" (FastGen, nubint.ai): Abstract, "提案手法",
+         Figure 2 caption.
+  [SH]   summary page of "Scissorhands: Exploiting the Persistence of
+         Importance Hypothesis for LLM KV Cache Compression at Test Time"
+         (fugumt.com): Abstract.
+  [HE]   summary page of "HashEvict: A Pre-Attention KV Cache Eviction
+         Strategy using Locality-Sensitive Hashing" (jarxiv.com): 要約 and
+         the original abstract.
+
+Parity pins: every function is pinned by a CPU test against a textbook
+routine, a closed form, an invariant or brute force (tests/test_oracle_*.py).
+Parity unpinned: the H2O score trajectory for generic inputs beyond those
+invariants and brute-force checks -- the pages print no worked example.
+"""

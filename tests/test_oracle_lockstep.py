@@ -1,0 +1,106 @@
+"""Self-tests of the lockstep checker: it must accept the oracle's own run, accept an
+in-band near-tie (and count it), and reject a wrong victim, a perturbed score and a
+perturbed output (CPU only)."""
+
+import numpy as np
+
+from oracle import h2o, hashevict, lockstep
+from tests.test_oracle_h2o import rand_qkv
+
+P, T, D, HH, R, SC = 40, 30, 16, 6, 6, 0.25
+
+
+def oracle_as_gpu():
+    Q, K, V = rand_qkv(77, P + T, D, heavy_pos=7)
+    tr = h2o.run_unit(Q, K, V, P, HH, R, SC)
+    g = lockstep.GpuUnit(prefill_pos=tr.prefill_kept.copy(), evicted=tr.evicted.copy(),
+                         out=tr.out.copy(), final_pos=tr.final.pos.copy(),
+                         prefill_S=tr.prefill_scores.copy(), final_S=tr.final.S.copy())
+    return (Q, K, V), tr, g
+
+
+def test_oracle_log_passes():
+    (Q, K, V), tr, g = oracle_as_gpu()
+    rep = lockstep.check_h2o(Q, K, V, P, HH, R, SC, g)
+    assert rep.ok, rep.failures
+    assert rep.adopted == 0 and rep.decisions == T
+
+
+def test_wrong_victim_fails():
+    (Q, K, V), tr, g = oracle_as_gpu()
+    s = 5
+    t = P + s
+    _, A, S_A = None, None, None
+    # replay to step s to find a candidate that is clearly not minimal
+    cache = h2o.Cache(tr.prefill_kept.copy(), tr.prefill_scores.copy())
+    for k in range(s + 1):
+        _, A, S_A = h2o.attend_step(cache, P + k, Q[P + k], K, V, SC)
+        i = h2o.h2o_victim(A, S_A, P + k, R)
+        if k < s:
+            cache = h2o.remove(A, S_A, i)
+    cand = h2o.h2o_candidates(A, t, R)
+    worst = cand[np.argmax(S_A[cand])]
+    assert S_A[worst] > S_A[i] * (1 + 1e-3)
+    g.evicted[s] = A[worst]
+    rep = lockstep.check_h2o(Q, K, V, P, HH, R, SC, g)
+    assert not rep.ok
+    assert any(f.startswith(f"step {s}:") for f in rep.failures)
+
+
+def test_perturbed_score_fails():
+    (Q, K, V), tr, g = oracle_as_gpu()
+    g.final_S[3] *= 1 + 2e-5
+    assert not lockstep.check_h2o(Q, K, V, P, HH, R, SC, g).ok
+    (Q, K, V), tr, g = oracle_as_gpu()
+    g.prefill_S[0] *= 1 - 2e-5
+    assert not lockstep.check_h2o(Q, K, V, P, HH, R, SC, g).ok
+
+
+def test_perturbed_output_fails():
+    (Q, K, V), tr, g = oracle_as_gpu()
+    g.out[7, 2] += 3e-3 * np.max(np.abs(tr.out[7]))
+    rep = lockstep.check_h2o(Q, K, V, P, HH, R, SC, g)
+    assert not rep.ok and any("output" in f for f in rep.failures)
+    (Q, K, V), tr, g = oracle_as_gpu()
+    g.out[7, 2] += 1e-3 * np.max(np.abs(tr.out[7]))
+    assert lockstep.check_h2o(Q, K, V, P, HH, R, SC, g).ok
+
+
+def test_near_tie_victim_is_accepted_far_one_is_not():
+    A = np.array([2, 5, 8, 11])
+    S = np.array([0.30, 0.30000001, 0.2, 0.9])
+    cand = np.array([0, 1, 2])           # position 11 is in the recent window
+    i_ref = 2
+    assert not lockstep.accept_h2o_victim(A, S, cand, i_ref, 5)
+    S2 = np.array([0.30, 0.2 * (1 + 5e-7), 0.2, 0.9])
+    assert lockstep.accept_h2o_victim(A, S2, cand, i_ref, 5)
+    assert not lockstep.accept_h2o_victim(A, S2, cand, i_ref, 11)   # recent: never admissible
+    assert not lockstep.accept_h2o_victim(A, S2, cand, i_ref, 99)   # not in the cache
+
+
+def test_prefill_near_tie_set_is_adopted():
+    c = np.array([0.9, 0.5, 0.5 * (1 + 3e-7), 0.1, 0.2, 0.3, 0.4])
+    # candidates [0, 5); heavy 2 -> oracle keeps 0 and 2; GPU keeps 0 and 1 (in band)
+    rep = lockstep.UnitReport()
+    kept = lockstep.check_prefill_set(rep, c, np.array([0, 1, 5, 6]), heavy=2, recent=2)
+    assert rep.ok and rep.adopted == 1 and kept.tolist() == [0, 1, 5, 6]
+    rep = lockstep.UnitReport()
+    lockstep.check_prefill_set(rep, c, np.array([0, 4, 5, 6]), heavy=2, recent=2)
+    assert not rep.ok
+
+
+def test_hash_checker_accepts_oracle_and_rejects_wrong_victim():
+    Pq, Tq, B = 30, 20, 10
+    Q, K, V = rand_qkv(5, Pq + Tq, 16)
+    W = np.random.default_rng(3).standard_normal((16, 32))
+    tr = hashevict.run_unit(Q, K, V, W, Pq, B, 0.25)
+    g = lockstep.GpuUnit(prefill_pos=tr.prefill_kept, evicted=tr.evicted.copy(), out=tr.out,
+                         final_pos=tr.final_kept)
+    assert lockstep.check_hash(Q, K, V, W, Pq, B, 0.25, g).ok
+    # pick a cached position at a strictly smaller distance than the maximum at step 0
+    cache = hashevict.replay_prompt(tr.qsk, tr.ksk, Pq, B)
+    h = hashevict.hamming(np.uint64(tr.qsk[Pq]), tr.ksk[cache])
+    near = cache[np.argmin(h)]
+    assert h.min() < h.max()
+    g.evicted[0] = near
+    assert not lockstep.check_hash(Q, K, V, W, Pq, B, 0.25, g).ok
