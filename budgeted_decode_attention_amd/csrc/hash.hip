@@ -1,0 +1,307 @@
+// HashEvict (summary page, original abstract): keys are tracked by sign
+// sketches of a Gaussian projection far narrower than the head dimension,
+// kept as a small binary structure in GPU memory; before attention, the new
+// token replaces the cached token whose sketch is farthest (Hamming distance)
+// from the query's sketch -- the one expected to receive the least attention.
+//
+// Sketch bit b of x is set iff the exact sum_i W[i][b] x[i] is positive.  The
+// products of bf16 W with bf16/fp16/fp32 inputs are exact in float64; their
+// float64 sum is within gamma_d * sum|terms| of the exact value, so the sign
+// is taken from it unless |sum| is inside that bound, in which case the terms
+// are re-added exactly as a non-overlapping expansion (two-sum chains).
+//
+// Ties in distance go to the oldest position.  The prompt is replayed: the
+// cache starts as positions [0, B) and each prompt position i >= B replaces
+// the farthest key from sketch(q_i).
+#include "common.hpp"
+
+namespace kve {
+namespace {
+
+constexpr int kNT = 256;
+constexpr int kMaxBits = 32;
+
+template <int DT> __device__ inline float load_elem(const char* row, int i);
+template <> __device__ inline float load_elem<F32>(const char* row, int i) {
+  return reinterpret_cast<const float*>(row)[i];
+}
+template <> __device__ inline float load_elem<BF16>(const char* row, int i) {
+  return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[i] << 16);
+}
+template <> __device__ inline float load_elem<F16>(const char* row, int i) {
+  return (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(row)[i]);
+}
+
+__device__ inline double bf16_to_double(uint16_t w) { return (double)__uint_as_float((uint32_t)w << 16); }
+
+// Exact sign of sum_i a_i b_i (each product exact in float64), by growing a
+// zero-free non-overlapping expansion with two-sum.  Rarely taken.
+template <int DT, int D>
+__device__ __attribute__((noinline)) int exact_sign(const char* row, const uint16_t* W, int bits, int b) {
+  double e[D + 1];
+  int len = 0;
+  for (int i = 0; i < D; ++i) {
+    double q = (double)load_elem<DT>(row, i) * bf16_to_double(W[i * bits + b]);
+    int k = 0;
+    for (int j = 0; j < len; ++j) {
+      const double s = q + e[j];
+      const double bv = s - q;
+      const double av = s - bv;
+      const double err = (q - av) + (e[j] - bv);
+      q = s;
+      if (err != 0.0) e[k++] = err;
+    }
+    if (q != 0.0) e[k++] = q;
+    len = k;
+  }
+  if (len == 0) return 0;
+  return e[len - 1] > 0.0 ? 1 : 0;   // the largest component carries the sign
+}
+
+// Sign bit b of a row: float64 dot with the error bound, exact fallback.
+template <int DT, int D>
+__device__ inline int sketch_bit(const char* row, const uint16_t* W, int bits, int b) {
+  double s = 0.0, a = 0.0;
+#pragma unroll 8
+  for (int i = 0; i < D; ++i) {
+    const double x = (double)load_elem<DT>(row, i);
+    const double w = bf16_to_double(W[i * bits + b]);
+    s = fma(x, w, s);
+    a = fma(fabs(x), fabs(w), a);
+  }
+  // |s - exact| <= gamma_D * sum|terms|; sum|terms| itself is computed with a
+  // relative error below gamma_D, so gamma_{2D+2} bounds the comparison.
+  constexpr double u = 1.1102230246251565e-16;
+  constexpr double g = (2 * D + 2) * u / (1.0 - (2 * D + 2) * u);
+  if (fabs(s) > g * a) return s > 0.0 ? 1 : 0;
+  return exact_sign<DT, D>(row, W, bits, b);
+}
+
+// One 32-lane half-wave per row; the lane index is the bit.
+template <int DT, int D>
+__global__ __launch_bounds__(kNT) void sketch_rows_kernel(Shape sh, UnitList ul, const void* x, int P, int row0,
+                                                          int nrows, const uint16_t* proj, uint32_t* out) {
+  constexpr int ES = elem_bytes<DT>();
+  const int u = ul.ids ? ul.ids[blockIdx.y] : blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int half = lane >> 5;
+  const int b = lane & 31;
+  const int r = (blockIdx.x * kNT + threadIdx.x) / 32;   // row index within [0, nrows)
+  const bool ok = r < nrows;
+  int bit = 0;
+  if (ok) {
+    const char* row = (const char*)x + ((size_t)u * P + row0 + r) * D * ES;
+    bit = sketch_bit<DT, D>(row, proj, kMaxBits, b);
+  }
+  const uint64_t m = __ballot(bit != 0);
+  if (ok && b == 0) out[(size_t)u * P + row0 + r] = (uint32_t)(m >> (32 * half));
+}
+
+// Prompt replay for one HASH unit per workgroup; slot state in LDS.
+template <int DT, int D>
+__global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c, UnitList ul, int P,
+                                                          const uint32_t* qsk, const uint32_t* ksk,
+                                                          const void* k, const void* v) {
+  constexpr int EPL = St<DT>::EPL;
+  constexpr int ES = elem_bytes<DT>();
+  constexpr int LPR = D / EPL;
+  constexpr int RPI = kNT / LPR;
+  extern __shared__ uint32_t lds[];          // sk[B] then pos[B]
+  __shared__ uint64_t kscr[kNT / kWave];
+  const int u = ul.ids[blockIdx.x];
+  const int tid = threadIdx.x;
+  const HeadMeta m = c.meta[u % sh.heads];
+  const int B = m.heavy;
+  const int n0 = min(P, B);
+  uint32_t* ssk = lds;
+  int32_t* spos = reinterpret_cast<int32_t*>(lds + B);
+  const uint32_t* kq = ksk + (size_t)u * P;
+  const uint32_t* qq = qsk + (size_t)u * P;
+  for (int s = tid; s < n0; s += kNT) {
+    ssk[s] = kq[s];
+    spos[s] = s;
+  }
+  __syncthreads();
+  // key = distance << 48 | (2^24 - 1 - position) << 24 | slot: the maximum is
+  // the farthest key, then the oldest position
+  for (int i = B; i < P; ++i) {
+    const uint32_t qs = qq[i];
+    uint64_t best = 0;
+    for (int s = tid; s < B; s += kNT) {
+      const uint64_t key = ((uint64_t)__popc(qs ^ ssk[s]) << 48) |
+                           ((uint64_t)(0xFFFFFF - spos[s]) << 24) | (uint64_t)s;
+      best = key > best ? key : best;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t ot = __shfl_xor(best, o);
+      best = ot > best ? ot : best;
+    }
+    if ((tid & (kWave - 1)) == 0) kscr[tid / kWave] = best;
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t bb = kscr[0];
+#pragma unroll
+      for (int w = 1; w < kNT / kWave; ++w) bb = kscr[w] > bb ? kscr[w] : bb;
+      const int slot = (int)(bb & 0xFFFFFF);
+      ssk[slot] = kq[i];
+      spos[slot] = i;
+    }
+    __syncthreads();
+  }
+  const size_t slot0 = (size_t)u * c.cap;
+  for (int s = tid; s < c.cap; s += kNT) {
+    int32_t p = -1;
+    uint32_t sk = 0u;
+    if (s < n0) {
+      p = spos[s];
+      sk = ssk[s];
+    }
+    c.pos[slot0 + s] = p;
+    c.sk[slot0 + s] = sk;
+    c.S[slot0 + s] = 0.0;
+  }
+  if (tid == 0) c.count[u] = n0;
+  // gather
+  const size_t src0 = (size_t)u * P * D * ES;
+  char* Kd = (char*)c.K + slot0 * D * ES;
+  char* Vd = (char*)c.V + slot0 * D * ES;
+  const int col = tid % LPR;
+  for (int s = tid / LPR; s < n0; s += RPI) {
+    const size_t so = ((size_t)spos[s] * D + col * EPL) * ES;
+    const size_t dof = ((size_t)s * D + col * EPL) * ES;
+    st16(Kd + dof, ld16((const char*)k + src0 + so));
+    st16(Vd + dof, ld16((const char*)v + src0 + so));
+  }
+}
+
+// Decode-time replacement for one HASH unit per workgroup.
+template <int DT, int D>
+__global__ __launch_bounds__(kNT) void hash_evict_kernel(Shape sh, LayerCache c, UnitList ul, int t,
+                                                         const void* q, const void* k, const void* v,
+                                                         int32_t* evicted) {
+  constexpr int EPL = St<DT>::EPL;
+  constexpr int ES = elem_bytes<DT>();
+  constexpr int LPR = D / EPL;
+  __shared__ uint32_t sk2[2];
+  __shared__ uint64_t kscr[kNT / kWave];
+  const int u = ul.ids[blockIdx.x];
+  const int tid = threadIdx.x;
+  const HeadMeta m = c.meta[u % sh.heads];
+  const int B = m.heavy;
+  // wave 0: lanes 0-31 sketch q, lanes 32-63 sketch k
+  if (tid < kWave) {
+    const int half = tid >> 5;
+    const char* row = (const char*)(half ? k : q) + (size_t)u * D * ES;
+    const int bit = sketch_bit<DT, D>(row, c.proj, kMaxBits, tid & 31);
+    const uint64_t msk = __ballot(bit != 0);
+    if (tid == 0) {
+      sk2[0] = (uint32_t)msk;
+      sk2[1] = (uint32_t)(msk >> 32);
+    }
+  }
+  __syncthreads();
+  const size_t slot0 = (size_t)u * c.cap;
+  const int n = c.count[u];
+  int slot, ev;
+  if (n >= B) {
+    const uint32_t qs = sk2[0];
+    uint64_t best = 0;
+    for (int s = tid; s < n; s += kNT) {
+      const uint64_t key = ((uint64_t)__popc(qs ^ c.sk[slot0 + s]) << 48) |
+                           ((uint64_t)(0xFFFFFF - c.pos[slot0 + s]) << 24) | (uint64_t)s;
+      best = key > best ? key : best;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t ot = __shfl_xor(best, o);
+      best = ot > best ? ot : best;
+    }
+    if ((tid & (kWave - 1)) == 0) kscr[tid / kWave] = best;
+    __syncthreads();
+    uint64_t bb = kscr[0];
+#pragma unroll
+    for (int w = 1; w < kNT / kWave; ++w) bb = kscr[w] > bb ? kscr[w] : bb;
+    slot = (int)(bb & 0xFFFFFF);
+    ev = 0xFFFFFF - (int)((bb >> 24) & 0xFFFFFF);
+  } else {
+    slot = n;
+    ev = -1;
+  }
+  __syncthreads();
+  char* Kd = (char*)c.K + (slot0 + slot) * D * ES;
+  char* Vd = (char*)c.V + (slot0 + slot) * D * ES;
+  if (tid < LPR) {
+    st16(Kd + tid * EPL * ES, ld16((const char*)k + ((size_t)u * D + tid * EPL) * ES));
+    st16(Vd + tid * EPL * ES, ld16((const char*)v + ((size_t)u * D + tid * EPL) * ES));
+  }
+  if (tid == 0) {
+    c.pos[slot0 + slot] = t;
+    c.sk[slot0 + slot] = sk2[1];
+    c.S[slot0 + slot] = 0.0;
+    if (slot == n) c.count[u] = n + 1;
+    if (evicted) evicted[u] = ev;
+  }
+}
+
+#define KVE_DISPATCH(FN, ...)                                                   \
+  switch (sh.dtype * 1000 + sh.d) {                                              \
+    case F32 * 1000 + 64: return FN<F32, 64>(__VA_ARGS__);                       \
+    case F32 * 1000 + 128: return FN<F32, 128>(__VA_ARGS__);                     \
+    case F16 * 1000 + 64: return FN<F16, 64>(__VA_ARGS__);                       \
+    case F16 * 1000 + 128: return FN<F16, 128>(__VA_ARGS__);                     \
+    case BF16 * 1000 + 64: return FN<BF16, 64>(__VA_ARGS__);                     \
+    case BF16 * 1000 + 128: return FN<BF16, 128>(__VA_ARGS__);                   \
+  }                                                                              \
+  return hipErrorInvalidValue;
+
+template <int DT, int D>
+hipError_t sketch_t(const Shape& sh, UnitList ul, const void* x, int P, int row0, int nrows,
+                    const uint16_t* proj, uint32_t* out, hipStream_t st) {
+  if (nrows <= 0 || ul.n <= 0) return hipSuccess;
+  dim3 grid((nrows * 32 + kNT - 1) / kNT, ul.n);
+  hipLaunchKernelGGL((sketch_rows_kernel<DT, D>), grid, dim3(kNT), 0, st, sh, ul, x, P, row0, nrows, proj, out);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t replay_t(const Shape& sh, const LayerCache& c, UnitList ul, int P, const uint32_t* qsk,
+                    const uint32_t* ksk, const void* k, const void* v, int B, hipStream_t st) {
+  if (ul.n <= 0) return hipSuccess;
+  const size_t lds = (size_t)B * 8;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)hash_replay_kernel<DT, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((hash_replay_kernel<DT, D>), dim3(ul.n), dim3(kNT), lds, st, sh, c, ul, P, qsk, ksk, k, v);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t evict_t(const Shape& sh, const LayerCache& c, UnitList ul, int t, const void* q, const void* k,
+                   const void* v, int32_t* evicted, hipStream_t st) {
+  if (ul.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL((hash_evict_kernel<DT, D>), dim3(ul.n), dim3(kNT), 0, st, sh, c, ul, t, q, k, v, evicted);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sketch_rows(const Shape& sh, UnitList units, const void* x, int P, int row0, int nrows,
+                              const uint16_t* proj, uint32_t* out, hipStream_t st) {
+  KVE_DISPATCH(sketch_t, sh, units, x, P, row0, nrows, proj, out, st)
+}
+
+hipError_t launch_hash_prefill(const Shape& sh, const LayerCache& c, UnitList units, int P, int max_budget,
+                               const uint32_t* qsk, const uint32_t* ksk, const void* k, const void* v,
+                               hipStream_t st) {
+  KVE_DISPATCH(replay_t, sh, c, units, P, qsk, ksk, k, v, max_budget, st)
+}
+
+hipError_t launch_hash_evict(const Shape& sh, const LayerCache& c, UnitList units, int t, const void* q,
+                             const void* k, const void* v, int32_t* evicted, hipStream_t st) {
+  KVE_DISPATCH(evict_t, sh, c, units, t, q, k, v, evicted, st)
+}
+
+}  // namespace kve

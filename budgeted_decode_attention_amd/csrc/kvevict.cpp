@@ -1,0 +1,414 @@
+// libkvevict host side: argument validation, workspace layout, per-layer
+// state and kernel dispatch behind the C ABI declared in include/kvevict.h.
+//
+// The library allocates no device memory.  Everything lives in the caller's
+// workspace, carved in a fixed order by Plan below; kvevict_workspace_size and
+// kvevict_create run the same plan so their layouts always agree.
+#include "kvevict.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kve_status fail(kve_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kve_status fail(kve_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+constexpr int kMaxContext = 32768;     // LDS-resident per-unit slot lists
+constexpr int kMaxHashBudget = 16384;  // replay keeps sketches and positions in LDS
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_size(int dtype) { return dtype == KVE_F32 ? 4 : 2; }
+
+int head_capacity(int policy, int heavy, int recent, int max_context) {
+  switch (policy) {
+    case KVE_H2O: return heavy + recent;
+    case KVE_LOCAL: return recent;
+    case KVE_HASH: return heavy;
+    default: return max_context;       // FULL, SPECIAL
+  }
+}
+
+// Per-layer summary of the head table.
+struct LayerInfo {
+  int cap = 0;
+  bool any_h2o = false, any_hash = false, any_special = false;
+  int max_hash_budget = 0;
+  std::vector<int32_t> h2o_units, hash_units;
+};
+
+kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
+  if (!c) return fail(KVE_EINVAL, "config is null");
+  if (c->layers < 1 || c->batch < 1 || c->heads < 1)
+    return fail(KVE_EINVAL, "layers, batch and heads must be >= 1");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(KVE_EUNSUPPORTED, "head_dim %d not built (64 or 128)", c->head_dim);
+  if (c->dtype != KVE_F32 && c->dtype != KVE_F16 && c->dtype != KVE_BF16)
+    return fail(KVE_EINVAL, "dtype %d unknown", c->dtype);
+  if (c->max_context < 1 || c->max_context > kMaxContext)
+    return fail(KVE_EUNSUPPORTED, "max_context %d outside [1, %d]", c->max_context, kMaxContext);
+  if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale))
+    return fail(KVE_EINVAL, "softmax_scale must be finite and >= 0");
+  if (!c->policy || !c->heavy || !c->recent) return fail(KVE_EINVAL, "policy/heavy/recent tables are null");
+  const long long units = (long long)c->batch * c->heads;
+  if (units > (1 << 24)) return fail(KVE_EUNSUPPORTED, "more than 2^24 units per layer");
+  info->assign(c->layers, LayerInfo());
+  bool need_bitmap = false, need_proj = false;
+  for (int l = 0; l < c->layers; ++l) {
+    LayerInfo& li = (*info)[l];
+    for (int h = 0; h < c->heads; ++h) {
+      const int i = l * c->heads + h;
+      const int p = c->policy[i], hv = c->heavy[i], rc = c->recent[i];
+      switch (p) {
+        case KVE_H2O:
+          if (hv < 0 || rc < 0 || hv + rc < 1)
+            return fail(KVE_EINVAL, "layer %d head %d: H2O needs heavy, recent >= 0 and heavy + recent >= 1", l, h);
+          if (hv + rc > c->max_context)
+            return fail(KVE_EINVAL, "layer %d head %d: heavy + recent exceeds max_context", l, h);
+          li.any_h2o = true;
+          break;
+        case KVE_LOCAL:
+          if (hv != 0 || rc < 1 || rc > c->max_context)
+            return fail(KVE_EINVAL, "layer %d head %d: LOCAL needs heavy = 0 and 1 <= recent <= max_context", l, h);
+          break;
+        case KVE_HASH:
+          if (rc != 0 || hv < 1 || hv > std::min(c->max_context, kMaxHashBudget))
+            return fail(KVE_EINVAL, "layer %d head %d: HASH needs recent = 0 and 1 <= budget <= %d", l, h,
+                        std::min(c->max_context, kMaxHashBudget));
+          li.any_hash = true;
+          li.max_hash_budget = std::max(li.max_hash_budget, hv);
+          need_proj = true;
+          break;
+        case KVE_FULL:
+        case KVE_SPECIAL:
+          if (hv != 0 || rc != 0)
+            return fail(KVE_EINVAL, "layer %d head %d: FULL/SPECIAL take heavy = recent = 0", l, h);
+          if (p == KVE_SPECIAL) {
+            li.any_special = true;
+            need_bitmap = true;
+          }
+          break;
+        default:
+          return fail(KVE_EINVAL, "layer %d head %d: policy %d unknown", l, h, p);
+      }
+      li.cap = std::max(li.cap, head_capacity(p, hv, rc, c->max_context));
+    }
+    for (int b = 0; b < c->batch; ++b)
+      for (int h = 0; h < c->heads; ++h) {
+        const int p = c->policy[l * c->heads + h];
+        if (p == KVE_H2O) li.h2o_units.push_back(b * c->heads + h);
+        if (p == KVE_HASH) li.hash_units.push_back(b * c->heads + h);
+      }
+  }
+  if (need_bitmap && (!c->keep_token_bitmap || c->vocab < 1))
+    return fail(KVE_EINVAL, "SPECIAL heads need keep_token_bitmap and vocab >= 1");
+  if (need_proj && (!c->lsh_proj_bf16 || c->sketch_bits != 32))
+    return fail(KVE_EUNSUPPORTED, "HASH heads need lsh_proj_bf16 and sketch_bits = 32");
+  return KVE_OK;
+}
+
+// Workspace layout.  With base == nullptr only sizes are accumulated.
+struct Plan {
+  char* base;
+  size_t off = 0;
+  explicit Plan(void* b) : base((char*)b) {}
+  template <class T> T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off = align_up(off + count * sizeof(T));
+    return p;
+  }
+};
+
+struct Layer {
+  kve::LayerCache cache{};
+  LayerInfo info;
+  kve::UnitList h2o{nullptr, 0}, hash{nullptr, 0};
+  int position = -1;   // next decode position; -1 before prefill
+};
+
+}  // namespace
+
+struct kve_ctx {
+  kve_config cfg{};
+  kve::Shape shape{};
+  std::vector<Layer> layers;
+  kve::HeadMeta* meta = nullptr;       // device [layers][heads]
+  uint32_t* bitmap = nullptr;          // device
+  uint16_t* proj = nullptr;            // device [layers][d][32]
+  float* lse = nullptr;                // device [U][max_context][2]
+  double* colsum = nullptr;            // device [U][max_context]
+  uint32_t* qsk = nullptr;             // device [U][max_context]
+  uint32_t* ksk = nullptr;             // device [U][max_context]
+  bool sync_check = false;
+};
+
+namespace {
+
+size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* base, kve_ctx* ctx) {
+  Plan pl(base);
+  const size_t U = (size_t)c->batch * c->heads;
+  const size_t d = c->head_dim, es = elem_size(c->dtype);
+  const size_t N = c->max_context;
+  bool any_hash = false, any_special = false;
+  for (const auto& li : info) {
+    any_hash |= li.any_hash;
+    any_special |= li.any_special;
+  }
+  auto* meta = pl.take<kve::HeadMeta>((size_t)c->layers * c->heads);
+  auto* bitmap = any_special ? pl.take<uint32_t>(((size_t)c->vocab + 31) / 32) : nullptr;
+  auto* proj = any_hash ? pl.take<uint16_t>((size_t)c->layers * d * 32) : nullptr;
+  auto* lse = pl.take<float>(U * N * 2);
+  auto* colsum = pl.take<double>(U * N);
+  auto* qsk = any_hash ? pl.take<uint32_t>(U * N) : nullptr;
+  auto* ksk = any_hash ? pl.take<uint32_t>(U * N) : nullptr;
+  if (ctx) {
+    ctx->meta = meta;
+    ctx->bitmap = bitmap;
+    ctx->proj = proj;
+    ctx->lse = lse;
+    ctx->colsum = colsum;
+    ctx->qsk = qsk;
+    ctx->ksk = ksk;
+  }
+  for (int l = 0; l < c->layers; ++l) {
+    const LayerInfo& li = info[l];
+    const size_t cap = li.cap;
+    kve::LayerCache lc{};
+    lc.K = pl.take<char>(U * cap * d * es);
+    lc.V = pl.take<char>(U * cap * d * es);
+    lc.S = pl.take<double>(U * cap);
+    lc.pos = pl.take<int32_t>(U * cap);
+    lc.sk = li.any_hash ? pl.take<uint32_t>(U * cap) : nullptr;
+    lc.count = pl.take<int32_t>(U);
+    lc.meta = meta ? meta + (size_t)l * c->heads : nullptr;
+    lc.proj = proj ? proj + (size_t)l * d * 32 : nullptr;
+    lc.cap = (int32_t)cap;
+    int32_t* h2o_ids = li.h2o_units.empty() ? nullptr : pl.take<int32_t>(li.h2o_units.size());
+    int32_t* hash_ids = li.hash_units.empty() ? nullptr : pl.take<int32_t>(li.hash_units.size());
+    if (ctx) {
+      Layer& L = ctx->layers[l];
+      L.cache = lc;
+      L.info = li;
+      L.h2o = {h2o_ids, (int32_t)li.h2o_units.size()};
+      L.hash = {hash_ids, (int32_t)li.hash_units.size()};
+    }
+  }
+  return pl.off;
+}
+
+kve_status dev(hipError_t e, const char* what) {
+  if (e == hipSuccess) return KVE_OK;
+  return fail(KVE_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+kve_status check_layer(kve_handle h, int32_t layer) {
+  if (!h) return fail(KVE_EINVAL, "handle is null");
+  if (layer < 0 || layer >= h->cfg.layers) return fail(KVE_EINVAL, "layer %d out of range", layer);
+  return KVE_OK;
+}
+
+kve_status finish(kve_handle h, hipStream_t st, const char* what) {
+  kve_status s = dev(hipGetLastError(), what);
+  if (s != KVE_OK) return s;
+  if (h->sync_check) {
+    s = dev(hipStreamSynchronize(st), what);
+    if (s != KVE_OK) return s;
+    s = dev(hipGetLastError(), what);
+  }
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+kve_status kvevict_workspace_size(const kve_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(KVE_EINVAL, "bytes is null");
+  std::vector<LayerInfo> info;
+  kve_status s = validate(cfg, &info);
+  if (s != KVE_OK) return s;
+  *bytes = layout(cfg, info, nullptr, nullptr);
+  return KVE_OK;
+}
+
+kve_status kvevict_create(const kve_config* cfg, void* d_workspace, size_t bytes, kve_handle* out) {
+  if (!out) return fail(KVE_EINVAL, "out is null");
+  *out = nullptr;
+  std::vector<LayerInfo> info;
+  kve_status s = validate(cfg, &info);
+  if (s != KVE_OK) return s;
+  if (!d_workspace) return fail(KVE_EINVAL, "workspace is null");
+  if ((uintptr_t)d_workspace % kAlign) return fail(KVE_EINVAL, "workspace is not 256-byte aligned");
+  const size_t need = layout(cfg, info, nullptr, nullptr);
+  if (bytes < need) return fail(KVE_ENOMEM, "workspace has %zu bytes, needs %zu", bytes, need);
+
+  kve_ctx* ctx = new (std::nothrow) kve_ctx();
+  if (!ctx) return fail(KVE_ENOMEM, "host allocation failed");
+  ctx->cfg = *cfg;
+  ctx->cfg.policy = ctx->cfg.heavy = ctx->cfg.recent = nullptr;
+  ctx->cfg.keep_token_bitmap = nullptr;
+  ctx->cfg.lsh_proj_bf16 = nullptr;
+  const float scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / std::sqrt((float)cfg->head_dim);
+  ctx->shape = {cfg->batch, cfg->heads, cfg->head_dim, cfg->dtype, scale};
+  ctx->layers.resize(cfg->layers);
+  layout(cfg, info, d_workspace, ctx);
+  const char* env = std::getenv("KVEVICT_SYNC_CHECK");
+  ctx->sync_check = env && env[0] == '1';
+
+  // tables to the device
+  std::vector<kve::HeadMeta> meta((size_t)cfg->layers * cfg->heads);
+  for (size_t i = 0; i < meta.size(); ++i) {
+    const int p = cfg->policy[i], hv = cfg->heavy[i], rc = cfg->recent[i];
+    meta[i] = {p, hv, rc, head_capacity(p, hv, rc, cfg->max_context)};
+  }
+  s = dev(hipMemcpy(ctx->meta, meta.data(), meta.size() * sizeof(kve::HeadMeta), hipMemcpyHostToDevice),
+          "copy head table");
+  if (s == KVE_OK && ctx->bitmap)
+    s = dev(hipMemcpy(ctx->bitmap, cfg->keep_token_bitmap, ((size_t)cfg->vocab + 31) / 32 * 4,
+                      hipMemcpyHostToDevice), "copy keep bitmap");
+  if (s == KVE_OK && ctx->proj)
+    s = dev(hipMemcpy(ctx->proj, cfg->lsh_proj_bf16, (size_t)cfg->layers * cfg->head_dim * 32 * 2,
+                      hipMemcpyHostToDevice), "copy projection");
+  for (int l = 0; l < cfg->layers && s == KVE_OK; ++l) {
+    Layer& L = ctx->layers[l];
+    if (L.h2o.n)
+      s = dev(hipMemcpy((void*)L.h2o.ids, L.info.h2o_units.data(), L.h2o.n * 4, hipMemcpyHostToDevice),
+              "copy unit list");
+    if (s == KVE_OK && L.hash.n)
+      s = dev(hipMemcpy((void*)L.hash.ids, L.info.hash_units.data(), L.hash.n * 4, hipMemcpyHostToDevice),
+              "copy unit list");
+  }
+  if (s != KVE_OK) {
+    delete ctx;
+    return s;
+  }
+  *out = ctx;
+  return KVE_OK;
+}
+
+kve_status kvevict_destroy(kve_handle h) {
+  if (!h) return fail(KVE_EINVAL, "handle is null");
+  delete h;
+  return KVE_OK;
+}
+
+kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t P, const void* q, const void* k, const void* v,
+                           const int32_t* token_ids, float* out, void* stream) {
+  kve_status s = check_layer(h, layer);
+  if (s != KVE_OK) return s;
+  if (P < 1 || P > h->cfg.max_context)
+    return fail(KVE_EINVAL, "prompt_len %d outside [1, %d]", P, h->cfg.max_context);
+  if (!q || !k || !v) return fail(KVE_EINVAL, "q, k and v are required");
+  Layer& L = h->layers[layer];
+  if (L.info.any_special && !token_ids) return fail(KVE_EINVAL, "token_ids required (layer has SPECIAL heads)");
+  hipStream_t st = (hipStream_t)stream;
+  const kve::Shape& sh = h->shape;
+  hipError_t e = hipSuccess;
+  // row statistics: all units when the prompt output is wanted, else H2O units
+  const kve::UnitList all{nullptr, sh.units()};
+  if (out) e = kve::launch_prefill_rowstats_valu(sh, P, all, q, k, v, h->lse, out, st);
+  else if (L.h2o.n) e = kve::launch_prefill_rowstats_valu(sh, P, L.h2o, q, k, v, h->lse, nullptr, st);
+  if (e == hipSuccess && L.h2o.n) e = kve::launch_prefill_colsum_valu(sh, P, L.h2o, q, k, h->lse, h->colsum, st);
+  if (e == hipSuccess)
+    e = kve::launch_prefill_select(sh, L.cache, P, h->colsum, k, v, token_ids, h->bitmap, h->cfg.vocab, st);
+  if (e == hipSuccess && L.hash.n) {
+    e = kve::launch_sketch_rows(sh, L.hash, q, P, 0, P, L.cache.proj, h->qsk, st);
+    if (e == hipSuccess) e = kve::launch_sketch_rows(sh, L.hash, k, P, 0, P, L.cache.proj, h->ksk, st);
+    if (e == hipSuccess)
+      e = kve::launch_hash_prefill(sh, L.cache, L.hash, P, L.info.max_hash_budget, h->qsk, h->ksk, k, v, st);
+  }
+  if (e != hipSuccess) return dev(e, "prefill launch");
+  s = finish(h, st, "prefill");
+  if (s == KVE_OK) L.position = P;
+  return s;
+}
+
+kve_status kvevict_decode_step(kve_handle h, int32_t layer, const void* q, const void* k, const void* v,
+                               const int32_t* token_ids, float* out, int32_t* evicted_pos, void* stream) {
+  kve_status s = check_layer(h, layer);
+  if (s != KVE_OK) return s;
+  Layer& L = h->layers[layer];
+  if (L.position < 0) return fail(KVE_ESTATE, "layer %d: decode before prefill", layer);
+  if (L.position >= h->cfg.max_context)
+    return fail(KVE_ESTATE, "layer %d: position %d reached max_context", layer, L.position);
+  if (!q || !k || !v || !out) return fail(KVE_EINVAL, "q, k, v and out are required");
+  if (L.info.any_special && !token_ids) return fail(KVE_EINVAL, "token_ids required (layer has SPECIAL heads)");
+  hipStream_t st = (hipStream_t)stream;
+  const kve::Shape& sh = h->shape;
+  hipError_t e = hipSuccess;
+  if (L.hash.n) e = kve::launch_hash_evict(sh, L.cache, L.hash, L.position, q, k, v, evicted_pos, st);
+  if (e == hipSuccess) {
+    const kve::DecodeIO io{q, k, v, token_ids, h->bitmap, h->cfg.vocab, out, evicted_pos, L.position};
+    e = kve::launch_decode_fused(sh, L.cache, io, st);
+  }
+  if (e != hipSuccess) return dev(e, "decode launch");
+  s = finish(h, st, "decode_step");
+  if (s == KVE_OK) L.position += 1;
+  return s;
+}
+
+kve_status kvevict_kept_indices(kve_handle h, int32_t layer, int32_t* pos_out, int32_t* count_out,
+                                double* scores_out, void* stream) {
+  kve_status s = check_layer(h, layer);
+  if (s != KVE_OK) return s;
+  if (!pos_out || !count_out) return fail(KVE_EINVAL, "pos_out and count_out are required");
+  const Layer& L = h->layers[layer];
+  if (L.position < 0) return fail(KVE_ESTATE, "layer %d has no cache yet", layer);
+  hipStream_t st = (hipStream_t)stream;
+  const size_t U = h->shape.units(), cap = L.cache.cap;
+  hipError_t e = hipMemcpyAsync(pos_out, L.cache.pos, U * cap * 4, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(count_out, L.cache.count, U * 4, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && scores_out)
+    e = hipMemcpyAsync(scores_out, L.cache.S, U * cap * 8, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return dev(e, "kept_indices copy");
+  return finish(h, st, "kept_indices");
+}
+
+int32_t kvevict_capacity(kve_handle h, int32_t layer) {
+  if (!h || layer < 0 || layer >= h->cfg.layers) return -1;
+  return h->layers[layer].cache.cap;
+}
+
+int32_t kvevict_position(kve_handle h, int32_t layer) {
+  if (!h || layer < 0 || layer >= h->cfg.layers) return -1;
+  return h->layers[layer].position;
+}
+
+const char* kvevict_status_string(kve_status s) {
+  switch (s) {
+    case KVE_OK: return "ok";
+    case KVE_EINVAL: return "invalid argument";
+    case KVE_ESTATE: return "invalid state";
+    case KVE_ENOMEM: return "workspace too small";
+    case KVE_EDEVICE: return "device error";
+    case KVE_EUNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+const char* kvevict_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+"""The C ABI library loads, exports every symbol the header declares, and
+validates arguments on the host (CPU only: no call here reaches the GPU)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from budgeted_decode_attention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "kvevict.h")).read()
+    return sorted(set(re.findall(r"\b(kvevict_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load_library()
+    names = header_functions()
+    assert len(names) == 10
+    assert set(names) == set(binding.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def cfg(**over):
+    base = dict(layers=1, batch=2, heads=3, head_dim=128, max_context=100, dtype=torch.bfloat16,
+                policy=[1, 1, 1], heavy=[10, 10, 10], recent=[5, 5, 5])
+    base.update(over)
+    return binding.make_config(**base)
+
+
+def status_of(c):
+    n = ctypes.c_size_t(0)
+    return binding.load_library().kvevict_workspace_size(ctypes.byref(c), ctypes.byref(n)), n.value
+
+
+def test_workspace_size_accepts_valid_configs_and_scales():
+    c, keep = cfg()
+    s, n1 = status_of(c)
+    assert s == binding.KVE_OK and n1 > 0
+    c, keep = cfg(max_context=1000)
+    s, n2 = status_of(c)
+    assert s == binding.KVE_OK and n2 > n1
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=96), binding.KVE_EUNSUPPORTED),
+    (dict(max_context=0), binding.KVE_EUNSUPPORTED),
+    (dict(max_context=40000), binding.KVE_EUNSUPPORTED),
+    (dict(policy=[7, 1, 1]), binding.KVE_EINVAL),
+    (dict(heavy=[0, 10, 10], recent=[0, 5, 5]), binding.KVE_EINVAL),
+    (dict(heavy=[-1, 10, 10]), binding.KVE_EINVAL),
+    (dict(heavy=[90, 10, 10], recent=[20, 5, 5]), binding.KVE_EINVAL),
+    (dict(policy=[2, 1, 1], heavy=[3, 10, 10]), binding.KVE_EINVAL),
+    (dict(policy=[0, 1, 1], heavy=[0, 10, 10], recent=[1, 5, 5]), binding.KVE_EINVAL),
+    (dict(policy=[3, 1, 1], heavy=[0, 10, 10], recent=[0, 5, 5]), binding.KVE_EINVAL),
+    (dict(policy=[4, 1, 1], heavy=[50, 10, 10], recent=[0, 5, 5]), binding.KVE_EUNSUPPORTED),
+    (dict(layers=0), binding.KVE_EINVAL),
+    (dict(softmax_scale=float("nan")), binding.KVE_EINVAL),
+])
+def test_workspace_size_rejects_bad_configs(over, status):
+    c, keep = cfg(**over)
+    s, _ = status_of(c)
+    assert s == status
+    assert binding.load_library().kvevict_last_error().decode() != ""
+
+
+def test_special_and_hash_need_their_tables():
+    c, keep = cfg(policy=[3, 1, 1], heavy=[0, 10, 10], recent=[0, 5, 5], keep_ids=[0, 1], vocab=100)
+    assert status_of(c)[0] == binding.KVE_OK
+    proj = torch.zeros((128, 32), dtype=torch.bfloat16)
+    c, keep = cfg(policy=[4, 1, 1], heavy=[50, 10, 10], recent=[0, 5, 5], proj=proj)
+    assert status_of(c)[0] == binding.KVE_OK
+
+
+def test_create_rejects_small_or_misaligned_workspace_without_touching_it():
+    lib = binding.load_library()
+    c, keep = cfg()
+    n = ctypes.c_size_t(0)
+    lib.kvevict_workspace_size(ctypes.byref(c), ctypes.byref(n))
+    h = ctypes.c_void_p()
+    fake = ctypes.c_void_p(1 << 40)          # never dereferenced: checks fail first
+    assert lib.kvevict_create(ctypes.byref(c), fake, n.value - 1, ctypes.byref(h)) == binding.KVE_ENOMEM
+    assert lib.kvevict_create(ctypes.byref(c), ctypes.c_void_p((1 << 40) + 8), n.value,
+                              ctypes.byref(h)) == binding.KVE_EINVAL
+    assert lib.kvevict_create(ctypes.byref(c), None, n.value, ctypes.byref(h)) == binding.KVE_EINVAL
+    assert h.value is None
+
+
+def test_calls_on_a_null_handle_fail_cleanly():
+    lib = binding.load_library()
+    assert lib.kvevict_prefill(None, 0, 10, None, None, None, None, None, None) == binding.KVE_EINVAL
+    assert lib.kvevict_decode_step(None, 0, None, None, None, None, None, None, None) == binding.KVE_EINVAL
+    assert lib.kvevict_kept_indices(None, 0, None, None, None, None) == binding.KVE_EINVAL
+    assert lib.kvevict_destroy(None) == binding.KVE_EINVAL
+    assert lib.kvevict_capacity(None, 0) == -1 and lib.kvevict_position(None, 0) == -1
+    for s in range(6):
+        assert lib.kvevict_status_string(s)

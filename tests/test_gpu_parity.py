@@ -1,0 +1,114 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle, in
+lockstep (kept sets exact up to the 1e-6 near-tie band, scores within 1e-5,
+outputs within 2e-3 of the max output element).
+
+Sizes are scaled-down versions of the five workloads that still span several
+tiles and a ragged tail; full-size launches are checked on sampled units in
+test_gpu_fullsize.py."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from tests import harness
+from workloads import configs
+from workloads.configs import FULL, H2O, HASH, LOCAL, SPECIAL
+from workloads.generate import generate_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_check(w, policy=None, heavy=None, recent=None, prompt_out=False, seed=0, units=None):
+    print(f"\n[parity] {w.name} B={w.batch} H={w.heads} d={w.head_dim} {w.dtype} P={w.prompt} "
+          f"T={w.steps} seed={seed}", flush=True)
+    inp = generate_layer(w, 0, "cpu", seed)
+    kv = harness.make_cache(w, inp, policy, heavy, recent)
+    r = harness.run_layer(kv, inp.to("cuda"), want_prompt_out=prompt_out)
+    rep = harness.check_all(w, inp, r, units, policy=policy, heavy=heavy, recent=recent)
+    print(f"[parity] decisions={rep.decisions} adopted={rep.adopted} max_out={rep.max_out_rel:.2e} "
+          f"max_prompt_out={rep.max_prompt_out_rel:.2e} max_S={rep.max_score_rel:.2e} "
+          f"min_gap={rep.min_gap:.2e}", flush=True)
+    assert rep.ok, rep.failures[:10]
+    bad = harness.check_invariants(w, r, inp.prompt_q.shape[2], policy, heavy, recent)
+    assert not bad, bad[:10]
+    kv.close()
+    return rep, r
+
+
+def test_tiny_h2o_full_size():
+    rep, _ = run_and_check(configs.get("tiny_h2o"), prompt_out=True)
+    assert rep.decisions == 2 * 64
+
+
+def test_h2o_fp16_scaled():
+    w = configs.scaled("opt6.7b_layer_h2o", batch=2, heads=4, prompt=300, steps=90)
+    assert (w.heavy, w.recent) == (30, 30)
+    run_and_check(w, prompt_out=True)
+
+
+def test_h2o_bf16_scaled():
+    w = configs.scaled("opt30b_decode_h2o", batch=2, heads=3, prompt=700, steps=60)
+    run_and_check(w)
+
+
+def test_h2o_fp32_d128():
+    w = dataclasses.replace(configs.scaled("opt6.7b_layer_h2o", batch=1, heads=3, prompt=150, steps=40),
+                            dtype="f32")
+    run_and_check(w, prompt_out=True)
+
+
+def test_fastgen_scaled():
+    w = configs.scaled("llama65b_fastgen", batch=2, heads=8, prompt=500, steps=60)
+    assert (w.local_window, w.freq_heavy) == (125, 50)
+    run_and_check(w, prompt_out=True)
+
+
+def test_hash_scaled():
+    w = configs.scaled("hashevict_lsh", batch=2, heads=4, prompt=600, steps=80)
+    assert w.hash_budget == 300
+    rep, _ = run_and_check(w)
+    assert rep.decisions == 8 * 80
+
+
+def test_budget_covering_context_is_full_attention():
+    """heavy + recent >= P + T: nothing is evicted; outputs equal causal attention."""
+    w = configs.scaled("opt30b_decode_h2o", batch=1, heads=2, prompt=100, steps=40)
+    N = w.context
+    rep, r = run_and_check(w, policy=[H2O] * 2, heavy=[N - 10] * 2, recent=[10] * 2, prompt_out=True)
+    assert (r.evicted == -1).all()
+
+
+@pytest.mark.parametrize("P,T,hh,rc", [(1, 30, 4, 4), (5, 40, 8, 8), (90, 30, 12, 0), (90, 30, 0, 12),
+                                       (64, 64, 16, 16), (257, 20, 100, 27)])
+def test_h2o_edge_shapes(P, T, hh, rc):
+    """Prompt of one token, prompt shorter than the budget (the cache grows),
+    no recent window (the new token may be evicted at once), no heavy part,
+    tile-aligned and ragged prompts."""
+    w = configs.scaled("opt6.7b_layer_h2o", batch=1, heads=2, prompt=P, steps=T)
+    run_and_check(w, policy=[H2O] * 2, heavy=[hh] * 2, recent=[rc] * 2)
+
+
+def test_special_without_kept_prompt_tokens():
+    w = configs.scaled("llama65b_fastgen", batch=1, heads=4, prompt=20, steps=30)
+    w = dataclasses.replace(w, special_ids=(31990,), punct_ids=(31991,))   # (almost) never drawn
+    run_and_check(w, policy=[SPECIAL, FULL, LOCAL, SPECIAL], heavy=[0] * 4, recent=[0, 0, 7, 0])
+
+
+def test_hash_prompt_shorter_than_budget():
+    w = configs.scaled("hashevict_lsh", batch=1, heads=2, prompt=50, steps=40)
+    run_and_check(w, policy=[HASH] * 2, heavy=[70] * 2, recent=[0] * 2)
+
+
+def test_deterministic_across_runs():
+    w = configs.scaled("opt6.7b_layer_h2o", batch=2, heads=2, prompt=200, steps=30)
+    inp = generate_layer(w, 0, "cpu", 3).to("cuda")
+    runs = []
+    for _ in range(2):
+        kv = harness.make_cache(w, inp)
+        runs.append(harness.run_layer(kv, inp))
+        kv.close()
+    a, b = runs
+    for f in ("out", "evicted", "final_pos", "final_S", "prefill_S"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
