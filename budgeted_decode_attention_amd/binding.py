@@ -195,7 +195,10 @@ class KVCache:
                  keep_ids: Sequence[int] = (), vocab: int = 0, proj: Optional[torch.Tensor] = None,
                  device="cuda"):
         self.layers, self.batch, self.heads, self.head_dim = layers, batch, heads, head_dim
-        self.max_context, self.dtype, self.device = max_context, dtype, torch.device(device)
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.max_context, self.dtype, self.device = max_context, dtype, dev
         self.cfg, self._keep = make_config(layers, batch, heads, head_dim, max_context, dtype, policy, heavy,
                                            recent, softmax_scale, keep_ids, vocab, proj)
         self.workspace_bytes = kvevict_workspace_size(self.cfg)
