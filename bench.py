@@ -1,0 +1,246 @@
+"""Benchmark: decode tokens/s with H2O eviction at a 20% KV budget, and the
+fused decode kernel's achieved HBM bandwidth against MI355X peak.
+
+One step is the whole hot path over one batch: prefill (scoring, selection,
+gather) of every layer, then every decode step of every layer, in model
+order (layer-major within a step).  Inputs are synthetic, seeded, generated
+on the GPU and resident in HBM before timing starts.
+
+Prints one JSON line.  `value` = batch * T / step time (prefill included).
+The roofline object covers the fused decode kernel: algorithmic bytes per
+launch (kept K/V read, score/position metadata, the step's q/k/v, the victim
+write and the fp32 output) divided by its average launch time, measured with
+HIP events around sampled decode steps (each a back-to-back group of one
+launch per layer, no other kernel in between) on the stream the kernel runs on.
+The CPU baseline times the float64 oracle on a bounded sample of units of the
+same workload, before the GPU is initialised, and scales it to the job.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/sec with H2O eviction at 20% budget; achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "opt30b_decode_h2o"
+
+
+# ---------------------------------------------------------------- CPU baseline (oracle)
+
+def _oracle_unit(args):
+    """One unit through the float64 oracle (prefill + every decode step)."""
+    import numpy as np
+    from oracle import fastgen, h2o, hashevict
+    kind, Q, K, V, P, a, b, scale, extra = args
+    Q, K, V = (np.asarray(x, dtype=np.float64) for x in (Q, K, V))
+    t0 = time.perf_counter()
+    if kind == "h2o":
+        h2o.run_unit(Q, K, V, P, a, b, scale)
+    elif kind == "hash":
+        hashevict.run_unit(Q, K, V, np.asarray(extra, dtype=np.float64), P, a, scale)
+    else:
+        pol, ids, keep = extra
+        fastgen.run_unit(pol, Q, K, V, P, scale, heavy=a, recent=b, ids=ids, keep_ids=keep)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, n_units: int, workers: int):
+    """Times the oracle on `n_units` units of workload `w` (inputs generated on the
+    CPU with the same recipe), with `workers` processes; returns the dict for
+    the JSON line.  Must run before anything initialises the GPU."""
+    import numpy as np
+    from workloads import configs
+    from workloads.generate import generate_layer, unit_ids, unit_sequence
+    sample_w = configs.scaled(w.name, batch=1, heads=w.heads, prompt=w.prompt, steps=w.steps)
+    pol, hv, rc = w.policy_table(0)
+    tasks = []
+    layer = 0
+    scale = 1.0 / np.sqrt(w.head_dim)
+    while len(tasks) < n_units:
+        inp = generate_layer(sample_w, layer, "cpu", 1)
+        for h in range(w.heads):
+            if len(tasks) >= n_units:
+                break
+            Q, K, V = (x.astype(np.float32) for x in unit_sequence(inp, 0, h))
+            if w.family == "h2o":
+                tasks.append(("h2o", Q, K, V, w.prompt, hv[h], rc[h], scale, None))
+            elif w.family == "hash":
+                tasks.append(("hash", Q, K, V, w.prompt, hv[h], 0, scale, inp.proj.float().numpy()))
+            else:
+                tasks.append(("fastgen", Q, K, V, w.prompt, hv[h], rc[h], scale,
+                              (pol[h], unit_ids(inp, 0), w.keep_ids())))
+        layer += 1
+    os.environ["OMP_NUM_THREADS"] = "1"
+    os.environ["OPENBLAS_NUM_THREADS"] = "1"
+    os.environ["MKL_NUM_THREADS"] = "1"
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        per = pool.map(_oracle_unit, tasks, chunksize=1)
+    wall = time.perf_counter() - t0
+    job_s = wall * w.units / len(tasks)
+    tokens = w.batch * w.steps
+    return {
+        "value": tokens / job_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+        "sample": f"{len(tasks)} of {w.units} units (full P={w.prompt}, T={w.steps}), float64 numpy, "
+                  f"{workers} processes x 1 BLAS thread, wall {wall:.2f} s "
+                  f"(mean {sum(per) / len(per):.3f} s per unit); job time scaled by units "
+                  f"({job_s:.0f} s for the whole job)",
+    }
+
+
+# ---------------------------------------------------------------- GPU
+
+def algorithmic_bytes_per_unit(w) -> float:
+    """Bytes the method itself moves per unit-step in the fused decode kernel:
+    kept K and V read, score read and write (counted at 4 bytes each, the
+    float32 minimum), position read, the step's q/k/v, the victim's K/V write
+    and the fp32 output."""
+    s = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    d = w.head_dim
+    if w.family != "h2o":
+        raise NotImplementedError("the bench's byte model covers the H2O workloads")
+    B = w.heavy + w.recent
+    return B * d * s * 2 + B * (4 + 4) + B * 4 + 3 * d * s + 2 * d * s + 4 * d
+
+
+def run_gpu(w, steps: int, warmup: int, sample_every: int):
+    import numpy as np
+    import torch
+    from budgeted_decode_attention_amd import KVCache
+    from workloads.generate import generate_layer
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    inputs = [generate_layer(w, l, dev, 0) for l in range(w.layers)]
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t0
+    pol, hv, rc = w.policy_table(0)
+    tabs = [np.tile(np.array(x, dtype=np.int32), w.layers) for x in (pol, hv, rc)]
+    kw = {}
+    if 3 in pol:
+        kw.update(keep_ids=w.keep_ids(), vocab=w.vocab)
+    if 4 in pol:
+        kw.update(proj=inputs[0].proj)
+    kv = KVCache(w.layers, w.batch, w.heads, w.head_dim, w.context, inputs[0].prompt_q.dtype,
+                 *tabs, device=dev, **kw)
+    ids = [x.ids for x in inputs]
+    pids = [x[:, :w.prompt].contiguous() if x is not None else None for x in ids]
+    dids = [[x[:, w.prompt + s].contiguous() for s in range(w.steps)] if x is not None else None for x in ids]
+    out = torch.empty((w.layers, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=dev)
+    ev = torch.empty((w.layers, w.batch, w.heads), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    samples = []
+
+    def step(timed: bool):
+        for l in range(w.layers):
+            x = inputs[l]
+            kv.prefill(l, x.prompt_q, x.prompt_k, x.prompt_v, pids[l])
+        for s in range(w.steps):
+            sample = timed and s % sample_every == 0
+            if sample:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            for l in range(w.layers):
+                x = inputs[l]
+                tid = dids[l][s] if dids[l] is not None else None
+                kv.decode_step(l, x.dec_q[s], x.dec_k[s], x.dec_v[s], tid, out[l], ev[l])
+            if sample:
+                e1.record(stream)
+                samples.append((e0, e1))
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    # phase split of one untimed step (prefill vs decode), for the report
+    p0, p1, p2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    p0.record(stream)
+    for l in range(w.layers):
+        x = inputs[l]
+        kv.prefill(l, x.prompt_q, x.prompt_k, x.prompt_v, pids[l])
+    p1.record(stream)
+    for s in range(w.steps):
+        for l in range(w.layers):
+            x = inputs[l]
+            tid = dids[l][s] if dids[l] is not None else None
+            kv.decode_step(l, x.dec_q[s], x.dec_k[s], x.dec_v[s], tid, out[l], ev[l])
+    p2.record(stream)
+    torch.cuda.synchronize()
+    prefill_ms, decode_ms = p0.elapsed_time(p1), p1.elapsed_time(p2)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    group_ms = [a.elapsed_time(b) for a, b in samples]
+    kernel_us = 1e3 * sum(group_ms) / (len(group_ms) * w.layers)
+    return {"wall_s": wall, "gen_s": gen_s, "prefill_ms": prefill_ms, "decode_ms": decode_ms,
+            "kernel_us": kernel_us, "n_samples": len(group_ms) * w.layers,
+            "finite": bool(torch.isfinite(out).all().item())}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-units", type=int, default=256, help="oracle sample size for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sample-every", type=int, default=4,
+                    help="event-time the per-layer decode launches of every k-th decode step")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {a.gpus}); the units shard across GPUs with no "
+              f"exchange, so a multi-GPU figure is N x the one-GPU value", file=sys.stderr)
+        sys.exit(2)
+    from workloads import configs
+    w = configs.get(a.workload)
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        workers = min(16, len(os.sched_getaffinity(0)))
+        cpu = cpu_baseline(w, a.cpu_units, workers)
+        print(f"[bench] cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
+
+    r = run_gpu(w, a.steps, a.warmup, a.sample_every)
+    ms = 1e3 * r["wall_s"] / a.steps
+    tokens = w.batch * w.steps
+    bpu = algorithmic_bytes_per_unit(w)
+    bytes_launch = bpu * w.units_per_layer
+    achieved = bytes_launch / (r["kernel_us"] * 1e-6) / 1e9
+    line = {
+        "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "batch": w.batch, "heads": w.heads,
+                   "head_dim": w.head_dim, "prompt": w.prompt, "decode_steps": w.steps,
+                   "budget": (f"{w.heavy} heavy + {w.recent} recent" if w.family == "h2o" else w.family)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_fused", "bytes_per_launch": bytes_launch,
+                     "kernel_us": r["kernel_us"], "launches_timed": r["n_samples"]},
+        "cpu_baseline": cpu,
+        "detail": {"prefill_ms_per_step": r["prefill_ms"], "decode_ms_per_step": r["decode_ms"],
+                   "decode_only_tokens_per_s": tokens / (r["decode_ms"] * 1e-3),
+                   "input_generation_s": r["gen_s"], "outputs_finite": r["finite"]},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -327,11 +327,20 @@ kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t P, const void* q
   hipStream_t st = (hipStream_t)stream;
   const kve::Shape& sh = h->shape;
   hipError_t e = hipSuccess;
-  // row statistics: all units when the prompt output is wanted, else H2O units
+  // Scores (H2O heads): row statistics, then column sums.  16-bit inputs use
+  // the matrix-core kernels; fp32 inputs and the optional prompt output use
+  // the vector-ALU kernels.
   const kve::UnitList all{nullptr, sh.units()};
-  if (out) e = kve::launch_prefill_rowstats_valu(sh, P, all, q, k, v, h->lse, out, st);
-  else if (L.h2o.n) e = kve::launch_prefill_rowstats_valu(sh, P, L.h2o, q, k, v, h->lse, nullptr, st);
-  if (e == hipSuccess && L.h2o.n) e = kve::launch_prefill_colsum_valu(sh, P, L.h2o, q, k, h->lse, h->colsum, st);
+  const bool mfma = sh.dtype != KVE_F32;
+  if (out) {
+    e = kve::launch_prefill_rowstats_valu(sh, P, all, q, k, v, h->lse, out, st);
+  } else if (L.h2o.n) {
+    e = mfma ? kve::launch_prefill_rowstats_mfma(sh, P, L.h2o, q, k, h->lse, st)
+             : kve::launch_prefill_rowstats_valu(sh, P, L.h2o, q, k, v, h->lse, nullptr, st);
+  }
+  if (e == hipSuccess && L.h2o.n)
+    e = mfma ? kve::launch_prefill_colsum_mfma(sh, P, L.h2o, q, k, h->lse, h->colsum, st)
+             : kve::launch_prefill_colsum_valu(sh, P, L.h2o, q, k, h->lse, h->colsum, st);
   if (e == hipSuccess)
     e = kve::launch_prefill_select(sh, L.cache, P, h->colsum, k, v, token_ids, h->bitmap, h->cfg.vocab, st);
   if (e == hipSuccess && L.hash.n) {

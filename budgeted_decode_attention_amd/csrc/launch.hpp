@@ -55,6 +55,12 @@ hipError_t launch_prefill_rowstats_valu(const Shape& sh, int P, UnitList units, 
 hipError_t launch_prefill_colsum_valu(const Shape& sh, int P, UnitList units, const void* q,
                                       const void* k, const float* lse, double* colsum,
                                       hipStream_t st);
+// The same two passes on the matrix cores (16-bit dtypes only; no output).
+hipError_t launch_prefill_rowstats_mfma(const Shape& sh, int P, UnitList units, const void* q,
+                                        const void* k, float* lse, hipStream_t st);
+hipError_t launch_prefill_colsum_mfma(const Shape& sh, int P, UnitList units, const void* q,
+                                      const void* k, const float* lse, double* colsum,
+                                      hipStream_t st);
 // Chooses the kept prompt positions per the head's policy and fills the cache.
 hipError_t launch_prefill_select(const Shape& sh, const LayerCache& c, int P, const double* colsum,
                                  const void* k, const void* v, const int32_t* ids,

@@ -1,0 +1,321 @@
+// Prefill scoring on the matrix cores (bf16 / fp16 inputs, d = 64 or 128).
+//
+// The H2O review page (proposed method) ranks tokens by accumulated attention;
+// at the prompt that is the column sum of the causal softmax,
+//   c_j = sum_{i >= j} exp(scale q_i.k_j - lse_i),  lse_i = log sum_{j <= i} exp(scale q_i.k_j),
+// a dense contraction (Q K^T) followed by elementwise exponentials.  Two passes:
+//
+//   rowstats: workgroup = (unit, 128 queries); waves hold 32 queries each as
+//             MFMA B fragments in registers; 64-key tiles of K are staged in
+//             LDS and read as A fragments; S^T = K Q^T per 16x16 block with
+//             v_mfma_f32_16x16x32_{bf16,f16}; online maximum per query; the
+//             per-tile sums are added in float64.
+//   colsum:   workgroup = (unit, 128 keys); waves hold 32 keys each as A
+//             fragments; 64-query tiles of Q (and their lse) are staged in LDS;
+//             weights exp2(s * scale * log2e - lse2) are summed per key in
+//             float32 within a tile and in float64 across tiles.  No atomics:
+//             each workgroup owns its columns.
+//
+// MFMA 16x16x32 lane layout: lane l supplies row (l % 16) of A and column
+// (l % 16) of B, each with 8 consecutive k values chosen by l / 16; it
+// receives D[4 (l / 16) + r][l % 16], r = 0..3.  With A = keys and B =
+// queries, lane l therefore holds s(query = l % 16, keys 4 (l / 16) + r).
+//
+// Exponents use base 2 with the factor scale * log2(e) split into a float
+// pair (hi + lo) applied by two fused multiply-adds, so the only rounding of
+// the argument is relative to its (small) result.  lse is exchanged in
+// natural-log units as a float pair (hi, lo) whose sum is the float64 value.
+#include "common.hpp"
+
+namespace kve {
+namespace {
+
+constexpr int kNT = 256;
+constexpr int kBlk = 128;          // queries (rowstats) / keys (colsum) per workgroup
+constexpr int kTile = 64;          // keys (rowstats) / queries (colsum) per LDS tile
+constexpr double kLog2e = 1.4426950408889634;
+constexpr double kLn2 = 0.6931471805599453;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Mfma;
+template <> struct Mfma<BF16> {
+  __device__ static inline f32x4 run(const uint4& a, const uint4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+};
+template <> struct Mfma<F16> {
+  __device__ static inline f32x4 run(const uint4& a, const uint4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+  }
+};
+
+// LDS tile of kTile rows x D 16-bit elements, rows padded by 16 bytes so that
+// the 16 rows read by one 16-lane group fall on distinct banks.
+template <int D> struct Tile {
+  static constexpr int kRowBytes = D * 2 + 16;
+  static constexpr int kBytes = kTile * kRowBytes;
+};
+
+// Stages rows [r0, r0 + kTile) of a [P][D] 16-bit block into LDS; rows at or
+// past P are zero.
+template <int D>
+__device__ inline void stage_tile(char* lds, const char* src, int r0, int P) {
+  constexpr int CPR = D * 2 / 16;               // 16-byte chunks per row
+#pragma unroll
+  for (int i = threadIdx.x; i < kTile * CPR; i += kNT) {
+    const int r = i / CPR, c = i % CPR;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + r < P) v = ld16(src + ((size_t)(r0 + r) * D) * 2 + c * 16);
+    *reinterpret_cast<uint4*>(lds + r * Tile<D>::kRowBytes + c * 16) = v;
+  }
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct Scale2 {
+  float hi, lo;   // hi + lo = scale * log2(e)
+};
+
+__device__ inline Scale2 make_scale2(float scale) {
+  const double c = (double)scale * kLog2e;
+  const float hi = (float)c;
+  return {hi, (float)(c - (double)hi)};
+}
+
+// ------------------------------------------------------------------ rowstats
+template <int DT, int D>
+__global__ __launch_bounds__(kNT) void rowstats_mfma_kernel(Shape sh, int P, UnitList ul, const void* q,
+                                                            const void* k, float* lse) {
+  constexpr int KS = D / 32;                    // MFMA k-steps over the head dimension
+  __shared__ __attribute__((aligned(16))) char Ks[Tile<D>::kBytes];
+  const int u = ul.ids ? ul.ids[blockIdx.x] : blockIdx.x;
+  const int nqb = (P + kBlk - 1) / kBlk;
+  const int qb = nqb - 1 - (int)blockIdx.y;     // heaviest (last) query block first
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const size_t base = (size_t)u * P * D * 2;
+  const char* qbase = (const char*)q + base;
+  const char* kbase = (const char*)k + base;
+  const int q0 = qb * kBlk + w * 32;            // this wave's first query
+  const Scale2 c2 = make_scale2(sh.scale);
+
+  // B fragments: the wave's 32 queries
+  uint4 qf[2][KS];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int qi = q0 + nb * 16 + c16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[nb][ks] = qi < P ? ld16(qbase + ((size_t)qi * D + ks * 32 + g * 8) * 2) : make_uint4(0, 0, 0, 0);
+  }
+  // mc: running offset = (max raw logit) * c2.hi, per query of this lane;
+  // weights are exp2(s * c2 - mc) with s * c2 formed by two fused steps
+  float mc[2] = {-INFINITY, -INFINITY};
+  double l[2] = {0.0, 0.0};
+  const int kend = min(P, qb * kBlk + kBlk);    // keys needed by the block
+  for (int k0 = 0; k0 < kend; k0 += kTile) {
+    __syncthreads();
+    stage_tile<D>(Ks, kbase, k0, P);
+    __syncthreads();
+    if (k0 > q0 + 31) continue;                 // tile entirely after this wave's queries
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(Ks + (mb * 16 + c16) * Tile<D>::kRowBytes + (ks * 32 + g * 8) * 2);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = Mfma<DT>::run(a, qf[nb][ks], acc[mb][nb]);
+      }
+    }
+    const bool edge = (k0 + kTile > q0) || (k0 + kTile > P);   // masking needed somewhere
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int qi = q0 + nb * 16 + c16;
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kj = k0 + mb * 16 + g * 4 + r;
+          const bool ok = !edge || (kj <= qi && kj < P);
+          tmax = fmaxf(tmax, ok ? acc[mb][nb][r] : -INFINITY);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mn = fmaxf(mc[nb], tmax * c2.hi);
+      if (mn > mc[nb]) {
+        l[nb] *= (double)exp2_fast(mc[nb] - mn);
+        mc[nb] = mn;
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kj = k0 + mb * 16 + g * 4 + r;
+          const bool ok = !edge || (kj <= qi && kj < P);
+          const float s = acc[mb][nb][r];
+          const float p = exp2_fast(fmaf(s, c2.lo, fmaf(s, c2.hi, -mn)));
+          sum += ok ? p : 0.f;
+        }
+      l[nb] += (double)sum;
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    double lt = l[nb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int qi = q0 + nb * 16 + c16;
+    if (g == 0 && qi < P) {
+      const double L = ((double)mc[nb] + log2(lt)) * kLn2;  // natural-log units
+      const float hi = (float)L;
+      lse[((size_t)u * P + qi) * 2] = hi;
+      lse[((size_t)u * P + qi) * 2 + 1] = (float)(L - (double)hi);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ colsum
+template <int DT, int D>
+__global__ __launch_bounds__(kNT) void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q,
+                                                          const void* k, const float* lse, double* colsum) {
+  constexpr int KS = D / 32;
+  __shared__ __attribute__((aligned(16))) char Qs[Tile<D>::kBytes];
+  __shared__ float Lh[kTile], Ll[kTile];       // lse in log2 units, float pair
+  const int u = ul.ids ? ul.ids[blockIdx.x] : blockIdx.x;
+  const int kb = blockIdx.y;                    // key block 0 (the heaviest) first
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const size_t base = (size_t)u * P * D * 2;
+  const char* qbase = (const char*)q + base;
+  const char* kbase = (const char*)k + base;
+  const int j0 = kb * kBlk + w * 32;            // this wave's first key
+  const Scale2 c2 = make_scale2(sh.scale);
+
+  uint4 kf[2][KS];                              // A fragments: the wave's 32 keys
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int kj = j0 + mb * 16 + c16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[mb][ks] = kj < P ? ld16(kbase + ((size_t)kj * D + ks * 32 + g * 8) * 2) : make_uint4(0, 0, 0, 0);
+  }
+  double cs[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cs[mb][r] = 0.0;
+
+  for (int i0 = kb * kBlk; i0 < P; i0 += kTile) {
+    __syncthreads();
+    stage_tile<D>(Qs, qbase, i0, P);
+    if (threadIdx.x < kTile) {
+      const int qi = min(i0 + (int)threadIdx.x, P - 1);
+      const double L2 = ((double)lse[((size_t)u * P + qi) * 2] + (double)lse[((size_t)u * P + qi) * 2 + 1]) * kLog2e;
+      const float hi = (float)L2;
+      Lh[threadIdx.x] = hi;
+      Ll[threadIdx.x] = (float)(L2 - (double)hi);
+    }
+    __syncthreads();
+    if (i0 + kTile - 1 < j0) continue;          // every query of the tile precedes this wave's keys
+    const bool diag = i0 < j0 + 32;
+    float part[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[mb][r] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 b = *reinterpret_cast<const uint4*>(Qs + (nb * 16 + c16) * Tile<D>::kRowBytes + (ks * 32 + g * 8) * 2);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc[mb] = Mfma<DT>::run(kf[mb][ks], b, acc[mb]);
+      }
+      const int qi = i0 + nb * 16 + c16;
+      const float lh = Lh[nb * 16 + c16], ll = Ll[nb * 16 + c16];
+      const bool qok = qi < P;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kj = j0 + mb * 16 + g * 4 + r;
+          const float s = acc[mb][r];
+          float x = fmaf(s, c2.hi, -lh);
+          x = fmaf(s, c2.lo, x) - ll;
+          float p = exp2_fast(x);
+          if (!qok || (diag && qi < kj)) p = 0.f;
+          part[mb][r] += p;
+        }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cs[mb][r] += (double)part[mb][r];
+  }
+  // sum over the 16 lanes (queries) that share each key
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      double v = cs[mb][r];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+      const int kj = j0 + mb * 16 + g * 4 + r;
+      if (c16 == 0 && kj < P) colsum[(size_t)u * P + kj] = v;
+    }
+}
+
+template <int DT, int D>
+hipError_t rowstats_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, float* lse,
+                      hipStream_t st) {
+  dim3 grid(ul.n, (P + kBlk - 1) / kBlk);
+  hipLaunchKernelGGL((rowstats_mfma_kernel<DT, D>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t colsum_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, const float* lse,
+                    double* colsum, hipStream_t st) {
+  dim3 grid(ul.n, (P + kBlk - 1) / kBlk);
+  hipLaunchKernelGGL((colsum_mfma_kernel<DT, D>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse, colsum);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_rowstats_mfma(const Shape& sh, int P, UnitList ul, const void* q, const void* k,
+                                        float* lse, hipStream_t st) {
+  if (ul.n <= 0) return hipSuccess;
+  switch (sh.dtype * 1000 + sh.d) {
+    case F16 * 1000 + 64: return rowstats_t<F16, 64>(sh, P, ul, q, k, lse, st);
+    case F16 * 1000 + 128: return rowstats_t<F16, 128>(sh, P, ul, q, k, lse, st);
+    case BF16 * 1000 + 64: return rowstats_t<BF16, 64>(sh, P, ul, q, k, lse, st);
+    case BF16 * 1000 + 128: return rowstats_t<BF16, 128>(sh, P, ul, q, k, lse, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_colsum_mfma(const Shape& sh, int P, UnitList ul, const void* q, const void* k,
+                                      const float* lse, double* colsum, hipStream_t st) {
+  if (ul.n <= 0) return hipSuccess;
+  switch (sh.dtype * 1000 + sh.d) {
+    case F16 * 1000 + 64: return colsum_t<F16, 64>(sh, P, ul, q, k, lse, colsum, st);
+    case F16 * 1000 + 128: return colsum_t<F16, 128>(sh, P, ul, q, k, lse, colsum, st);
+    case BF16 * 1000 + 64: return colsum_t<BF16, 64>(sh, P, ul, q, k, lse, colsum, st);
+    case BF16 * 1000 + 128: return colsum_t<BF16, 128>(sh, P, ul, q, k, lse, colsum, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kve
