@@ -16,11 +16,41 @@
 namespace kve {
 namespace {
 
+// Compile-time tuning: rows loaded per thread before use; the register budget
+// as resident waves per SIMD (0 = compiler's choice; 8 lets every workgroup of
+// a 1,792-unit layer be resident at once); non-temporal K/V loads.
+#ifndef KVE_DECODE_UNROLL
+#define KVE_DECODE_UNROLL 2
+#endif
+#ifndef KVE_DECODE_WAVES_PER_EU
+#define KVE_DECODE_WAVES_PER_EU 8
+#endif
+#ifndef KVE_DECODE_NT_LOADS
+#define KVE_DECODE_NT_LOADS 1
+#endif
+
 constexpr int kNT = 256;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = KVE_DECODE_UNROLL;
+
+#if KVE_DECODE_WAVES_PER_EU > 0
+#define KVE_DECODE_ATTR __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(KVE_DECODE_WAVES_PER_EU)))
+#else
+#define KVE_DECODE_ATTR __launch_bounds__(kNT)
+#endif
+
+// Cached K/V rows are read once per step: optionally mark them streaming.
+__device__ inline uint4 ld_kv(const void* p) {
+#if KVE_DECODE_NT_LOADS
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return ld16(p);
+#endif
+}
 
 template <int DT, int D>
-__global__ __launch_bounds__(kNT) void decode_fused_kernel(Shape sh, LayerCache c, DecodeIO io) {
+__global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, DecodeIO io) {
   constexpr int EPL = St<DT>::EPL;
   constexpr int ES = elem_bytes<DT>();
   constexpr int LPR = D / EPL;
@@ -55,7 +85,7 @@ __global__ __launch_bounds__(kNT) void decode_fused_kernel(Shape sh, LayerCache 
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
       const int r = r0 + i * RPI + rg;
-      raw[i] = r < n ? ld16(Kb + ((size_t)r * D + col * EPL) * ES) : make_uint4(0, 0, 0, 0);
+      raw[i] = r < n ? ld_kv(Kb + ((size_t)r * D + col * EPL) * ES) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
@@ -103,7 +133,7 @@ __global__ __launch_bounds__(kNT) void decode_fused_kernel(Shape sh, LayerCache 
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
       const int r = r0 + i * RPI + rg;
-      raw[i] = r < n ? ld16(Vb + ((size_t)r * D + col * EPL) * ES) : make_uint4(0, 0, 0, 0);
+      raw[i] = r < n ? ld_kv(Vb + ((size_t)r * D + col * EPL) * ES) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
