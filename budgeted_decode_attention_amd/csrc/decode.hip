@@ -1,5 +1,5 @@
-// Fused decode step: attention over a unit's kept slots, score accumulation
-// and the cache policy's replacement, one workgroup per unit.
+// Decode step: attention over a unit's kept slots, score accumulation and
+// the cache policy's replacement.
 //
 // H2O review page, proposed method: each decode step's attention weights are
 // the statistics that drive a greedy eviction; the lowest-scoring token
@@ -7,10 +7,17 @@
 // review page: the same step under per-head positional policies.
 //
 // Layout: slot rows of d elements, 16 bytes per lane; LPR lanes cover one row
-// and the workgroup covers NT / LPR rows per load wave.  Logits and then the
-// unnormalised weights live in LDS (one float per slot), so the softmax is
-// exact (max, then sum in float64) and the score update uses the same weights
-// the output does.
+// (a row group) and the workgroup covers NT / LPR rows per load wave.  Logits
+// are formed by DPP sums inside each row group.
+//
+// Two launch shapes, chosen per layer by the slot stride:
+//   fused     one workgroup per unit: logits to LDS, exact softmax (maximum,
+//             float64 sum), P.V, then the policy step;
+//   split     `partials` over (unit, chunk of slots) writes each chunk's
+//             maximum, sum and unnormalised output plus the raw logits;
+//             `combine`, one workgroup per unit, merges the chunks under the
+//             global maximum and runs the same policy step, recomputing the
+//             exact weights from the logits for the float64 score update.
 #include "common.hpp"
 
 namespace kve {
@@ -38,7 +45,7 @@ constexpr int kUnroll = KVE_DECODE_UNROLL;
 #define KVE_DECODE_ATTR __launch_bounds__(kNT)
 #endif
 
-// Cached K/V rows are read once per step: optionally mark them streaming.
+// Cached K/V rows are read once per step: mark them streaming.
 __device__ inline uint4 ld_kv(const void* p) {
 #if KVE_DECODE_NT_LOADS
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -49,120 +56,105 @@ __device__ inline uint4 ld_kv(const void* p) {
 #endif
 }
 
-template <int DT, int D>
-__global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, DecodeIO io) {
-  constexpr int EPL = St<DT>::EPL;
-  constexpr int ES = elem_bytes<DT>();
-  constexpr int LPR = D / EPL;
-  constexpr int RPI = kNT / LPR;
+template <int DT, int D> struct Rows {
+  static constexpr int EPL = St<DT>::EPL;
+  static constexpr int ES = elem_bytes<DT>();
+  static constexpr int LPR = D / EPL;
+  static constexpr int RPI = kNT / LPR;
   static_assert(LPR >= 4 && LPR <= 32 && kNT % LPR == 0, "row layout");
+};
 
-  extern __shared__ float wts[];                 // [cap + 1]
-  __shared__ float red[RPI * D];
-  __shared__ float fscr[kNT / kWave];
-  __shared__ double dscr[kNT / kWave];
-  __shared__ MinKey kscr[kNT / kWave];
-
-  const int u = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int col = tid % LPR;
-  const int rg = tid / LPR;
-  const HeadMeta m = c.meta[u % sh.heads];
-  const int n = c.count[u];
-  const int with_new = m.policy == HASH ? 0 : 1;  // HASH: token t is already in a slot
-  const int t = io.t;
-  const size_t slot0 = (size_t)u * c.cap;
-  char* Kb = (char*)c.K + slot0 * D * ES;
-  char* Vb = (char*)c.V + slot0 * D * ES;
-  const size_t in_off = ((size_t)u * D + col * EPL) * ES;
-
-  float qf[EPL];
-  St<DT>::unpack(ld16((const char*)io.q + in_off), qf);
-
-  // ---- logits l_j = scale * q . k_j
-  for (int r0 = 0; r0 < n; r0 += RPI * kUnroll) {
+// Logits scale * q.k_r for rows [r0, r1) into lg[r - r0] (LDS) and, when
+// lgg is non-null, lgg[r] (global).  qf holds this lane's q elements.
+template <int DT, int D>
+__device__ inline void row_logits(const char* Kb, const float* qf, float scale, int r0, int r1, float* lg,
+                                  float* lgg) {
+  using R = Rows<DT, D>;
+  const int col = threadIdx.x % R::LPR, rg = threadIdx.x / R::LPR;
+  for (int b = r0; b < r1; b += R::RPI * kUnroll) {
     uint4 raw[kUnroll];
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int r = r0 + i * RPI + rg;
-      raw[i] = r < n ? ld_kv(Kb + ((size_t)r * D + col * EPL) * ES) : make_uint4(0, 0, 0, 0);
+      const int r = b + i * R::RPI + rg;
+      raw[i] = r < r1 ? ld_kv(Kb + ((size_t)r * D + col * R::EPL) * R::ES) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int r = r0 + i * RPI + rg;
-      float f[EPL];
+      const int r = b + i * R::RPI + rg;
+      float f[R::EPL];
       St<DT>::unpack(raw[i], f);
       float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) s = fmaf(qf[j], f[j], s);
-      s = group_sum<LPR>(s);
-      if (col == 0 && r < n) wts[r] = s * sh.scale;
+      for (int j = 0; j < R::EPL; ++j) s = fmaf(qf[j], f[j], s);
+      s = group_sum<R::LPR>(s) * scale;
+      if (col == 0 && r < r1) {
+        lg[r - r0] = s;
+        if (lgg) lgg[r] = s;
+      }
     }
   }
-  if (with_new && rg == 0) {
-    float f[EPL];
-    St<DT>::unpack(ld16((const char*)io.k + in_off), f);
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) s = fmaf(qf[j], f[j], s);
-    s = group_sum<LPR>(s);
-    if (col == 0) wts[n] = s * sh.scale;
-  }
-  __syncthreads();
+}
 
-  // ---- softmax over the n kept slots (+ the new token)
-  const int nt = n + with_new;
-  float mx = -INFINITY;
-  for (int r = tid; r < nt; r += kNT) mx = fmaxf(mx, wts[r]);
-  mx = block_max<kNT>(mx, fscr);
-  double ls = 0.0;
-  for (int r = tid; r < nt; r += kNT) {
-    const float w = expf(wts[r] - mx);
-    wts[r] = w;
-    ls += (double)w;
-  }
-  const double L = block_sum<kNT>(ls, dscr);     // barriers inside: wts[] complete
-  const double invL = 1.0 / L;
-
-  // ---- output o = sum_j w_j v_j / L
-  float acc[EPL];
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
-  for (int r0 = 0; r0 < n; r0 += RPI * kUnroll) {
+// acc (this lane's EPL columns) += sum over rows [r0, r1) of w[r - r0] * v_r.
+template <int DT, int D>
+__device__ inline void row_values(const char* Vb, const float* w, int r0, int r1, float* acc) {
+  using R = Rows<DT, D>;
+  const int col = threadIdx.x % R::LPR, rg = threadIdx.x / R::LPR;
+  for (int b = r0; b < r1; b += R::RPI * kUnroll) {
     uint4 raw[kUnroll];
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int r = r0 + i * RPI + rg;
-      raw[i] = r < n ? ld_kv(Vb + ((size_t)r * D + col * EPL) * ES) : make_uint4(0, 0, 0, 0);
+      const int r = b + i * R::RPI + rg;
+      raw[i] = r < r1 ? ld_kv(Vb + ((size_t)r * D + col * R::EPL) * R::ES) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int r = r0 + i * RPI + rg;
-      const float w = r < n ? wts[r] : 0.f;
-      float f[EPL];
+      const int r = b + i * R::RPI + rg;
+      const float wr = r < r1 ? w[r - r0] : 0.f;
+      float f[R::EPL];
       St<DT>::unpack(raw[i], f);
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) acc[j] = fmaf(w, f[j], acc[j]);
+      for (int j = 0; j < R::EPL; ++j) acc[j] = fmaf(wr, f[j], acc[j]);
     }
   }
-  if (with_new && rg == 0) {
-    const float w = wts[n];
-    float f[EPL];
-    St<DT>::unpack(ld16((const char*)io.v + in_off), f);
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) acc[j] = fmaf(w, f[j], acc[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) red[rg * D + col * EPL + j] = acc[j];
-  __syncthreads();
-  for (int i = tid; i < D; i += kNT) {
-    float s = 0.f;
-#pragma unroll 4
-    for (int g = 0; g < RPI; ++g) s += red[g * D + i];
-    io.out[(size_t)u * D + i] = (float)((double)s * invL);
-  }
+}
 
-  // ---- the head's policy: score update, victim, in-place write
+// Dot of q with one input row of unit u, held by row group 0 (threads
+// [0, LPR)); every lane of the group receives the value.
+template <int DT, int D>
+__device__ inline float group0_dot(const float* qf, const void* rows, int u) {
+  using R = Rows<DT, D>;
+  const int col = threadIdx.x % R::LPR;
+  float f[R::EPL];
+  St<DT>::unpack(ld16((const char*)rows + ((size_t)u * D + col * R::EPL) * R::ES), f);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < R::EPL; ++j) s = fmaf(qf[j], f[j], s);
+  return group_sum<R::LPR>(s);
+}
+
+// Per-lane partial outputs -> red[rg][d]; after a barrier column i's total is
+// the sum over row groups of red[g][i].
+template <int DT, int D>
+__device__ inline void stash_groups(const float* acc, float* red) {
+  using R = Rows<DT, D>;
+  const int col = threadIdx.x % R::LPR, rg = threadIdx.x / R::LPR;
+#pragma unroll
+  for (int j = 0; j < R::EPL; ++j) red[rg * D + col * R::EPL + j] = acc[j];
+}
+
+// The head's policy after attention: H2O score update and victim, or the
+// positional rule; writes token t's key/value/score/position into its slot.
+// wts[r] = exp(l_r - M) for the n kept slots (read for H2O heads only),
+// e_new = exp(l_t - M), invL = 1 / (sum of every weight).  Control flow is
+// uniform over the workgroup; contains barriers.
+template <int DT, int D>
+__device__ inline void policy_step(const Shape& sh, const LayerCache& c, const DecodeIO& io, const HeadMeta& m,
+                                   int u, int n, const float* wts, float e_new, double invL, MinKey* kscr) {
+  using R = Rows<DT, D>;
+  const int tid = threadIdx.x;
+  const int t = io.t;
+  const size_t slot0 = (size_t)u * c.cap;
   int wslot = -1;        // slot that receives token t
   int evicted = -1;
   double s_new = 0.0;
@@ -178,7 +170,7 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
         if (key_less(k, best)) best = k;
       }
     }
-    s_new = (double)wts[n] * invL;
+    s_new = (double)e_new * invL;
     if (tid == 0 && t <= lim) {
       const MinKey k{s_new, t, n};
       if (key_less(k, best)) best = k;
@@ -209,9 +201,13 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
   }
   if (wslot >= 0) {
     __syncthreads();                           // every read of the slot is done
-    if (tid < LPR) {
-      st16(Kb + ((size_t)wslot * D + tid * EPL) * ES, ld16((const char*)io.k + ((size_t)u * D + tid * EPL) * ES));
-      st16(Vb + ((size_t)wslot * D + tid * EPL) * ES, ld16((const char*)io.v + ((size_t)u * D + tid * EPL) * ES));
+    char* Kb = (char*)c.K + slot0 * D * R::ES;
+    char* Vb = (char*)c.V + slot0 * D * R::ES;
+    if (tid < R::LPR) {
+      const size_t src = ((size_t)u * D + tid * R::EPL) * R::ES;
+      const size_t dst = ((size_t)wslot * D + tid * R::EPL) * R::ES;
+      st16(Kb + dst, ld16((const char*)io.k + src));
+      st16(Vb + dst, ld16((const char*)io.v + src));
     }
     if (tid == 0) {
       c.S[slot0 + wslot] = s_new;
@@ -223,28 +219,233 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
   if (tid == 0 && io.evicted && m.policy != HASH) io.evicted[u] = evicted;
 }
 
+// ------------------------------------------------------------------ fused
 template <int DT, int D>
-hipError_t launch_fused_t(const Shape& sh, const LayerCache& c, const DecodeIO& io, hipStream_t st) {
-  const size_t lds = (size_t)(c.cap + 1) * sizeof(float);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_fused_kernel<DT, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+__global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, DecodeIO io) {
+  using R = Rows<DT, D>;
+  extern __shared__ float wts[];                 // [cap + 1]
+  __shared__ float red[R::RPI * D];
+  __shared__ float fscr[kNT / kWave];
+  __shared__ double dscr[kNT / kWave];
+  __shared__ MinKey kscr[kNT / kWave];
+
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int col = tid % R::LPR;
+  const int rg = tid / R::LPR;
+  const HeadMeta m = c.meta[u % sh.heads];
+  const int n = c.count[u];
+  const int with_new = m.policy == HASH ? 0 : 1;  // HASH: token t is already in a slot
+  const size_t slot0 = (size_t)u * c.cap;
+  const char* Kb = (const char*)c.K + slot0 * D * R::ES;
+  const char* Vb = (const char*)c.V + slot0 * D * R::ES;
+
+  float qf[R::EPL];
+  St<DT>::unpack(ld16((const char*)io.q + ((size_t)u * D + col * R::EPL) * R::ES), qf);
+
+  row_logits<DT, D>(Kb, qf, sh.scale, 0, n, wts, nullptr);
+  if (with_new && rg == 0) {
+    const float s = group0_dot<DT, D>(qf, io.k, u) * sh.scale;
+    if (col == 0) wts[n] = s;
   }
-  hipLaunchKernelGGL((decode_fused_kernel<DT, D>), dim3(sh.units()), dim3(kNT), lds, st, sh, c, io);
+  __syncthreads();
+
+  // softmax over the n kept slots (+ the new token)
+  const int nt = n + with_new;
+  float mx = -INFINITY;
+  for (int r = tid; r < nt; r += kNT) mx = fmaxf(mx, wts[r]);
+  mx = block_max<kNT>(mx, fscr);
+  double ls = 0.0;
+  for (int r = tid; r < nt; r += kNT) {
+    const float w = expf(wts[r] - mx);
+    wts[r] = w;
+    ls += (double)w;
+  }
+  const double L = block_sum<kNT>(ls, dscr);     // barriers inside: wts[] complete
+  const double invL = 1.0 / L;
+
+  // output o = sum_j w_j v_j / L
+  float acc[R::EPL];
+#pragma unroll
+  for (int j = 0; j < R::EPL; ++j) acc[j] = 0.f;
+  row_values<DT, D>(Vb, wts, 0, n, acc);
+  if (with_new && rg == 0) {
+    const float w = wts[n];
+    float f[R::EPL];
+    St<DT>::unpack(ld16((const char*)io.v + ((size_t)u * D + col * R::EPL) * R::ES), f);
+#pragma unroll
+    for (int j = 0; j < R::EPL; ++j) acc[j] = fmaf(w, f[j], acc[j]);
+  }
+  stash_groups<DT, D>(acc, red);
+  __syncthreads();
+  for (int i = tid; i < D; i += kNT) {
+    float s = 0.f;
+#pragma unroll 4
+    for (int g = 0; g < R::RPI; ++g) s += red[g * D + i];
+    io.out[(size_t)u * D + i] = (float)((double)s * invL);
+  }
+  policy_step<DT, D>(sh, c, io, m, u, n, wts, with_new ? wts[n] : 0.f, invL, kscr);
+}
+
+// ------------------------------------------------------------------ split
+// One chunk [c0, c0 + chunk) of one unit's kept slots:
+// part = (unnormalised output[d], chunk maximum, chunk sum of exp(l - max)).
+template <int DT, int D>
+__global__ KVE_DECODE_ATTR void decode_partial_kernel(Shape sh, LayerCache c, DecodeIO io, SplitScratch sp) {
+  using R = Rows<DT, D>;
+  extern __shared__ float lg[];                  // [chunk]
+  __shared__ float red[R::RPI * D];
+  __shared__ float fscr[kNT / kWave];
+  __shared__ double dscr[kNT / kWave];
+  const int u = blockIdx.y;
+  const int ch = blockIdx.x;
+  const int n = c.count[u];
+  const int c0 = ch * sp.chunk;
+  if (c0 >= n) return;                           // uniform: the whole workgroup leaves
+  const int c1 = min(n, c0 + sp.chunk);
+  const int tid = threadIdx.x;
+  const int col = tid % R::LPR;
+  const HeadMeta m = c.meta[u % sh.heads];
+  const size_t slot0 = (size_t)u * c.cap;
+  const char* Kb = (const char*)c.K + slot0 * D * R::ES;
+  const char* Vb = (const char*)c.V + slot0 * D * R::ES;
+  float qf[R::EPL];
+  St<DT>::unpack(ld16((const char*)io.q + ((size_t)u * D + col * R::EPL) * R::ES), qf);
+
+  row_logits<DT, D>(Kb, qf, sh.scale, c0, c1, lg, m.policy == H2O ? sp.logits + slot0 : nullptr);
+  __syncthreads();
+  const int len = c1 - c0;
+  float mx = -INFINITY;
+  for (int r = tid; r < len; r += kNT) mx = fmaxf(mx, lg[r]);
+  mx = block_max<kNT>(mx, fscr);
+  double ls = 0.0;
+  for (int r = tid; r < len; r += kNT) {
+    const float w = expf(lg[r] - mx);
+    lg[r] = w;
+    ls += (double)w;
+  }
+  const double L = block_sum<kNT>(ls, dscr);     // barriers inside: lg[] complete
+  float acc[R::EPL];
+#pragma unroll
+  for (int j = 0; j < R::EPL; ++j) acc[j] = 0.f;
+  row_values<DT, D>(Vb, lg, c0, c1, acc);
+  stash_groups<DT, D>(acc, red);
+  __syncthreads();
+  float* part = sp.part + ((size_t)u * sp.max_chunks + ch) * (D + 2);
+  for (int i = tid; i < D; i += kNT) {
+    float s = 0.f;
+#pragma unroll 4
+    for (int g = 0; g < R::RPI; ++g) s += red[g * D + i];
+    part[i] = s;
+  }
+  if (tid == 0) {
+    part[D] = mx;
+    part[D + 1] = (float)L;
+  }
+}
+
+// Merges a unit's chunks, normalises the output and runs the policy step.
+template <int DT, int D>
+__global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, DecodeIO io, SplitScratch sp) {
+  using R = Rows<DT, D>;
+  extern __shared__ float wts[];                 // [cap]: exact weights (H2O units)
+  __shared__ float gf[kMaxChunks];
+  __shared__ double dscr[kNT / kWave];
+  __shared__ MinKey kscr[kNT / kWave];
+  __shared__ float snew_s;
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int col = tid % R::LPR;
+  const int rg = tid / R::LPR;
+  const HeadMeta m = c.meta[u % sh.heads];
+  const int n = c.count[u];
+  const int with_new = m.policy == HASH ? 0 : 1;
+  const int nch = (n + sp.chunk - 1) / sp.chunk;
+  const float* part = sp.part + (size_t)u * sp.max_chunks * (D + 2);
+  const size_t slot0 = (size_t)u * c.cap;
+
+  if (with_new && rg == 0) {
+    float qf[R::EPL];
+    St<DT>::unpack(ld16((const char*)io.q + ((size_t)u * D + col * R::EPL) * R::ES), qf);
+    const float s = group0_dot<DT, D>(qf, io.k, u) * sh.scale;
+    if (col == 0) snew_s = s;
+  }
+  __syncthreads();
+  const float s_new = with_new ? snew_s : -INFINITY;
+  float M = s_new;
+  for (int ch = 0; ch < nch; ++ch) M = fmaxf(M, part[(size_t)ch * (D + 2) + D]);
+  const float e_new = with_new ? expf(s_new - M) : 0.f;
+  for (int ch = tid; ch < nch; ch += kNT) gf[ch] = expf(part[(size_t)ch * (D + 2) + D] - M);
+  double ls = 0.0;
+  if (m.policy == H2O) {
+    // exact weights of every kept slot, recomputed from the stored logits
+    const float* lgs = sp.logits + slot0;
+    for (int r = tid; r < n; r += kNT) {
+      const float w = expf(lgs[r] - M);
+      wts[r] = w;
+      ls += (double)w;
+    }
+  } else {
+    for (int ch = tid; ch < nch; ch += kNT)
+      ls += (double)part[(size_t)ch * (D + 2) + D + 1] * (double)expf(part[(size_t)ch * (D + 2) + D] - M);
+  }
+  const double L = block_sum<kNT>(ls, dscr) + (double)e_new;  // barriers inside: wts[], gf[] complete
+  const double invL = 1.0 / L;
+  for (int i = tid; i < D; i += kNT) {
+    float s = 0.f;
+    for (int ch = 0; ch < nch; ++ch) s = fmaf(part[(size_t)ch * (D + 2) + i], gf[ch], s);
+    if (with_new) {
+      float f[R::EPL];
+      St<DT>::unpack(ld16((const char*)io.v + ((size_t)u * D + (i / R::EPL) * R::EPL) * R::ES), f);
+      s = fmaf(e_new, f[i % R::EPL], s);
+    }
+    io.out[(size_t)u * D + i] = (float)((double)s * invL);
+  }
+  policy_step<DT, D>(sh, c, io, m, u, n, wts, e_new, invL, kscr);
+}
+
+hipError_t set_lds(const void* fn, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+template <int DT, int D>
+hipError_t launch_t(const Shape& sh, const LayerCache& c, const DecodeIO& io, const SplitScratch* sp,
+                    hipStream_t st) {
+  if (!sp) {
+    const size_t lds = (size_t)(c.cap + 1) * sizeof(float);
+    hipError_t e = set_lds((const void*)decode_fused_kernel<DT, D>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_fused_kernel<DT, D>), dim3(sh.units()), dim3(kNT), lds, st, sh, c, io);
+    return hipGetLastError();
+  }
+  const size_t lds_p = (size_t)sp->chunk * sizeof(float);
+  const size_t lds_c = (size_t)c.cap * sizeof(float);
+  hipError_t e = set_lds((const void*)decode_partial_kernel<DT, D>, lds_p);
+  if (e == hipSuccess) e = set_lds((const void*)decode_combine_kernel<DT, D>, lds_c);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_partial_kernel<DT, D>), dim3(sp->max_chunks, sh.units()), dim3(kNT), lds_p, st, sh, c,
+                     io, *sp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<DT, D>), dim3(sh.units()), dim3(kNT), lds_c, st, sh, c, io, *sp);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_fused(const Shape& sh, const LayerCache& c, const DecodeIO& io, hipStream_t st) {
+hipError_t launch_decode(const Shape& sh, const LayerCache& c, const DecodeIO& io, const SplitScratch* sp,
+                         hipStream_t st) {
+  if (sp && (sp->max_chunks < 1 || sp->max_chunks > kMaxChunks || sp->chunk < 1 ||
+             (long long)sp->max_chunks * sp->chunk < c.cap))
+    return hipErrorInvalidValue;
   switch (sh.dtype * 1000 + sh.d) {
-    case F32 * 1000 + 64: return launch_fused_t<F32, 64>(sh, c, io, st);
-    case F32 * 1000 + 128: return launch_fused_t<F32, 128>(sh, c, io, st);
-    case F16 * 1000 + 64: return launch_fused_t<F16, 64>(sh, c, io, st);
-    case F16 * 1000 + 128: return launch_fused_t<F16, 128>(sh, c, io, st);
-    case BF16 * 1000 + 64: return launch_fused_t<BF16, 64>(sh, c, io, st);
-    case BF16 * 1000 + 128: return launch_fused_t<BF16, 128>(sh, c, io, st);
+    case F32 * 1000 + 64: return launch_t<F32, 64>(sh, c, io, sp, st);
+    case F32 * 1000 + 128: return launch_t<F32, 128>(sh, c, io, sp, st);
+    case F16 * 1000 + 64: return launch_t<F16, 64>(sh, c, io, sp, st);
+    case F16 * 1000 + 128: return launch_t<F16, 128>(sh, c, io, sp, st);
+    case BF16 * 1000 + 64: return launch_t<BF16, 64>(sh, c, io, sp, st);
+    case BF16 * 1000 + 128: return launch_t<BF16, 128>(sh, c, io, sp, st);
   }
   return hipErrorInvalidValue;
 }

@@ -36,10 +36,35 @@ kve_status fail(kve_status s, const char* fmt, ...) {
 }
 
 constexpr int kMaxContext = 32768;     // LDS-resident per-unit slot lists
+// Layers whose slot stride exceeds this use the split decode (chunks of
+// kSplitChunk slots); both can be overridden at create time through the
+// environment (KVEVICT_SPLIT_ABOVE, KVEVICT_SPLIT_CHUNK) to exercise either
+// path at any size.
+constexpr int kSplitAbove = 1024;
+constexpr int kSplitChunk = 512;
 constexpr int kMaxHashBudget = 16384;  // replay keeps sketches and positions in LDS
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  char* end = nullptr;
+  const long x = std::strtol(v, &end, 10);
+  return (end && *end == 0 && x >= 0 && x <= (1 << 30)) ? (int)x : dflt;
+}
+
+struct SplitPolicy {
+  int above, chunk;
+};
+
+SplitPolicy split_policy() {
+  SplitPolicy p{env_int("KVEVICT_SPLIT_ABOVE", kSplitAbove), env_int("KVEVICT_SPLIT_CHUNK", kSplitChunk)};
+  if (p.chunk < 16) p.chunk = kSplitChunk;
+  return p;
+}
+
 
 int elem_size(int dtype) { return dtype == KVE_F32 ? 4 : 2; }
 
@@ -55,6 +80,7 @@ int head_capacity(int policy, int heavy, int recent, int max_context) {
 // Per-layer summary of the head table.
 struct LayerInfo {
   int cap = 0;
+  bool split = false;
   bool any_h2o = false, any_hash = false, any_special = false;
   int max_hash_budget = 0;
   std::vector<int32_t> h2o_units, hash_units;
@@ -123,6 +149,14 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
         if (p == KVE_HASH) li.hash_units.push_back(b * c->heads + h);
       }
   }
+  const SplitPolicy sp = split_policy();
+  for (int l = 0; l < c->layers; ++l) {
+    LayerInfo& li = (*info)[l];
+    li.split = li.cap > sp.above;
+    if (li.split && (li.cap + sp.chunk - 1) / sp.chunk > kve::kMaxChunks)
+      return fail(KVE_EUNSUPPORTED, "layer %d: %d slots need more than %d chunks of %d", l, li.cap,
+                  kve::kMaxChunks, sp.chunk);
+  }
   if (need_bitmap && (!c->keep_token_bitmap || c->vocab < 1))
     return fail(KVE_EINVAL, "SPECIAL heads need keep_token_bitmap and vocab >= 1");
   if (need_proj && (!c->lsh_proj_bf16 || c->sketch_bits != 32))
@@ -144,6 +178,7 @@ struct Plan {
 
 struct Layer {
   kve::LayerCache cache{};
+  kve::SplitScratch split{};   // chunk == 0: fused path
   LayerInfo info;
   kve::UnitList h2o{nullptr, 0}, hash{nullptr, 0};
   int position = -1;   // next decode position; -1 before prefill
@@ -165,10 +200,12 @@ struct kve_ctx {
   bool sync_check = false;
 };
 
+
 namespace {
 
 size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* base, kve_ctx* ctx) {
   Plan pl(base);
+  const SplitPolicy sp = split_policy();
   const size_t U = (size_t)c->batch * c->heads;
   const size_t d = c->head_dim, es = elem_size(c->dtype);
   const size_t N = c->max_context;
@@ -184,6 +221,13 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
   auto* colsum = pl.take<double>(U * N);
   auto* qsk = any_hash ? pl.take<uint32_t>(U * N) : nullptr;
   auto* ksk = any_hash ? pl.take<uint32_t>(U * N) : nullptr;
+  // split-decode scratch, sized for the largest split layer
+  size_t split_cap = 0;
+  for (const auto& li : info)
+    if (li.cap > sp.above) split_cap = std::max(split_cap, (size_t)li.cap);
+  const int max_chunks = split_cap ? (int)((split_cap + sp.chunk - 1) / sp.chunk) : 0;
+  float* part = split_cap ? pl.take<float>(U * max_chunks * (d + 2)) : nullptr;
+  float* logits = split_cap ? pl.take<float>(U * split_cap) : nullptr;
   if (ctx) {
     ctx->meta = meta;
     ctx->bitmap = bitmap;
@@ -211,6 +255,8 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
     if (ctx) {
       Layer& L = ctx->layers[l];
       L.cache = lc;
+      if (li.cap > sp.above)
+        L.split = {part, logits, sp.chunk, (int32_t)((li.cap + sp.chunk - 1) / sp.chunk)};
       L.info = li;
       L.h2o = {h2o_ids, (int32_t)li.h2o_units.size()};
       L.hash = {hash_ids, (int32_t)li.hash_units.size()};
@@ -371,7 +417,7 @@ kve_status kvevict_decode_step(kve_handle h, int32_t layer, const void* q, const
   if (L.hash.n) e = kve::launch_hash_evict(sh, L.cache, L.hash, L.position, q, k, v, evicted_pos, st);
   if (e == hipSuccess) {
     const kve::DecodeIO io{q, k, v, token_ids, h->bitmap, h->cfg.vocab, out, evicted_pos, L.position};
-    e = kve::launch_decode_fused(sh, L.cache, io, st);
+    e = kve::launch_decode(sh, L.cache, io, L.split.chunk ? &L.split : nullptr, st);
   }
   if (e != hipSuccess) return dev(e, "decode launch");
   s = finish(h, st, "decode_step");

@@ -94,10 +94,21 @@ struct DecodeIO {
   int32_t t;                // position of the new token
 };
 
-// Attention + score update + policy step for every unit of the layer, one
-// workgroup per unit.
-hipError_t launch_decode_fused(const Shape& sh, const LayerCache& c, const DecodeIO& io,
-                               hipStream_t st);
+// Scratch of the split decode: per-chunk partials [U][max_chunks][d + 2]
+// (unnormalised output, chunk maximum, chunk sum) and raw logits [U][cap].
+constexpr int kMaxChunks = 64;
+struct SplitScratch {
+  float* part;
+  float* logits;
+  int32_t chunk;        // slots per chunk
+  int32_t max_chunks;   // ceil(cap / chunk), <= kMaxChunks
+};
+
+// Attention + score update + policy step for every unit of the layer: one
+// workgroup per unit when sp is null, else partials over (unit, chunk) then a
+// per-unit combine.
+hipError_t launch_decode(const Shape& sh, const LayerCache& c, const DecodeIO& io,
+                         const SplitScratch* sp, hipStream_t st);
 
 
 }  // namespace kve

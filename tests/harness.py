@@ -93,7 +93,7 @@ def check_unit(w: Workload, inp_cpu: LayerInputs, r: GpuRun, b: int, h: int, pol
     if p == H2O:
         rep = lockstep.check_h2o(Q, K, V, P, hh, rr, sc, g, steps=T)
     elif p == HASH:
-        Wp = inp_cpu.proj.float().double().numpy()
+        Wp = inp_cpu.proj.float().double().cpu().numpy()
         rep = lockstep.check_hash(Q, K, V, Wp, P, hh, sc, g, steps=T)
     else:
         rep = lockstep.check_fastgen(p, Q, K, V, P, sc, g, heavy=hh, recent=rr,

@@ -20,8 +20,19 @@ from workloads.generate import generate_layer
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["fused", "split"])
+def decode_path(request, monkeypatch):
+    """Runs a test with the one-workgroup-per-unit decode and again with the
+    split decode forced at small sizes (chunks of 32 slots)."""
+    if request.param == "split":
+        monkeypatch.setenv("KVEVICT_SPLIT_ABOVE", "0")
+        monkeypatch.setenv("KVEVICT_SPLIT_CHUNK", "32")
+    return request.param
+
+
 def run_and_check(w, policy=None, heavy=None, recent=None, prompt_out=False, seed=0, units=None):
-    print(f"\n[parity] {w.name} B={w.batch} H={w.heads} d={w.head_dim} {w.dtype} P={w.prompt} "
+    import os
+    print(f"\n[parity] split_above={os.environ.get('KVEVICT_SPLIT_ABOVE', '-')} {w.name} B={w.batch} H={w.heads} d={w.head_dim} {w.dtype} P={w.prompt} "
           f"T={w.steps} seed={seed}", flush=True)
     inp = generate_layer(w, 0, "cpu", seed)
     kv = harness.make_cache(w, inp, policy, heavy, recent)
@@ -37,18 +48,18 @@ def run_and_check(w, policy=None, heavy=None, recent=None, prompt_out=False, see
     return rep, r
 
 
-def test_tiny_h2o_full_size():
+def test_tiny_h2o_full_size(decode_path):
     rep, _ = run_and_check(configs.get("tiny_h2o"), prompt_out=True)
     assert rep.decisions == 2 * 64
 
 
-def test_h2o_fp16_scaled():
+def test_h2o_fp16_scaled(decode_path):
     w = configs.scaled("opt6.7b_layer_h2o", batch=2, heads=4, prompt=300, steps=90)
     assert (w.heavy, w.recent) == (30, 30)
     run_and_check(w, prompt_out=True)
 
 
-def test_h2o_bf16_scaled():
+def test_h2o_bf16_scaled(decode_path):
     w = configs.scaled("opt30b_decode_h2o", batch=2, heads=3, prompt=700, steps=60)
     run_and_check(w)
 
@@ -59,20 +70,20 @@ def test_h2o_fp32_d128():
     run_and_check(w, prompt_out=True)
 
 
-def test_fastgen_scaled():
+def test_fastgen_scaled(decode_path):
     w = configs.scaled("llama65b_fastgen", batch=2, heads=8, prompt=500, steps=60)
     assert (w.local_window, w.freq_heavy) == (125, 50)
     run_and_check(w, prompt_out=True)
 
 
-def test_hash_scaled():
+def test_hash_scaled(decode_path):
     w = configs.scaled("hashevict_lsh", batch=2, heads=4, prompt=600, steps=80)
     assert w.hash_budget == 300
     rep, _ = run_and_check(w)
     assert rep.decisions == 8 * 80
 
 
-def test_budget_covering_context_is_full_attention():
+def test_budget_covering_context_is_full_attention(decode_path):
     """heavy + recent >= P + T: nothing is evicted; outputs equal causal attention."""
     w = configs.scaled("opt30b_decode_h2o", batch=1, heads=2, prompt=100, steps=40)
     N = w.context
@@ -82,7 +93,7 @@ def test_budget_covering_context_is_full_attention():
 
 @pytest.mark.parametrize("P,T,hh,rc", [(1, 30, 4, 4), (5, 40, 8, 8), (90, 30, 12, 0), (90, 30, 0, 12),
                                        (64, 64, 16, 16), (257, 20, 100, 27)])
-def test_h2o_edge_shapes(P, T, hh, rc):
+def test_h2o_edge_shapes(P, T, hh, rc, decode_path):
     """Prompt of one token, prompt shorter than the budget (the cache grows),
     no recent window (the new token may be evicted at once), no heavy part,
     tile-aligned and ragged prompts."""
@@ -90,13 +101,13 @@ def test_h2o_edge_shapes(P, T, hh, rc):
     run_and_check(w, policy=[H2O] * 2, heavy=[hh] * 2, recent=[rc] * 2)
 
 
-def test_special_without_kept_prompt_tokens():
+def test_special_without_kept_prompt_tokens(decode_path):
     w = configs.scaled("llama65b_fastgen", batch=1, heads=4, prompt=20, steps=30)
     w = dataclasses.replace(w, special_ids=(31990,), punct_ids=(31991,))   # (almost) never drawn
     run_and_check(w, policy=[SPECIAL, FULL, LOCAL, SPECIAL], heavy=[0] * 4, recent=[0, 0, 7, 0])
 
 
-def test_hash_prompt_shorter_than_budget():
+def test_hash_prompt_shorter_than_budget(decode_path):
     w = configs.scaled("hashevict_lsh", batch=1, heads=2, prompt=50, steps=40)
     run_and_check(w, policy=[HASH] * 2, heavy=[70] * 2, recent=[0] * 2)
 
