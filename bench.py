@@ -100,20 +100,47 @@ def cpu_baseline(w, n_units: int, workers: int):
 
 # ---------------------------------------------------------------- GPU
 
-def algorithmic_bytes_per_unit(w) -> float:
-    """Bytes the method itself moves per unit-step in the fused decode kernel:
-    kept K and V read, score read and write (counted at 4 bytes each, the
-    float32 minimum), position read, the step's q/k/v, the victim's K/V write
-    and the fp32 output."""
+def decode_bytes_per_layer_step(w, ids=None) -> float:
+    """Algorithmic bytes of one layer's decode step, averaged over the T steps:
+    per unit, the kept K and V rows read (n slots x d x s x 2), the per-slot
+    metadata the policy needs (H2O: score read and write at the 4-byte float32
+    minimum plus the position, 12 B; HashEvict: sketch and position, 8 B), the
+    step's q, k, v, the new token's K/V write and the fp32 output.  n is the
+    unit's kept count at that step: B for H2O and HashEvict, W for the local
+    window, t for the full cache, and for the special policy the number of
+    earlier positions whose id is kept (counted from the ids)."""
     s = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
     d = w.head_dim
-    if w.family != "h2o":
-        raise NotImplementedError("the bench's byte model covers the H2O workloads")
-    B = w.heavy + w.recent
-    return B * d * s * 2 + B * (4 + 4) + B * 4 + 3 * d * s + 2 * d * s + 4 * d
+    io = 3 * d * s + 2 * d * s + 4 * d
+    pol, hv, rc = w.policy_table(0)
+    if w.family == "h2o":
+        B = w.heavy + w.recent
+        return w.units_per_layer * (B * d * s * 2 + B * 12 + io)
+    if w.family == "hash":
+        B = w.hash_budget
+        return w.units_per_layer * (B * d * s * 2 + B * 8 + io + 4)
+    import numpy as np
+    P, T = w.prompt, w.steps
+    keep = np.isin(np.asarray(ids), np.array(w.keep_ids()))           # [batch, N]
+    kept_before = np.cumsum(keep, axis=1) - keep                       # kept ids strictly before t
+    total = 0.0
+    for h in range(w.heads):
+        for b in range(w.batch):
+            for st in range(T):
+                t = P + st
+                if pol[h] == 1:
+                    n, meta = hv[h] + rc[h], 12
+                elif pol[h] == 2:
+                    n, meta = min(t, rc[h]), 0
+                elif pol[h] == 0:
+                    n, meta = t, 0
+                else:
+                    n, meta = int(kept_before[b, t]), 0
+                total += n * d * s * 2 + n * meta + io
+    return total / T
 
 
-def run_gpu(w, steps: int, warmup: int, sample_every: int):
+def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0):
     import numpy as np
     import torch
     from budgeted_decode_attention_amd import KVCache
@@ -121,6 +148,13 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int):
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if calib_mib:
+        # a plain copy of known size, for scaling hardware byte counters
+        a = torch.ones(calib_mib << 18, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     t0 = time.perf_counter()
     inputs = [generate_layer(w, l, dev, 0) for l in range(w.layers)]
     torch.cuda.synchronize()
@@ -186,11 +220,13 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ids0 = inputs[0].ids.cpu().numpy() if inputs[0].ids is not None else None
     group_ms = [a.elapsed_time(b) for a, b in samples]
     kernel_us = 1e3 * sum(group_ms) / (len(group_ms) * w.layers)
     return {"wall_s": wall, "gen_s": gen_s, "prefill_ms": prefill_ms, "decode_ms": decode_ms,
             "kernel_us": kernel_us, "n_samples": len(group_ms) * w.layers,
-            "finite": bool(torch.isfinite(out).all().item())}
+            "finite": bool(torch.isfinite(out).all().item()), "ids0": ids0,
+            "split": kv.capacity(0) > 1024}
 
 
 def main():
@@ -199,8 +235,11 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cpu-units", type=int, default=256, help="oracle sample size for the CPU baseline")
+    ap.add_argument("--cpu-units", type=int, default=0,
+                    help="oracle sample size for the CPU baseline (0: per-workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--sample-every", type=int, default=4,
                     help="event-time the per-layer decode launches of every k-th decode step")
     a = ap.parse_args()
@@ -214,25 +253,31 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         workers = min(16, len(os.sched_getaffinity(0)))
-        cpu = cpu_baseline(w, a.cpu_units, workers)
+        n_units = a.cpu_units or {"h2o": 256, "fastgen": 64, "hash": 32}[w.family]
+        cpu = cpu_baseline(w, n_units, workers)
         print(f"[bench] cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
 
-    r = run_gpu(w, a.steps, a.warmup, a.sample_every)
+    r = run_gpu(w, a.steps, a.warmup, a.sample_every, a.calibration_copy_mib)
     ms = 1e3 * r["wall_s"] / a.steps
     tokens = w.batch * w.steps
-    bpu = algorithmic_bytes_per_unit(w)
-    bytes_launch = bpu * w.units_per_layer
+    bytes_launch = decode_bytes_per_layer_step(w, r["ids0"])
     achieved = bytes_launch / (r["kernel_us"] * 1e-6) / 1e9
+    kernel = ("decode_partial_kernel + decode_combine_kernel" if r["split"] else "decode_fused_kernel")
+    if w.family == "hash":
+        kernel = "hash_evict_kernel + " + kernel
     line = {
         "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "batch": w.batch, "heads": w.heads,
                    "head_dim": w.head_dim, "prompt": w.prompt, "decode_steps": w.steps,
-                   "budget": (f"{w.heavy} heavy + {w.recent} recent" if w.family == "h2o" else w.family)},
+                   "budget": {"h2o": f"{w.heavy} heavy + {w.recent} recent",
+                              "fastgen": f"per head: full / local {w.local_window} / special+punct / "
+                                         f"{w.freq_heavy} frequency + {w.local_window} local",
+                              "hash": f"{w.hash_budget} slots, {w.sketch_bits}-bit sketches"}[w.family]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_fused", "bytes_per_launch": bytes_launch,
+                     "kernel": kernel, "bytes_per_launch": bytes_launch,
                      "kernel_us": r["kernel_us"], "launches_timed": r["n_samples"]},
         "cpu_baseline": cpu,
         "detail": {"prefill_ms_per_step": r["prefill_ms"], "decode_ms_per_step": r["decode_ms"],

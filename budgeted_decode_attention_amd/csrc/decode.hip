@@ -345,10 +345,11 @@ __global__ KVE_DECODE_ATTR void decode_partial_kernel(Shape sh, LayerCache c, De
 }
 
 // Merges a unit's chunks, normalises the output and runs the policy step.
+// The unit's chunk partials are staged in LDS with coalesced loads first.
 template <int DT, int D>
 __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, DecodeIO io, SplitScratch sp) {
   using R = Rows<DT, D>;
-  extern __shared__ float wts[];                 // [cap]: exact weights (H2O units)
+  extern __shared__ float lds[];                 // [max_chunks * (D + 2)] partials, then [cap] weights
   __shared__ float gf[kMaxChunks];
   __shared__ double dscr[kNT / kWave];
   __shared__ MinKey kscr[kNT / kWave];
@@ -361,8 +362,11 @@ __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, De
   const int n = c.count[u];
   const int with_new = m.policy == HASH ? 0 : 1;
   const int nch = (n + sp.chunk - 1) / sp.chunk;
-  const float* part = sp.part + (size_t)u * sp.max_chunks * (D + 2);
   const size_t slot0 = (size_t)u * c.cap;
+  float* part = lds;
+  float* wts = lds + (size_t)sp.max_chunks * (D + 2);
+  const float* gpart = sp.part + (size_t)u * sp.max_chunks * (D + 2);
+  for (int i = tid; i < nch * (D + 2); i += kNT) part[i] = gpart[i];
 
   if (with_new && rg == 0) {
     float qf[R::EPL];
@@ -373,9 +377,9 @@ __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, De
   __syncthreads();
   const float s_new = with_new ? snew_s : -INFINITY;
   float M = s_new;
-  for (int ch = 0; ch < nch; ++ch) M = fmaxf(M, part[(size_t)ch * (D + 2) + D]);
+  for (int ch = 0; ch < nch; ++ch) M = fmaxf(M, part[ch * (D + 2) + D]);
   const float e_new = with_new ? expf(s_new - M) : 0.f;
-  for (int ch = tid; ch < nch; ch += kNT) gf[ch] = expf(part[(size_t)ch * (D + 2) + D] - M);
+  for (int ch = tid; ch < nch; ch += kNT) gf[ch] = expf(part[ch * (D + 2) + D] - M);
   double ls = 0.0;
   if (m.policy == H2O) {
     // exact weights of every kept slot, recomputed from the stored logits
@@ -387,13 +391,13 @@ __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, De
     }
   } else {
     for (int ch = tid; ch < nch; ch += kNT)
-      ls += (double)part[(size_t)ch * (D + 2) + D + 1] * (double)expf(part[(size_t)ch * (D + 2) + D] - M);
+      ls += (double)part[ch * (D + 2) + D + 1] * (double)expf(part[ch * (D + 2) + D] - M);
   }
   const double L = block_sum<kNT>(ls, dscr) + (double)e_new;  // barriers inside: wts[], gf[] complete
   const double invL = 1.0 / L;
   for (int i = tid; i < D; i += kNT) {
     float s = 0.f;
-    for (int ch = 0; ch < nch; ++ch) s = fmaf(part[(size_t)ch * (D + 2) + i], gf[ch], s);
+    for (int ch = 0; ch < nch; ++ch) s = fmaf(part[ch * (D + 2) + i], gf[ch], s);
     if (with_new) {
       float f[R::EPL];
       St<DT>::unpack(ld16((const char*)io.v + ((size_t)u * D + (i / R::EPL) * R::EPL) * R::ES), f);
@@ -420,7 +424,7 @@ hipError_t launch_t(const Shape& sh, const LayerCache& c, const DecodeIO& io, co
     return hipGetLastError();
   }
   const size_t lds_p = (size_t)sp->chunk * sizeof(float);
-  const size_t lds_c = (size_t)c.cap * sizeof(float);
+  const size_t lds_c = ((size_t)sp->max_chunks * (D + 2) + c.cap) * sizeof(float);
   hipError_t e = set_lds((const void*)decode_partial_kernel<DT, D>, lds_p);
   if (e == hipSuccess) e = set_lds((const void*)decode_combine_kernel<DT, D>, lds_c);
   if (e != hipSuccess) return e;

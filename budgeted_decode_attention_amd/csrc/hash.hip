@@ -207,9 +207,28 @@ __global__ __launch_bounds__(kNT) void hash_evict_kernel(Shape sh, LayerCache c,
   if (n >= B) {
     const uint32_t qs = sk2[0];
     uint64_t best = 0;
-    for (int s = tid; s < n; s += kNT) {
-      const uint64_t key = ((uint64_t)__popc(qs ^ c.sk[slot0 + s]) << 48) |
-                           ((uint64_t)(0xFFFFFF - c.pos[slot0 + s]) << 24) | (uint64_t)s;
+    // four slots per 16-byte load of sketches and of positions when the unit's
+    // first slot is 16-byte aligned (slot0 % 4 == 0); the remainder, or every
+    // slot otherwise, one at a time
+    const uint32_t* skp = c.sk + slot0;
+    const int32_t* psp = c.pos + slot0;
+    const bool vec = ((slot0 & 3) == 0);
+    const int n4 = vec ? (n & ~3) : 0;
+    for (int s4 = tid * 4; s4 < n4; s4 += kNT * 4) {
+      const uint4 a = *reinterpret_cast<const uint4*>(skp + s4);
+      const int4 p = *reinterpret_cast<const int4*>(psp + s4);
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w};
+      const int32_t pv[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint64_t key = ((uint64_t)__popc(qs ^ av[j]) << 48) | ((uint64_t)(0xFFFFFF - pv[j]) << 24) |
+                             (uint64_t)(s4 + j);
+        best = key > best ? key : best;
+      }
+    }
+    for (int s = n4 + tid; s < n; s += kNT) {
+      const uint64_t key = ((uint64_t)__popc(qs ^ skp[s]) << 48) | ((uint64_t)(0xFFFFFF - psp[s]) << 24) |
+                           (uint64_t)s;
       best = key > best ? key : best;
     }
 #pragma unroll

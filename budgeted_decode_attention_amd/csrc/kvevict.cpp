@@ -42,6 +42,7 @@ constexpr int kMaxContext = 32768;     // LDS-resident per-unit slot lists
 // path at any size.
 constexpr int kSplitAbove = 1024;
 constexpr int kSplitChunk = 512;
+constexpr size_t kMaxSplitLds = 150 * 1024;
 constexpr int kMaxHashBudget = 16384;  // replay keeps sketches and positions in LDS
 constexpr size_t kAlign = 256;
 
@@ -156,6 +157,10 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
     if (li.split && (li.cap + sp.chunk - 1) / sp.chunk > kve::kMaxChunks)
       return fail(KVE_EUNSUPPORTED, "layer %d: %d slots need more than %d chunks of %d", l, li.cap,
                   kve::kMaxChunks, sp.chunk);
+    // the combine kernel holds a unit's chunk partials and weights in LDS
+    const size_t nch = li.split ? (size_t)(li.cap + sp.chunk - 1) / sp.chunk : 0;
+    if (li.split && (nch * (c->head_dim + 2) + li.cap) * 4 > kMaxSplitLds)
+      return fail(KVE_EUNSUPPORTED, "layer %d: %d slots exceed the split decode's LDS", l, li.cap);
   }
   if (need_bitmap && (!c->keep_token_bitmap || c->vocab < 1))
     return fail(KVE_EINVAL, "SPECIAL heads need keep_token_bitmap and vocab >= 1");
