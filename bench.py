@@ -238,6 +238,9 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=0,
                     help="oracle sample size for the CPU baseline (0: per-workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="hardware-counter passes only: keep just the first N layers resident (the per-launch "
+                         "shape is unchanged); the printed line then describes that reduced job")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--sample-every", type=int, default=4,
@@ -248,7 +251,10 @@ def main():
               f"exchange, so a multi-GPU figure is N x the one-GPU value", file=sys.stderr)
         sys.exit(2)
     from workloads import configs
+    import dataclasses
     w = configs.get(a.workload)
+    if a.layers:
+        w = dataclasses.replace(w, layers=min(a.layers, w.layers))
 
     cpu = None
     if not a.no_cpu_baseline:
