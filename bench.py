@@ -140,6 +140,32 @@ def decode_bytes_per_layer_step(w, ids=None) -> float:
     return total / T
 
 
+def counter_traffic(workload: str):
+    """HBM bytes per launch of the decode kernel from a committed counter record
+    (profiles/counters_*.txt whose `workload:` matches: FETCH_SIZE and
+    WRITE_SIZE passes scaled by a plain copy of known size), or None if there
+    is none or the kernel sources have changed since it was taken."""
+    import glob
+    import hashlib
+    for p in sorted(glob.glob(os.path.join(ROOT, "profiles", "counters_*.txt"))):
+        rec = {}
+        for line in open(p):
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+        if rec.get("workload") != workload:
+            continue
+        h = hashlib.sha256()
+        for f in rec.get("kernel_sources", "").split():
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest()[:16] != rec.get("kernel_sources_sha256"):
+            return None
+        return float(rec["traffic_bytes_per_launch"])
+    return None
+
+
 def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0):
     import numpy as np
     import torch
@@ -282,7 +308,7 @@ def main():
                                          f"{w.freq_heavy} frequency + {w.local_window} local",
                               "hash": f"{w.hash_budget} slots, {w.sketch_bits}-bit sketches"}[w.family]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(w.name),
                      "kernel": kernel, "bytes_per_launch": bytes_launch,
                      "kernel_us": r["kernel_us"], "launches_timed": r["n_samples"]},
         "cpu_baseline": cpu,
