@@ -30,6 +30,12 @@
 namespace kve {
 namespace {
 
+// Register budget as resident waves per SIMD (3 keeps both kernels free of
+// spills at d = 128).
+#ifndef KVE_PREFILL_WAVES_PER_EU
+#define KVE_PREFILL_WAVES_PER_EU 3
+#endif
+
 constexpr int kNT = 256;
 constexpr int kBlk = 128;          // queries (rowstats) / keys (colsum) per workgroup
 constexpr int kTile = 64;          // keys (rowstats) / queries (colsum) per LDS tile
@@ -61,17 +67,36 @@ template <int D> struct Tile {
   static constexpr int kBytes = kTile * kRowBytes;
 };
 
-// Stages rows [r0, r0 + kTile) of a [P][D] 16-bit block into LDS; rows at or
-// past P are zero.
+// A tile of kTile rows x D 16-bit elements moves global -> registers ->
+// LDS: each thread carries kChunks 16-byte chunks, so the next tile's global
+// loads are in flight while the current tile is consumed from LDS.
+template <int D> struct TileRegs {
+  static constexpr int CPR = D * 2 / 16;                 // 16-byte chunks per row
+  static constexpr int kChunks = kTile * CPR / kNT;
+  static_assert(kTile * CPR % kNT == 0, "tile chunks");
+  uint4 v[kChunks];
+};
+
+// Rows at or past P read as zero.
 template <int D>
-__device__ inline void stage_tile(char* lds, const char* src, int r0, int P) {
-  constexpr int CPR = D * 2 / 16;               // 16-byte chunks per row
+__device__ inline void load_tile(TileRegs<D>& t, const char* src, int r0, int P) {
+  constexpr int CPR = TileRegs<D>::CPR;
 #pragma unroll
-  for (int i = threadIdx.x; i < kTile * CPR; i += kNT) {
+  for (int j = 0; j < TileRegs<D>::kChunks; ++j) {
+    const int i = threadIdx.x + j * kNT;
     const int r = i / CPR, c = i % CPR;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + r < P) v = ld16(src + ((size_t)(r0 + r) * D) * 2 + c * 16);
-    *reinterpret_cast<uint4*>(lds + r * Tile<D>::kRowBytes + c * 16) = v;
+    t.v[j] = r0 + r < P ? ld16(src + ((size_t)(r0 + r) * D) * 2 + c * 16) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int D>
+__device__ inline void store_tile(const TileRegs<D>& t, char* lds) {
+  constexpr int CPR = TileRegs<D>::CPR;
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::kChunks; ++j) {
+    const int i = threadIdx.x + j * kNT;
+    const int r = i / CPR, c = i % CPR;
+    *reinterpret_cast<uint4*>(lds + r * Tile<D>::kRowBytes + c * 16) = t.v[j];
   }
 }
 
@@ -88,11 +113,53 @@ __device__ inline Scale2 make_scale2(float scale) {
 }
 
 // ------------------------------------------------------------------ rowstats
+// Folds one 64-key tile (already in acc) into the online statistics of this
+// lane's two queries.  EDGE: some keys follow a query or lie past P.
+template <bool EDGE>
+__device__ inline void rowstats_fold(const f32x4 (&acc)[4][2], int k0, int q0, int P, int g, int c16,
+                                     const Scale2& c2, float (&mc)[2], double (&l)[2]) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int qi = q0 + nb * 16 + c16;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kj = k0 + mb * 16 + g * 4 + r;
+        const bool ok = !EDGE || (kj <= qi && kj < P);
+        tmax = fmaxf(tmax, ok ? acc[mb][nb][r] : -INFINITY);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mn = fmaxf(mc[nb], tmax * c2.hi);
+    if (mn > mc[nb]) {
+      l[nb] *= (double)exp2_fast(mc[nb] - mn);
+      mc[nb] = mn;
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float s = acc[mb][nb][r];
+        const float p = exp2_fast(fmaf(s, c2.lo, fmaf(s, c2.hi, -mn)));
+        if (EDGE) {
+          const int kj = k0 + mb * 16 + g * 4 + r;
+          sum += (kj <= qi && kj < P) ? p : 0.f;
+        } else {
+          sum += p;
+        }
+      }
+    l[nb] += (double)sum;
+  }
+}
+
 template <int DT, int D>
-__global__ __launch_bounds__(kNT) void rowstats_mfma_kernel(Shape sh, int P, UnitList ul, const void* q,
-                                                            const void* k, float* lse) {
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(KVE_PREFILL_WAVES_PER_EU)))
+void rowstats_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void* k, float* lse) {
   constexpr int KS = D / 32;                    // MFMA k-steps over the head dimension
-  __shared__ __attribute__((aligned(16))) char Ks[Tile<D>::kBytes];
+  __shared__ __attribute__((aligned(16))) char Ks[2][Tile<D>::kBytes];
   const int u = ul.ids ? ul.ids[blockIdx.x] : blockIdx.x;
   const int nqb = (P + kBlk - 1) / kBlk;
   const int qb = nqb - 1 - (int)blockIdx.y;     // heaviest (last) query block first
@@ -118,56 +185,32 @@ __global__ __launch_bounds__(kNT) void rowstats_mfma_kernel(Shape sh, int P, Uni
   float mc[2] = {-INFINITY, -INFINITY};
   double l[2] = {0.0, 0.0};
   const int kend = min(P, qb * kBlk + kBlk);    // keys needed by the block
-  for (int k0 = 0; k0 < kend; k0 += kTile) {
-    __syncthreads();
-    stage_tile<D>(Ks, kbase, k0, P);
-    __syncthreads();
-    if (k0 > q0 + 31) continue;                 // tile entirely after this wave's queries
-    f32x4 acc[4][2];
+  TileRegs<D> nxt;
+  load_tile<D>(nxt, kbase, 0, P);
+  store_tile<D>(nxt, Ks[0]);
+  __syncthreads();
+  for (int it = 0, k0 = 0; k0 < kend; ++it, k0 += kTile) {
+    const char* cur = Ks[it & 1];
+    const bool more = k0 + kTile < kend;
+    if (more) load_tile<D>(nxt, kbase, k0 + kTile, P);   // in flight during the compute below
+    if (k0 <= q0 + 31) {                        // some key of the tile precedes a query of the wave
+      f32x4 acc[4][2];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(Ks + (mb * 16 + c16) * Tile<D>::kRowBytes + (ks * 32 + g * 8) * 2);
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 a = *reinterpret_cast<const uint4*>(cur + (mb * 16 + c16) * Tile<D>::kRowBytes + (ks * 32 + g * 8) * 2);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = Mfma<DT>::run(a, qf[nb][ks], acc[mb][nb]);
-      }
-    }
-    const bool edge = (k0 + kTile > q0) || (k0 + kTile > P);   // masking needed somewhere
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int qi = q0 + nb * 16 + c16;
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kj = k0 + mb * 16 + g * 4 + r;
-          const bool ok = !edge || (kj <= qi && kj < P);
-          tmax = fmaxf(tmax, ok ? acc[mb][nb][r] : -INFINITY);
+          for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = Mfma<DT>::run(a, qf[nb][ks], acc[mb][nb]);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(mc[nb], tmax * c2.hi);
-      if (mn > mc[nb]) {
-        l[nb] *= (double)exp2_fast(mc[nb] - mn);
-        mc[nb] = mn;
       }
-      float sum = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kj = k0 + mb * 16 + g * 4 + r;
-          const bool ok = !edge || (kj <= qi && kj < P);
-          const float s = acc[mb][nb][r];
-          const float p = exp2_fast(fmaf(s, c2.lo, fmaf(s, c2.hi, -mn)));
-          sum += ok ? p : 0.f;
-        }
-      l[nb] += (double)sum;
+      if (k0 + kTile > q0 || k0 + kTile > P) rowstats_fold<true>(acc, k0, q0, P, g, c16, c2, mc, l);
+      else rowstats_fold<false>(acc, k0, q0, P, g, c16, c2, mc, l);
     }
+    if (more) store_tile<D>(nxt, Ks[(it + 1) & 1]);   // that buffer was last read before the previous barrier
+    __syncthreads();
   }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -185,12 +228,36 @@ __global__ __launch_bounds__(kNT) void rowstats_mfma_kernel(Shape sh, int P, Uni
 }
 
 // ------------------------------------------------------------------ colsum
+// Adds one 64-query tile's weights exp2(s * c2 - lse2) into part (this lane's
+// keys).  EDGE: some query precedes a key of the wave or lies past P.
+template <bool EDGE>
+__device__ inline void colsum_fold(const f32x4 (&acc)[2], int i0, int nb, int j0, int P, int g, int c16,
+                                   const Scale2& c2, float lh, float ll, float (&part)[2][4]) {
+  const int qi = i0 + nb * 16 + c16;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = acc[mb][r];
+      float x = fmaf(s, c2.hi, -lh);
+      x = fmaf(s, c2.lo, x) - ll;
+      const float p = exp2_fast(x);
+      if (EDGE) {
+        const int kj = j0 + mb * 16 + g * 4 + r;
+        part[mb][r] += (qi < P && qi >= kj) ? p : 0.f;
+      } else {
+        part[mb][r] += p;
+      }
+    }
+}
+
 template <int DT, int D>
-__global__ __launch_bounds__(kNT) void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q,
-                                                          const void* k, const float* lse, double* colsum) {
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(KVE_PREFILL_WAVES_PER_EU)))
+void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void* k, const float* lse,
+                        double* colsum) {
   constexpr int KS = D / 32;
-  __shared__ __attribute__((aligned(16))) char Qs[Tile<D>::kBytes];
-  __shared__ float Lh[kTile], Ll[kTile];       // lse in log2 units, float pair
+  __shared__ __attribute__((aligned(16))) char Qs[2][Tile<D>::kBytes];
+  __shared__ float Lh[2][kTile], Ll[2][kTile];  // lse in log2 units, float pair
   const int u = ul.ids ? ul.ids[blockIdx.x] : blockIdx.x;
   const int kb = blockIdx.y;                    // key block 0 (the heaviest) first
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -215,53 +282,64 @@ __global__ __launch_bounds__(kNT) void colsum_mfma_kernel(Shape sh, int P, UnitL
 #pragma unroll
     for (int r = 0; r < 4; ++r) cs[mb][r] = 0.0;
 
-  for (int i0 = kb * kBlk; i0 < P; i0 += kTile) {
-    __syncthreads();
-    stage_tile<D>(Qs, qbase, i0, P);
-    if (threadIdx.x < kTile) {
-      const int qi = min(i0 + (int)threadIdx.x, P - 1);
-      const double L2 = ((double)lse[((size_t)u * P + qi) * 2] + (double)lse[((size_t)u * P + qi) * 2 + 1]) * kLog2e;
-      const float hi = (float)L2;
-      Lh[threadIdx.x] = hi;
-      Ll[threadIdx.x] = (float)(L2 - (double)hi);
+  // lse of one query, in log2 units as a float pair
+  auto lse2 = [&](int i, float& hi, float& lo) {
+    const int qi = min(i, P - 1);
+    const double L2 = ((double)lse[((size_t)u * P + qi) * 2] + (double)lse[((size_t)u * P + qi) * 2 + 1]) * kLog2e;
+    hi = (float)L2;
+    lo = (float)(L2 - (double)hi);
+  };
+  const int i_first = kb * kBlk;
+  TileRegs<D> nxt;
+  float nh = 0.f, nl = 0.f;
+  load_tile<D>(nxt, qbase, i_first, P);
+  store_tile<D>(nxt, Qs[0]);
+  if (threadIdx.x < kTile) {
+    lse2(i_first + threadIdx.x, nh, nl);
+    Lh[0][threadIdx.x] = nh;
+    Ll[0][threadIdx.x] = nl;
+  }
+  __syncthreads();
+  for (int it = 0, i0 = i_first; i0 < P; ++it, i0 += kTile) {
+    const int buf = it & 1;
+    const bool more = i0 + kTile < P;
+    if (more) {
+      load_tile<D>(nxt, qbase, i0 + kTile, P);
+      if (threadIdx.x < kTile) lse2(i0 + kTile + threadIdx.x, nh, nl);
     }
-    __syncthreads();
-    if (i0 + kTile - 1 < j0) continue;          // every query of the tile precedes this wave's keys
-    const bool diag = i0 < j0 + 32;
-    float part[2][4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part[mb][r] = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 b = *reinterpret_cast<const uint4*>(Qs + (nb * 16 + c16) * Tile<D>::kRowBytes + (ks * 32 + g * 8) * 2);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc[mb] = Mfma<DT>::run(kf[mb][ks], b, acc[mb]);
-      }
-      const int qi = i0 + nb * 16 + c16;
-      const float lh = Lh[nb * 16 + c16], ll = Ll[nb * 16 + c16];
-      const bool qok = qi < P;
+    if (i0 + kTile - 1 >= j0) {                 // some query of the tile follows a key of the wave
+      const bool edge = i0 < j0 + 32 || i0 + kTile > P;
+      float part[2][4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kj = j0 + mb * 16 + g * 4 + r;
-          const float s = acc[mb][r];
-          float x = fmaf(s, c2.hi, -lh);
-          x = fmaf(s, c2.lo, x) - ll;
-          float p = exp2_fast(x);
-          if (!qok || (diag && qi < kj)) p = 0.f;
-          part[mb][r] += p;
+        for (int r = 0; r < 4; ++r) part[mb][r] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 b = *reinterpret_cast<const uint4*>(Qs[buf] + (nb * 16 + c16) * Tile<D>::kRowBytes + (ks * 32 + g * 8) * 2);
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) acc[mb] = Mfma<DT>::run(kf[mb][ks], b, acc[mb]);
         }
+        const float lh = Lh[buf][nb * 16 + c16], ll = Ll[buf][nb * 16 + c16];
+        if (edge) colsum_fold<true>(acc, i0, nb, j0, P, g, c16, c2, lh, ll, part);
+        else colsum_fold<false>(acc, i0, nb, j0, P, g, c16, c2, lh, ll, part);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cs[mb][r] += (double)part[mb][r];
     }
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) cs[mb][r] += (double)part[mb][r];
+    if (more) {
+      store_tile<D>(nxt, Qs[buf ^ 1]);          // that buffer was last read before the previous barrier
+      if (threadIdx.x < kTile) {
+        Lh[buf ^ 1][threadIdx.x] = nh;
+        Ll[buf ^ 1][threadIdx.x] = nl;
+      }
+    }
+    __syncthreads();
   }
   // sum over the 16 lanes (queries) that share each key
 #pragma unroll
