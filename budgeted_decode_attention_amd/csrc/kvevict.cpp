@@ -36,12 +36,15 @@ kve_status fail(kve_status s, const char* fmt, ...) {
 }
 
 constexpr int kMaxContext = 32768;     // LDS-resident per-unit slot lists
-// Layers whose slot stride exceeds this use the split decode (chunks of
-// kSplitChunk slots); both can be overridden at create time through the
-// environment (KVEVICT_SPLIT_ABOVE, KVEVICT_SPLIT_CHUNK) to exercise either
-// path at any size.
+// Layers whose slot stride exceeds kSplitAbove use the split decode.  Chunk
+// size: a layer whose heads all share one capacity splits each unit in about
+// two (half the capacity rounded up to 256, at least 512: fewer partials to
+// merge); a layer with mixed capacities uses 256-slot chunks so units of very
+// different sizes balance across the GPU.  Both can be overridden at create
+// time through the environment (KVEVICT_SPLIT_ABOVE, KVEVICT_SPLIT_CHUNK) to
+// exercise either path at any size.
 constexpr int kSplitAbove = 1024;
-constexpr int kSplitChunk = 512;
+constexpr int kSplitChunkMixed = 256;
 constexpr size_t kMaxSplitLds = 150 * 1024;
 constexpr int kMaxHashBudget = 16384;  // replay keeps sketches and positions in LDS
 constexpr size_t kAlign = 256;
@@ -57,13 +60,20 @@ int env_int(const char* name, int dflt) {
 }
 
 struct SplitPolicy {
-  int above, chunk;
+  int above;
+  int chunk;   // 0: chosen per layer
 };
 
 SplitPolicy split_policy() {
-  SplitPolicy p{env_int("KVEVICT_SPLIT_ABOVE", kSplitAbove), env_int("KVEVICT_SPLIT_CHUNK", kSplitChunk)};
-  if (p.chunk < 16) p.chunk = kSplitChunk;
+  SplitPolicy p{env_int("KVEVICT_SPLIT_ABOVE", kSplitAbove), env_int("KVEVICT_SPLIT_CHUNK", 0)};
+  if (p.chunk != 0 && p.chunk < 16) p.chunk = 0;
   return p;
+}
+
+int layer_chunk(const SplitPolicy& sp, int cap, bool uniform) {
+  if (sp.chunk) return sp.chunk;
+  if (!uniform) return kSplitChunkMixed;
+  return std::max(512, (cap / 2 + 255) / 256 * 256);
 }
 
 
@@ -82,6 +92,9 @@ int head_capacity(int policy, int heavy, int recent, int max_context) {
 struct LayerInfo {
   int cap = 0;
   bool split = false;
+  bool uniform = true;   // every head of the layer has the same capacity
+  int chunk = 0;         // split-decode chunk (slots)
+  int nch = 0;           // chunks per unit
   bool any_h2o = false, any_hash = false, any_special = false;
   int max_hash_budget = 0;
   std::vector<int32_t> h2o_units, hash_units;
@@ -141,7 +154,9 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
         default:
           return fail(KVE_EINVAL, "layer %d head %d: policy %d unknown", l, h, p);
       }
-      li.cap = std::max(li.cap, head_capacity(p, hv, rc, c->max_context));
+      const int hc = head_capacity(p, hv, rc, c->max_context);
+      if (h > 0 && hc != li.cap) li.uniform = false;
+      li.cap = std::max(li.cap, hc);
     }
     for (int b = 0; b < c->batch; ++b)
       for (int h = 0; h < c->heads; ++h) {
@@ -154,12 +169,14 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
   for (int l = 0; l < c->layers; ++l) {
     LayerInfo& li = (*info)[l];
     li.split = li.cap > sp.above;
-    if (li.split && (li.cap + sp.chunk - 1) / sp.chunk > kve::kMaxChunks)
+    if (!li.split) continue;
+    li.chunk = layer_chunk(sp, li.cap, li.uniform);
+    li.nch = (li.cap + li.chunk - 1) / li.chunk;
+    if (li.nch > kve::kMaxChunks)
       return fail(KVE_EUNSUPPORTED, "layer %d: %d slots need more than %d chunks of %d", l, li.cap,
-                  kve::kMaxChunks, sp.chunk);
+                  kve::kMaxChunks, li.chunk);
     // the combine kernel holds a unit's chunk partials and weights in LDS
-    const size_t nch = li.split ? (size_t)(li.cap + sp.chunk - 1) / sp.chunk : 0;
-    if (li.split && (nch * (c->head_dim + 2) + li.cap) * 4 > kMaxSplitLds)
+    if (((size_t)li.nch * (c->head_dim + 2) + li.cap) * 4 > kMaxSplitLds)
       return fail(KVE_EUNSUPPORTED, "layer %d: %d slots exceed the split decode's LDS", l, li.cap);
   }
   if (need_bitmap && (!c->keep_token_bitmap || c->vocab < 1))
@@ -210,8 +227,7 @@ namespace {
 
 size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* base, kve_ctx* ctx) {
   Plan pl(base);
-  const SplitPolicy sp = split_policy();
-  const size_t U = (size_t)c->batch * c->heads;
+    const size_t U = (size_t)c->batch * c->heads;
   const size_t d = c->head_dim, es = elem_size(c->dtype);
   const size_t N = c->max_context;
   bool any_hash = false, any_special = false;
@@ -227,11 +243,13 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
   auto* qsk = any_hash ? pl.take<uint32_t>(U * N) : nullptr;
   auto* ksk = any_hash ? pl.take<uint32_t>(U * N) : nullptr;
   // split-decode scratch, sized for the largest split layer
-  size_t split_cap = 0;
+  size_t split_cap = 0, split_nch = 0;
   for (const auto& li : info)
-    if (li.cap > sp.above) split_cap = std::max(split_cap, (size_t)li.cap);
-  const int max_chunks = split_cap ? (int)((split_cap + sp.chunk - 1) / sp.chunk) : 0;
-  float* part = split_cap ? pl.take<float>(U * max_chunks * (d + 2)) : nullptr;
+    if (li.split) {
+      split_cap = std::max(split_cap, (size_t)li.cap);
+      split_nch = std::max(split_nch, (size_t)li.nch);
+    }
+  float* part = split_cap ? pl.take<float>(U * split_nch * (d + 2)) : nullptr;
   float* logits = split_cap ? pl.take<float>(U * split_cap) : nullptr;
   if (ctx) {
     ctx->meta = meta;
@@ -260,8 +278,7 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
     if (ctx) {
       Layer& L = ctx->layers[l];
       L.cache = lc;
-      if (li.cap > sp.above)
-        L.split = {part, logits, sp.chunk, (int32_t)((li.cap + sp.chunk - 1) / sp.chunk)};
+      if (li.split) L.split = {part, logits, li.chunk, li.nch};
       L.info = li;
       L.h2o = {h2o_ids, (int32_t)li.h2o_units.size()};
       L.hash = {hash_ids, (int32_t)li.hash_units.size()};
