@@ -161,13 +161,28 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
   if (m.policy == H2O) {
     const int lim = t - m.recent;              // candidates: position <= t - recent
     MinKey best{INFINITY, INT32_MAX, INT32_MAX};
-    for (int r = tid; r < n; r += kNT) {
-      const double s = c.S[slot0 + r] + (double)wts[r] * invL;
-      c.S[slot0 + r] = s;
-      const int p = c.pos[slot0 + r];
-      if (p <= lim) {
-        const MinKey k{s, p, r};
-        if (key_less(k, best)) best = k;
+    // four slots per thread per round: their score/position loads are issued
+    // together, so a large cache costs n / (4 NT) load latencies, not n / NT
+    for (int r0 = tid; r0 < n; r0 += 4 * kNT) {
+      double sv[4];
+      int pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i * kNT;
+        sv[i] = r < n ? c.S[slot0 + r] : 0.0;
+        pv[i] = r < n ? c.pos[slot0 + r] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i * kNT;
+        if (r < n) {
+          const double s = sv[i] + (double)wts[r] * invL;
+          c.S[slot0 + r] = s;
+          if (pv[i] <= lim) {
+            const MinKey k{s, pv[i], r};
+            if (key_less(k, best)) best = k;
+          }
+        }
       }
     }
     s_new = (double)e_new * invL;
@@ -366,7 +381,15 @@ __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, De
   float* part = lds;
   float* wts = lds + (size_t)sp.max_chunks * (D + 2);
   const float* gpart = sp.part + (size_t)u * sp.max_chunks * (D + 2);
-  for (int i = tid; i < nch * (D + 2); i += kNT) part[i] = gpart[i];
+  const int total = nch * (D + 2);
+  for (int i0 = tid; i0 < total; i0 += 8 * kNT) {   // eight loads in flight per thread
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = i0 + j * kNT < total ? gpart[i0 + j * kNT] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (i0 + j * kNT < total) part[i0 + j * kNT] = v[j];
+  }
 
   if (with_new && rg == 0) {
     float qf[R::EPL];
@@ -384,10 +407,19 @@ __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, De
   if (m.policy == H2O) {
     // exact weights of every kept slot, recomputed from the stored logits
     const float* lgs = sp.logits + slot0;
-    for (int r = tid; r < n; r += kNT) {
-      const float w = expf(lgs[r] - M);
-      wts[r] = w;
-      ls += (double)w;
+    for (int r0 = tid; r0 < n; r0 += 4 * kNT) {
+      float lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lv[i] = r0 + i * kNT < n ? lgs[r0 + i * kNT] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i * kNT;
+        if (r < n) {
+          const float w = expf(lv[i] - M);
+          wts[r] = w;
+          ls += (double)w;
+        }
+      }
     }
   } else {
     for (int ch = tid; ch < nch; ch += kNT)

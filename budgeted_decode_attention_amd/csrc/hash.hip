@@ -59,13 +59,16 @@ __device__ __attribute__((noinline)) int exact_sign(const char* row, const uint1
 }
 
 // Sign bit b of a row: float64 dot with the error bound, exact fallback.
+// xs: the row as floats (LDS), Ws: the projection as bf16 bits (LDS); the
+// exact fallback re-reads the row and projection from global memory.
 template <int DT, int D>
-__device__ inline int sketch_bit(const char* row, const uint16_t* W, int bits, int b) {
+__device__ inline int sketch_bit(const float* xs, const uint16_t* Ws, const char* row, const uint16_t* W,
+                                 int bits, int b) {
   double s = 0.0, a = 0.0;
 #pragma unroll 8
   for (int i = 0; i < D; ++i) {
-    const double x = (double)load_elem<DT>(row, i);
-    const double w = bf16_to_double(W[i * bits + b]);
+    const double x = (double)xs[i];
+    const double w = bf16_to_double(Ws[i * bits + b]);
     s = fma(x, w, s);
     a = fma(fabs(x), fabs(w), a);
   }
@@ -77,24 +80,41 @@ __device__ inline int sketch_bit(const char* row, const uint16_t* W, int bits, i
   return exact_sign<DT, D>(row, W, bits, b);
 }
 
-// One 32-lane half-wave per row; the lane index is the bit.
+// Copies the [D][32] bf16 projection into LDS (all threads of the workgroup).
+template <int D>
+__device__ inline void stage_proj(uint16_t* Ws, const uint16_t* W) {
+  for (int i = threadIdx.x; i < D * kMaxBits / 8; i += kNT)
+    reinterpret_cast<uint4*>(Ws)[i] = reinterpret_cast<const uint4*>(W)[i];
+}
+
+constexpr int kSketchRows = 64;   // rows per workgroup in sketch_rows_kernel
+
+// Sketches of rows [row0, row0 + nrows) of each listed unit: a workgroup
+// stages the projection once and then covers kSketchRows rows, eight at a
+// time (one 32-lane half-wave per row; the lane index is the bit).
 template <int DT, int D>
 __global__ __launch_bounds__(kNT) void sketch_rows_kernel(Shape sh, UnitList ul, const void* x, int P, int row0,
                                                           int nrows, const uint16_t* proj, uint32_t* out) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[D * kMaxBits];
+  __shared__ float xs[kNT / 32][D];
   constexpr int ES = elem_bytes<DT>();
   const int u = ul.ids ? ul.ids[blockIdx.y] : blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int half = lane >> 5;
   const int b = lane & 31;
-  const int r = (blockIdx.x * kNT + threadIdx.x) / 32;   // row index within [0, nrows)
-  const bool ok = r < nrows;
-  int bit = 0;
-  if (ok) {
-    const char* row = (const char*)x + ((size_t)u * P + row0 + r) * D * ES;
-    bit = sketch_bit<DT, D>(row, proj, kMaxBits, b);
+  const int slot = threadIdx.x / 32;                       // row slot within a pass of 8 rows
+  stage_proj<D>(Ws, proj);
+  for (int pass = 0; pass < kSketchRows / (kNT / 32); ++pass) {
+    const int r = blockIdx.x * kSketchRows + pass * (kNT / 32) + slot;   // row index within [0, nrows)
+    const bool ok = r < nrows;
+    const char* row = (const char*)x + ((size_t)u * P + row0 + (ok ? r : 0)) * D * ES;
+    __syncthreads();                                        // previous pass done with xs; Ws staged
+    for (int i = b; i < D; i += 32) xs[slot][i] = ok ? load_elem<DT>(row, i) : 0.f;
+    __syncthreads();
+    const int bit = ok ? sketch_bit<DT, D>(xs[slot], Ws, row, proj, kMaxBits, b) : 0;
+    const uint64_t m = __ballot(bit != 0);
+    if (ok && b == 0) out[(size_t)u * P + row0 + r] = (uint32_t)(m >> (32 * half));
   }
-  const uint64_t m = __ballot(bit != 0);
-  if (ok && b == 0) out[(size_t)u * P + row0 + r] = (uint32_t)(m >> (32 * half));
 }
 
 // Prompt replay for one HASH unit per workgroup; slot state in LDS.
@@ -185,15 +205,21 @@ __global__ __launch_bounds__(kNT) void hash_evict_kernel(Shape sh, LayerCache c,
   constexpr int LPR = D / EPL;
   __shared__ uint32_t sk2[2];
   __shared__ uint64_t kscr[kNT / kWave];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[D * kMaxBits];
+  __shared__ float xs[2][D];
   const int u = ul.ids[blockIdx.x];
   const int tid = threadIdx.x;
   const HeadMeta m = c.meta[u % sh.heads];
   const int B = m.heavy;
+  stage_proj<D>(Ws, c.proj);
+  for (int i = tid; i < 2 * D; i += kNT)
+    xs[i / D][i % D] = load_elem<DT>((const char*)(i < D ? q : k) + (size_t)u * D * ES, i % D);
+  __syncthreads();
   // wave 0: lanes 0-31 sketch q, lanes 32-63 sketch k
   if (tid < kWave) {
     const int half = tid >> 5;
     const char* row = (const char*)(half ? k : q) + (size_t)u * D * ES;
-    const int bit = sketch_bit<DT, D>(row, c.proj, kMaxBits, tid & 31);
+    const int bit = sketch_bit<DT, D>(xs[half], Ws, row, c.proj, kMaxBits, tid & 31);
     const uint64_t msk = __ballot(bit != 0);
     if (tid == 0) {
       sk2[0] = (uint32_t)msk;
@@ -278,7 +304,7 @@ template <int DT, int D>
 hipError_t sketch_t(const Shape& sh, UnitList ul, const void* x, int P, int row0, int nrows,
                     const uint16_t* proj, uint32_t* out, hipStream_t st) {
   if (nrows <= 0 || ul.n <= 0) return hipSuccess;
-  dim3 grid((nrows * 32 + kNT - 1) / kNT, ul.n);
+  dim3 grid((nrows + kSketchRows - 1) / kSketchRows, ul.n);
   hipLaunchKernelGGL((sketch_rows_kernel<DT, D>), grid, dim3(kNT), 0, st, sh, ul, x, P, row0, nrows, proj, out);
   return hipGetLastError();
 }
