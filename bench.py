@@ -166,7 +166,7 @@ def counter_traffic(workload: str):
     return None
 
 
-def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0):
+def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, cold: bool = False):
     import numpy as np
     import torch
     from budgeted_decode_attention_amd import KVCache
@@ -246,13 +246,41 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    cold_us = None
+    if cold:
+        # one more pass in which every sampled step group starts after a 1 GiB
+        # read-modify-write of another buffer (outside the timed group), so
+        # neither the L2 nor the 256 MB Infinity Cache holds the cache's rows
+        fl = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        cold_samples = []
+        for l in range(w.layers):
+            x = inputs[l]
+            kv.prefill(l, x.prompt_q, x.prompt_k, x.prompt_v, pids[l])
+        for s in range(w.steps):
+            sample = s % sample_every == 0
+            if sample:
+                fl.mul_(1.0)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            for l in range(w.layers):
+                x = inputs[l]
+                tid = dids[l][s] if dids[l] is not None else None
+                kv.decode_step(l, x.dec_q[s], x.dec_k[s], x.dec_v[s], tid, out[l], ev[l])
+            if sample:
+                e1.record(stream)
+                cold_samples.append((e0, e1))
+        torch.cuda.synchronize()
+        cold_us = 1e3 * sum(a.elapsed_time(b) for a, b in cold_samples) / (len(cold_samples) * w.layers)
+        del fl
     ids0 = inputs[0].ids.cpu().numpy() if inputs[0].ids is not None else None
     group_ms = [a.elapsed_time(b) for a, b in samples]
     kernel_us = 1e3 * sum(group_ms) / (len(group_ms) * w.layers)
     return {"wall_s": wall, "gen_s": gen_s, "prefill_ms": prefill_ms, "decode_ms": decode_ms,
             "kernel_us": kernel_us, "n_samples": len(group_ms) * w.layers,
             "finite": bool(torch.isfinite(out).all().item()), "ids0": ids0,
-            "split": kv.capacity(0) > 1024}
+            "split": kv.capacity(0) > 1024, "cold_us": cold_us}
 
 
 def main():
@@ -264,6 +292,8 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=0,
                     help="oracle sample size for the CPU baseline (0: per-workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time decode launches that start with the L2 and Infinity Cache flushed")
     ap.add_argument("--layers", type=int, default=0,
                     help="hardware-counter passes only: keep just the first N layers resident (the per-launch "
                          "shape is unchanged); the printed line then describes that reduced job")
@@ -289,7 +319,7 @@ def main():
         cpu = cpu_baseline(w, n_units, workers)
         print(f"[bench] cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
 
-    r = run_gpu(w, a.steps, a.warmup, a.sample_every, a.calibration_copy_mib)
+    r = run_gpu(w, a.steps, a.warmup, a.sample_every, a.calibration_copy_mib, a.cold)
     ms = 1e3 * r["wall_s"] / a.steps
     tokens = w.batch * w.steps
     bytes_launch = decode_bytes_per_layer_step(w, r["ids0"])
@@ -314,7 +344,9 @@ def main():
         "cpu_baseline": cpu,
         "detail": {"prefill_ms_per_step": r["prefill_ms"], "decode_ms_per_step": r["decode_ms"],
                    "decode_only_tokens_per_s": tokens / (r["decode_ms"] * 1e-3),
-                   "input_generation_s": r["gen_s"], "outputs_finite": r["finite"]},
+                   "input_generation_s": r["gen_s"], "outputs_finite": r["finite"],
+                   "cold_kernel_us": r["cold_us"],
+                   "cold_frac": (bytes_launch / (r["cold_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS) if r["cold_us"] else None},
     }
     print(json.dumps(line), flush=True)
 

@@ -112,7 +112,13 @@ def test_hash_prompt_shorter_than_budget(decode_path):
     run_and_check(w, policy=[HASH] * 2, heavy=[70] * 2, recent=[0] * 2)
 
 
-def test_deterministic_across_runs():
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_h2o_bf16_more_seeds(seed, decode_path):
+    w = configs.scaled("opt30b_decode_h2o", batch=2, heads=2, prompt=333, steps=50)
+    run_and_check(w, seed=seed)
+
+
+def test_deterministic_across_runs(decode_path):
     w = configs.scaled("opt6.7b_layer_h2o", batch=2, heads=2, prompt=200, steps=30)
     inp = generate_layer(w, 0, "cpu", 3).to("cuda")
     runs = []
