@@ -166,7 +166,23 @@ def counter_traffic(workload: str):
     return None
 
 
-def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, cold: bool = False):
+def prefill_flops_per_layer(w, prompt_out: bool) -> float:
+    """Algorithmic prefill flops of one layer: one causal Q K^T pass (2 d flops
+    per query-key pair with key <= query) for the row statistics and one for
+    the column sums of every heavy-hitter head, plus one P V pass per unit when
+    the prompt output is produced."""
+    pairs = w.prompt * (w.prompt + 1) / 2
+    pol = w.policy_table(0)[0]
+    h2o_units = w.batch * sum(1 for p in pol if p == 1)
+    units = w.batch * w.heads
+    per = 2.0 * w.head_dim * pairs
+    if prompt_out:
+        return per * (2 * units + h2o_units)
+    return per * 2 * h2o_units
+
+
+def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, cold: bool = False,
+            prompt_out: bool = False):
     import numpy as np
     import torch
     from budgeted_decode_attention_amd import KVCache
@@ -199,6 +215,9 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
     dids = [[x[:, w.prompt + s].contiguous() for s in range(w.steps)] if x is not None else None for x in ids]
     out = torch.empty((w.layers, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=dev)
     ev = torch.empty((w.layers, w.batch, w.heads), dtype=torch.int32, device=dev)
+    # the optional prompt attention output, one layer's worth, rewritten by every layer
+    pout = (torch.empty((w.batch, w.heads, w.prompt, w.head_dim), dtype=torch.float32, device=dev)
+            if prompt_out else None)
     stream = torch.cuda.current_stream()
 
     samples = []
@@ -206,7 +225,7 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
     def step(timed: bool):
         for l in range(w.layers):
             x = inputs[l]
-            kv.prefill(l, x.prompt_q, x.prompt_k, x.prompt_v, pids[l])
+            kv.prefill(l, x.prompt_q, x.prompt_k, x.prompt_v, pids[l], pout)
         for s in range(w.steps):
             sample = timed and s % sample_every == 0
             if sample:
@@ -229,7 +248,7 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
     p0.record(stream)
     for l in range(w.layers):
         x = inputs[l]
-        kv.prefill(l, x.prompt_q, x.prompt_k, x.prompt_v, pids[l])
+        kv.prefill(l, x.prompt_q, x.prompt_k, x.prompt_v, pids[l], pout)
     p1.record(stream)
     for s in range(w.steps):
         for l in range(w.layers):
@@ -256,7 +275,7 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
         cold_samples = []
         for l in range(w.layers):
             x = inputs[l]
-            kv.prefill(l, x.prompt_q, x.prompt_k, x.prompt_v, pids[l])
+            kv.prefill(l, x.prompt_q, x.prompt_k, x.prompt_v, pids[l], pout)
         for s in range(w.steps):
             sample = s % sample_every == 0
             if sample:
@@ -279,7 +298,8 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
     kernel_us = 1e3 * sum(group_ms) / (len(group_ms) * w.layers)
     return {"wall_s": wall, "gen_s": gen_s, "prefill_ms": prefill_ms, "decode_ms": decode_ms,
             "kernel_us": kernel_us, "n_samples": len(group_ms) * w.layers,
-            "finite": bool(torch.isfinite(out).all().item()), "ids0": ids0,
+            "finite": bool(torch.isfinite(out).all().item()) and (pout is None or bool(torch.isfinite(pout).all().item())),
+            "ids0": ids0,
             "split": kv.capacity(0) > 1024, "cold_us": cold_us}
 
 
@@ -299,6 +319,8 @@ def main():
                          "shape is unchanged); the printed line then describes that reduced job")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--prompt-out", action="store_true",
+                    help="also produce the prompt attention output in every prefill")
     ap.add_argument("--sample-every", type=int, default=4,
                     help="event-time the per-layer decode launches of every k-th decode step")
     a = ap.parse_args()
@@ -319,7 +341,8 @@ def main():
         cpu = cpu_baseline(w, n_units, workers)
         print(f"[bench] cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
 
-    r = run_gpu(w, a.steps, a.warmup, a.sample_every, a.calibration_copy_mib, a.cold)
+    r = run_gpu(w, a.steps, a.warmup, a.sample_every, a.calibration_copy_mib, a.cold, a.prompt_out)
+    pf_flops = prefill_flops_per_layer(w, a.prompt_out) * w.layers
     ms = 1e3 * r["wall_s"] / a.steps
     tokens = w.batch * w.steps
     bytes_launch = decode_bytes_per_layer_step(w, r["ids0"])
@@ -344,6 +367,9 @@ def main():
         "cpu_baseline": cpu,
         "detail": {"prefill_ms_per_step": r["prefill_ms"], "decode_ms_per_step": r["decode_ms"],
                    "decode_only_tokens_per_s": tokens / (r["decode_ms"] * 1e-3),
+                   "prompt_out": a.prompt_out,
+                   "prefill_algorithmic_tflops": pf_flops / (r["prefill_ms"] * 1e-3) / 1e12,
+                   "prefill_frac_of_dense_16bit_mfma_peak": pf_flops / (r["prefill_ms"] * 1e-3) / 2.5e15,
                    "input_generation_s": r["gen_s"], "outputs_finite": r["finite"],
                    "cold_kernel_us": r["cold_us"],
                    "cold_frac": (bytes_launch / (r["cold_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS) if r["cold_us"] else None},

@@ -396,12 +396,13 @@ kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t P, const void* q
   const kve::Shape& sh = h->shape;
   hipError_t e = hipSuccess;
   // Scores (H2O heads): row statistics, then column sums.  16-bit inputs use
-  // the matrix-core kernels; fp32 inputs and the optional prompt output use
-  // the vector-ALU kernels.
+  // the matrix-core kernels, fp32 inputs the vector-ALU ones.  The optional
+  // prompt output covers every unit and writes the row statistics with it.
   const kve::UnitList all{nullptr, sh.units()};
   const bool mfma = sh.dtype != KVE_F32;
   if (out) {
-    e = kve::launch_prefill_rowstats_valu(sh, P, all, q, k, v, h->lse, out, st);
+    e = mfma ? kve::launch_prefill_attend_mfma(sh, P, all, q, k, v, h->lse, out, st)
+             : kve::launch_prefill_rowstats_valu(sh, P, all, q, k, v, h->lse, out, st);
   } else if (L.h2o.n) {
     e = mfma ? kve::launch_prefill_rowstats_mfma(sh, P, L.h2o, q, k, h->lse, st)
              : kve::launch_prefill_rowstats_valu(sh, P, L.h2o, q, k, v, h->lse, nullptr, st);

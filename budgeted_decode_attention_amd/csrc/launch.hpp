@@ -55,9 +55,14 @@ hipError_t launch_prefill_rowstats_valu(const Shape& sh, int P, UnitList units, 
 hipError_t launch_prefill_colsum_valu(const Shape& sh, int P, UnitList units, const void* q,
                                       const void* k, const float* lse, double* colsum,
                                       hipStream_t st);
-// The same two passes on the matrix cores (16-bit dtypes only; no output).
+// The same two passes on the matrix cores (16-bit dtypes only).
 hipError_t launch_prefill_rowstats_mfma(const Shape& sh, int P, UnitList units, const void* q,
                                         const void* k, float* lse, hipStream_t st);
+// Row statistics and the causal attention output out[u][i][:] (fp32) on the
+// matrix cores (16-bit dtypes only).
+hipError_t launch_prefill_attend_mfma(const Shape& sh, int P, UnitList units, const void* q,
+                                      const void* k, const void* v, float* lse, float* out,
+                                      hipStream_t st);
 hipError_t launch_prefill_colsum_mfma(const Shape& sh, int P, UnitList units, const void* q,
                                       const void* k, const float* lse, double* colsum,
                                       hipStream_t st);

@@ -15,6 +15,14 @@
 //             weights exp2(s * scale * log2e - lse2) are summed per key in
 //             float32 within a tile and in float64 across tiles.  No atomics:
 //             each workgroup owns its columns.
+//   attend:   rowstats plus the causal attention output o_i = sum_j p_ij v_j
+//             (the optional prompt output), as O^T = V^T P^T on the matrix
+//             cores: the weights a lane forms for its query are already a B
+//             fragment, and the accumulator lane that receives O^T[dim][query]
+//             owns that same query, so the online rescaling and the final
+//             normalisation stay within the lane.  V tiles are staged
+//             transposed in LDS; each weight enters as a 16-bit pair (hi, lo)
+//             so the output keeps about 16 significant bits of every weight.
 //
 // MFMA 16x16x32 lane layout: lane l supplies row (l % 16) of A and column
 // (l % 16) of B, each with 8 consecutive k values chosen by l / 16; it
@@ -34,6 +42,10 @@ namespace {
 // spills at d = 128).
 #ifndef KVE_PREFILL_WAVES_PER_EU
 #define KVE_PREFILL_WAVES_PER_EU 3
+#endif
+// The output pass keeps a D x 32 float accumulator per wave as well.
+#ifndef KVE_ATTEND_WAVES_PER_EU
+#define KVE_ATTEND_WAVES_PER_EU 2
 #endif
 
 constexpr int kNT = 256;
@@ -99,6 +111,103 @@ __device__ inline void store_tile(const TileRegs<D>& t, char* lds) {
     *reinterpret_cast<uint4*>(lds + r * Tile<D>::kRowBytes + c * 16) = t.v[j];
   }
 }
+
+// V tile transposed for the A operand of O^T = V^T P^T: D rows (one per head
+// dimension) of kTile keys in 16 groups of 4, rows padded by 8 bytes.  The
+// group index is XOR-swizzled by bits 5..6 of the row: the transposing stores
+// (16 rows 8 apart per wave) then fall on distinct banks up to 2-way, and the
+// fragment reads need one address per swizzle value, with the block of 16
+// rows, the k-step and the half as immediate offsets.
+template <int D> struct VtTile {
+  static constexpr int kRowBytes = kTile * 2 + 8;
+  static constexpr int kBytes = D * kRowBytes;
+};
+
+__device__ inline int vt_offset(int row, int key) {
+  return row * (kTile * 2 + 8) + (((key >> 2) ^ ((row >> 5) & 3)) << 3) + ((key & 3) << 1);
+}
+
+// Global -> registers -> LDS for a V tile: thread t carries the 16-byte chunk
+// t % CPR (8 head dimensions) of pairs of consecutive keys, so each LDS store
+// is one 32-bit word holding the same dimension of two keys.
+template <int D> struct VtRegs {
+  static constexpr int CPR = D * 2 / 16;
+  static constexpr int kPairs = kNT / CPR;               // key pairs per pass
+  static constexpr int kPasses = kTile / 2 / kPairs;
+  static_assert(kTile / 2 % kPairs == 0, "V tile pairs");
+  uint4 v[kPasses][2];
+};
+
+template <int D>
+__device__ inline void load_vtile(VtRegs<D>& t, const char* src, int r0, int P) {
+  constexpr int CPR = VtRegs<D>::CPR;
+  const int c = threadIdx.x % CPR, m = threadIdx.x / CPR;
+#pragma unroll
+  for (int ps = 0; ps < VtRegs<D>::kPasses; ++ps)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = r0 + 2 * (m + ps * VtRegs<D>::kPairs) + e;
+      t.v[ps][e] = r < P ? ld16(src + ((size_t)r * D) * 2 + c * 16) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <int D>
+__device__ inline void store_vtile(const VtRegs<D>& t, char* lds) {
+  constexpr int CPR = VtRegs<D>::CPR;
+  const int c = threadIdx.x % CPR, m = threadIdx.x / CPR;
+#pragma unroll
+  for (int ps = 0; ps < VtRegs<D>::kPasses; ++ps) {
+    const int key = 2 * (m + ps * VtRegs<D>::kPairs);
+    const uint32_t a[4] = {t.v[ps][0].x, t.v[ps][0].y, t.v[ps][0].z, t.v[ps][0].w};
+    const uint32_t b[4] = {t.v[ps][1].x, t.v[ps][1].y, t.v[ps][1].z, t.v[ps][1].w};
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int sh = (x & 1) * 16;
+      const uint32_t wd = ((a[x >> 1] >> sh) & 0xFFFFu) | (((b[x >> 1] >> sh) & 0xFFFFu) << 16);
+      *reinterpret_cast<uint32_t*>(lds + vt_offset(8 * c + x, key)) = wd;
+    }
+  }
+}
+
+// A fragment of V^T for rows (dims) d0 + lane % 16 and the 8 keys that the
+// weight fragments of k-step kp carry: 32 kp + 4 g + {0..3} and
+// 32 kp + 16 + 4 g + {0..3}, g = lane / 16.
+__device__ inline uint4 vt_fragment(const char* lds, int d0, int kp, int g, int c16) {
+  const int row = d0 + c16;
+  const uint2 x = *reinterpret_cast<const uint2*>(lds + vt_offset(row, 32 * kp + 4 * g));
+  const uint2 y = *reinterpret_cast<const uint2*>(lds + vt_offset(row, 32 * kp + 16 + 4 * g));
+  return make_uint4(x.x, x.y, y.x, y.y);
+}
+
+// Splits 8 float weights into 16-bit (hi, lo) halves of the input dtype,
+// hi = round(w), lo = round(w - hi).
+template <int DT> struct Split16;
+template <> struct Split16<BF16> {
+  __device__ static inline void run(const float (&w)[8], uint4& hi, uint4& lo) {
+    bf16x8 h, l;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 t = (__bf16)w[e];
+      h[e] = t;
+      l[e] = (__bf16)(w[e] - (float)t);
+    }
+    hi = __builtin_bit_cast(uint4, h);
+    lo = __builtin_bit_cast(uint4, l);
+  }
+};
+template <> struct Split16<F16> {
+  __device__ static inline void run(const float (&w)[8], uint4& hi, uint4& lo) {
+    f16x8 h, l;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const _Float16 t = (_Float16)w[e];
+      h[e] = t;
+      l[e] = (_Float16)(w[e] - (float)t);
+    }
+    hi = __builtin_bit_cast(uint4, h);
+    lo = __builtin_bit_cast(uint4, l);
+  }
+};
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -354,6 +463,192 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
     }
 }
 
+// ------------------------------------------------------------------ attend
+// rowstats_fold plus the output: rescales this lane's output accumulators
+// when a query's offset grows, and returns the tile's weights (zero where
+// masked) as (hi, lo) B fragments, pw[nb][kp][0 = hi, 1 = lo].
+template <int DT, int DB, bool EDGE>
+__device__ inline void attend_fold(const f32x4 (&acc)[4][2], int k0, int q0, int P, int g, int c16,
+                                   const Scale2& c2, float (&mc)[2], double (&l)[2], f32x4 (&o)[DB][2],
+                                   uint4 (&pw)[2][2][2]) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int qi = q0 + nb * 16 + c16;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kj = k0 + mb * 16 + g * 4 + r;
+        const bool ok = !EDGE || (kj <= qi && kj < P);
+        tmax = fmaxf(tmax, ok ? acc[mb][nb][r] : -INFINITY);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mn = fmaxf(mc[nb], tmax * c2.hi);
+    if (mn > mc[nb]) {
+      const float a = exp2_fast(mc[nb] - mn);
+      l[nb] *= (double)a;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db][nb] *= a;
+      mc[nb] = mn;
+    }
+    float p[4][4];
+    float sum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float s = acc[mb][nb][r];
+        float x = exp2_fast(fmaf(s, c2.lo, fmaf(s, c2.hi, -mn)));
+        if (EDGE) {
+          const int kj = k0 + mb * 16 + g * 4 + r;
+          x = (kj <= qi && kj < P) ? x : 0.f;
+        }
+        p[mb][r] = x;
+        sum += x;
+      }
+    l[nb] += (double)sum;
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      const float w[8] = {p[2 * kp][0], p[2 * kp][1], p[2 * kp][2], p[2 * kp][3],
+                          p[2 * kp + 1][0], p[2 * kp + 1][1], p[2 * kp + 1][2], p[2 * kp + 1][3]};
+      Split16<DT>::run(w, pw[nb][kp][0], pw[nb][kp][1]);
+    }
+  }
+}
+
+template <int D>
+constexpr size_t attend_lds_bytes() {
+  return 2 * (size_t)Tile<D>::kBytes + 2 * (size_t)VtTile<D>::kBytes;
+}
+
+// Workgroup = (unit, 128 queries) as in rowstats; LDS holds double-buffered K
+// tiles and transposed V tiles.  Writes lse (as rowstats) and out[u][i][:].
+template <int DT, int D>
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(KVE_ATTEND_WAVES_PER_EU)))
+void attend_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void* k, const void* v, float* lse,
+                        float* out) {
+  constexpr int KS = D / 32;
+  constexpr int DB = D / 16;                    // 16-row blocks of V^T (head dimensions)
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const Ks = smem;                        // [2][Tile]
+  char* const Vt = smem + 2 * Tile<D>::kBytes;  // [2][VtTile]
+  const int u = ul.ids ? ul.ids[blockIdx.x] : blockIdx.x;
+  const int nqb = (P + kBlk - 1) / kBlk;
+  const int qb = nqb - 1 - (int)blockIdx.y;     // heaviest (last) query block first
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const size_t base = (size_t)u * P * D * 2;
+  const char* qbase = (const char*)q + base;
+  const char* kbase = (const char*)k + base;
+  const char* vbase = (const char*)v + base;
+  const int q0 = qb * kBlk + w * 32;
+  const Scale2 c2 = make_scale2(sh.scale);
+
+  uint4 qf[2][KS];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int qi = q0 + nb * 16 + c16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[nb][ks] = qi < P ? ld16(qbase + ((size_t)qi * D + ks * 32 + g * 8) * 2) : make_uint4(0, 0, 0, 0);
+  }
+  float mc[2] = {-INFINITY, -INFINITY};
+  double l[2] = {0.0, 0.0};
+  f32x4 o[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) o[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int kend = min(P, qb * kBlk + kBlk);
+  TileRegs<D> nk;
+  VtRegs<D> nv;
+  load_tile<D>(nk, kbase, 0, P);
+  load_vtile<D>(nv, vbase, 0, P);
+  store_tile<D>(nk, Ks);
+  store_vtile<D>(nv, Vt);
+  __syncthreads();
+  for (int it = 0, k0 = 0; k0 < kend; ++it, k0 += kTile) {
+    const int buf = it & 1;
+    const char* ck = Ks + buf * Tile<D>::kBytes;
+    const char* cv = Vt + buf * VtTile<D>::kBytes;
+    const bool more = k0 + kTile < kend;
+    if (more) {
+      load_tile<D>(nk, kbase, k0 + kTile, P);
+      load_vtile<D>(nv, vbase, k0 + kTile, P);
+    }
+    if (k0 <= q0 + 31) {
+      f32x4 acc[4][2];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 a = *reinterpret_cast<const uint4*>(ck + (mb * 16 + c16) * Tile<D>::kRowBytes + (ks * 32 + g * 8) * 2);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = Mfma<DT>::run(a, qf[nb][ks], acc[mb][nb]);
+        }
+      }
+      if (more) {                               // those buffers were last read before the previous barrier
+        store_tile<D>(nk, Ks + (buf ^ 1) * Tile<D>::kBytes);
+        store_vtile<D>(nv, Vt + (buf ^ 1) * VtTile<D>::kBytes);
+      }
+      uint4 pw[2][2][2];
+      if (k0 + kTile > q0 || k0 + kTile > P) attend_fold<DT, DB, true>(acc, k0, q0, P, g, c16, c2, mc, l, o, pw);
+      else attend_fold<DT, DB, false>(acc, k0, q0, P, g, c16, c2, mc, l, o, pw);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          const uint4 a = vt_fragment(cv, db * 16, kp, g, c16);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            o[db][nb] = Mfma<DT>::run(a, pw[nb][kp][0], o[db][nb]);
+            o[db][nb] = Mfma<DT>::run(a, pw[nb][kp][1], o[db][nb]);
+          }
+        }
+    } else if (more) {
+      store_tile<D>(nk, Ks + (buf ^ 1) * Tile<D>::kBytes);
+      store_vtile<D>(nv, Vt + (buf ^ 1) * VtTile<D>::kBytes);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    double lt = l[nb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int qi = q0 + nb * 16 + c16;
+    if (qi < P) {
+      if (g == 0) {
+        const double L = ((double)mc[nb] + log2(lt)) * kLn2;
+        const float hi = (float)L;
+        lse[((size_t)u * P + qi) * 2] = hi;
+        lse[((size_t)u * P + qi) * 2 + 1] = (float)(L - (double)hi);
+      }
+      // this lane holds O^T[db * 16 + 4 g + r][qi], r = 0..3
+      const float inv = (float)(1.0 / lt);
+      float* orow = out + ((size_t)u * P + qi) * D + 4 * g;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(orow + db * 16) = o[db][nb] * inv;
+    }
+  }
+}
+
+template <int DT, int D>
+hipError_t attend_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, const void* v, float* lse,
+                    float* out, hipStream_t st) {
+  const size_t lds = attend_lds_bytes<D>();
+  hipError_t e = hipFuncSetAttribute((const void*)attend_mfma_kernel<DT, D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(ul.n, (P + kBlk - 1) / kBlk);
+  hipLaunchKernelGGL((attend_mfma_kernel<DT, D>), grid, dim3(kNT), lds, st, sh, P, ul, q, k, v, lse, out);
+  return hipGetLastError();
+}
+
 template <int DT, int D>
 hipError_t rowstats_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, float* lse,
                       hipStream_t st) {
@@ -380,6 +675,18 @@ hipError_t launch_prefill_rowstats_mfma(const Shape& sh, int P, UnitList ul, con
     case F16 * 1000 + 128: return rowstats_t<F16, 128>(sh, P, ul, q, k, lse, st);
     case BF16 * 1000 + 64: return rowstats_t<BF16, 64>(sh, P, ul, q, k, lse, st);
     case BF16 * 1000 + 128: return rowstats_t<BF16, 128>(sh, P, ul, q, k, lse, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_attend_mfma(const Shape& sh, int P, UnitList ul, const void* q, const void* k,
+                                      const void* v, float* lse, float* out, hipStream_t st) {
+  if (ul.n <= 0) return hipSuccess;
+  switch (sh.dtype * 1000 + sh.d) {
+    case F16 * 1000 + 64: return attend_t<F16, 64>(sh, P, ul, q, k, v, lse, out, st);
+    case F16 * 1000 + 128: return attend_t<F16, 128>(sh, P, ul, q, k, v, lse, out, st);
+    case BF16 * 1000 + 64: return attend_t<BF16, 64>(sh, P, ul, q, k, v, lse, out, st);
+    case BF16 * 1000 + 128: return attend_t<BF16, 128>(sh, P, ul, q, k, v, lse, out, st);
   }
   return hipErrorInvalidValue;
 }

@@ -14,7 +14,8 @@ import torch
 from tests import harness
 from workloads import configs
 from workloads.configs import FULL, H2O, HASH, LOCAL, SPECIAL
-from workloads.generate import generate_layer
+from oracle import attention, lockstep
+from workloads.generate import generate_layer, unit_sequence
 
 pytestmark = pytest.mark.gpu
 
@@ -65,3 +66,34 @@ def test_llama65b_fastgen_full_size():
 def test_hashevict_full_size():
     rep = run_full("hashevict_lsh", 4)
     assert rep.decisions == 4 * 1024
+
+
+@pytest.mark.parametrize("name", ["hashevict_lsh", "opt30b_decode_h2o"])
+def test_prompt_output_full_size(name):
+    """The optional prompt output at a full prompt (all units of one layer in
+    one launch): sampled rows of sampled units against the float64 oracle,
+    every row finite."""
+    w = configs.get(name)
+    print(f"\n[fullsize] {name}: prompt output, units={w.units_per_layer} P={w.prompt}", flush=True)
+    inp = generate_layer(w, 0, "cuda", 1)
+    kv = harness.make_cache(w, inp)
+    po = torch.empty((w.batch, w.heads, w.prompt, w.head_dim), dtype=torch.float32, device="cuda")
+    ids = inp.ids[:, :w.prompt].contiguous() if inp.ids is not None else None
+    kv.prefill(0, inp.prompt_q, inp.prompt_k, inp.prompt_v, ids, po)
+    torch.cuda.synchronize()
+    kv.close()
+    assert bool(torch.isfinite(po).all())
+    rng = np.random.default_rng(0)
+    inp_cpu = inp.to("cpu")
+    P, scale = w.prompt, 1.0 / np.sqrt(w.head_dim)
+    worst = 0.0
+    for b, h in sample_units(w, 3):
+        Q, K, V = unit_sequence(inp_cpu, b, h)
+        rows = sorted({0, 1, 63, 64, 127, 128, P - 2, P - 1, *rng.integers(0, P, 8).tolist()})
+        got = po[b, h, rows].cpu().double().numpy()
+        for n, i in enumerate(rows):
+            _, ref = attention.attend(Q[i], K[:i + 1], V[:i + 1], scale)
+            e = np.max(np.abs(got[n] - ref)) / max(np.max(np.abs(ref)), 1e-30)
+            worst = max(worst, e)
+            assert e <= lockstep.OUT_RTOL, (b, h, i, e)
+    print(f"[fullsize] prompt output max rel err {worst:.2e}", flush=True)

@@ -79,8 +79,23 @@ def test_fastgen_scaled(decode_path):
 def test_hash_scaled(decode_path):
     w = configs.scaled("hashevict_lsh", batch=2, heads=4, prompt=600, steps=80)
     assert w.hash_budget == 300
-    rep, _ = run_and_check(w)
+    rep, _ = run_and_check(w, prompt_out=True)
     assert rep.decisions == 8 * 80
+
+
+@pytest.mark.parametrize("dtype,P", [("f16", 200), ("bf16", 129), ("bf16", 64)])
+def test_prompt_out_d64_16bit(dtype, P):
+    """Matrix-core prompt output at head_dim 64: a ragged prompt, one just
+    past a 128-query block, and exactly one 64-key tile."""
+    w = dataclasses.replace(configs.scaled("tiny_h2o", prompt=P, steps=20, batch=2), dtype=dtype)
+    rep, _ = run_and_check(w, prompt_out=True)
+    assert rep.max_prompt_out_rel > 0
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prompt_out_one_token(dtype):
+    w = dataclasses.replace(configs.scaled("opt6.7b_layer_h2o", batch=1, heads=2, prompt=1, steps=30), dtype=dtype)
+    run_and_check(w, policy=[H2O] * 2, heavy=[4] * 2, recent=[4] * 2, prompt_out=True)
 
 
 def test_budget_covering_context_is_full_attention(decode_path):
