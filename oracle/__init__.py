@@ -19,6 +19,9 @@ method:
                   special+punctuation tokens, frequency (H2O) + local.
 * ``hashevict`` - HashEvict's sign sketches, Hamming ranking, prompt replay
                   and pre-attention replacement.
+* ``persistence`` - the persistence-of-importance reading of [SH]: pivotal
+                  bits (weight >= 1/|A|) over a history window, eviction of
+                  the lowest count outside the recent window.
 * ``lockstep``  - replays a unit against a GPU run's logs with the near-tie
                   acceptance band, and measures the score and output errors.
 
@@ -39,5 +42,8 @@ Sources (cited per function):
 Parity pins: every function is pinned by a CPU test against a textbook
 routine, a closed form, an invariant or brute force (tests/test_oracle_*.py).
 Parity unpinned: the H2O score trajectory for generic inputs beyond those
-invariants and brute-force checks -- the pages print no worked example.
+invariants and brute-force checks -- the pages print no worked example; the
+persistence rule itself is a reading of a one-sentence hypothesis, so its
+pins (closed forms on constructed inputs, invariants, a replay of recorded
+weights) check the oracle against that reading, not against the page.
 """

@@ -21,6 +21,14 @@ candidate score.
 Tolerances: attention output per (unit, step) max|o_gpu - o_ref| <=
 2e-3 max|o_ref|; accumulated scores |S_gpu - S_ref| <= 1e-5 S_ref per kept
 slot; kept sets compared as sets of positions.
+
+Persistence counts are integers decided by comparing a weight with 1/|A|;
+the oracle flags the bits whose weight lies within a relative 1e-5 of that
+threshold as ambiguous, bounds each count between its value with those bits
+clear and set, and accepts a GPU choice that some setting of them explains.
+The GPU's exported histories must equal the oracle's on every unambiguous
+bit; at the prompt the oracle then takes the GPU's ambiguous bits, so the
+replay continues from the GPU's state.
 """
 
 from __future__ import annotations
@@ -30,7 +38,7 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-from . import fastgen, h2o, hashevict
+from . import fastgen, h2o, hashevict, persistence
 from .attention import attend, causal_attention
 
 TIE_BAND = 1e-6
@@ -269,4 +277,94 @@ def check_hash(Q, K, V, Wp, P: int, B: int, scale: float, gpu: GpuUnit, steps: O
         _check_out(rep, s, gpu.out[s], attend(Q[t], K[A], V[A], scale)[1])
     if not np.array_equal(np.sort(np.asarray(gpu.final_pos, dtype=np.int64)), np.sort(np.array(cache))):
         rep.failures.append("final kept set differs")
+    return rep
+
+
+def _as_bits(x) -> np.ndarray:
+    """Histories exported in the float64 score array: the raw 64-bit patterns."""
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64)).view(np.uint64)
+
+
+def _count_bounds(hist: np.ndarray, amb: np.ndarray):
+    lo = persistence.count(hist & ~amb)
+    hi = persistence.count(hist | amb)
+    return lo, hi
+
+
+def _check_history_bits(rep: UnitReport, where: str, pos, gpu_bits, ref_pos, ref_hist, ref_amb) -> None:
+    ref = {int(p): (int(h), int(a)) for p, h, a in zip(ref_pos, ref_hist, ref_amb)}
+    for p, g in zip(pos, gpu_bits):
+        r = ref.get(int(p))
+        if r is None:
+            continue                      # set mismatch is reported separately
+        if (int(g) ^ r[0]) & ~r[1] & ((1 << 64) - 1):
+            rep.failures.append(f"{where}: history of position {int(p)} {int(g):#x} vs {r[0]:#x} "
+                                f"(ambiguous {r[1]:#x})")
+
+
+def check_persist(Q, K, V, P: int, heavy: int, recent: int, window: int, scale: float, gpu: GpuUnit,
+                  steps: Optional[int] = None) -> UnitReport:
+    """Persistence-count eviction (Scissorhands reading)."""
+    rep = UnitReport()
+    T = len(gpu.evicted) if steps is None else steps
+    budget = heavy + recent
+    hist, amb = persistence.prefill_histories(Q[:P], K[:P], scale, window)
+    gpos = np.asarray(gpu.prefill_pos, dtype=np.int64)
+    ref = h2o.prefill_select(persistence.count(hist).astype(np.float64), heavy, recent)
+    if len(np.unique(gpos)) != len(gpos):
+        rep.failures.append("prefill: duplicate positions")
+    if not np.array_equal(np.sort(gpos), ref):
+        ok = P > budget and len(gpos) == budget and set(range(P - recent, P)) <= set(gpos.tolist())
+        lo, hi = _count_bounds(hist, amb)
+        kept_heavy = [int(j) for j in gpos if j < P - recent]
+        dropped = sorted(set(range(P - recent)) - set(kept_heavy))
+        if ok and kept_heavy and dropped:
+            weakest = min((int(hi[j]), j) for j in kept_heavy)
+            strongest = max((int(lo[k]), k) for k in dropped)
+            ok = strongest < weakest
+        if ok:
+            rep.adopted += 1
+        else:
+            rep.failures.append("prefill: kept set not explained by the ambiguous bits")
+    kept = np.sort(gpos)
+    k_hist, k_amb = hist[kept].copy(), amb[kept].copy()
+    if gpu.prefill_S is not None:
+        order = np.argsort(gpos)
+        gbits = _as_bits(gpu.prefill_S)[order]
+        _check_history_bits(rep, "prefill", kept, gbits, kept, k_hist, k_amb)
+        k_hist = (k_hist & ~k_amb) | (gbits & k_amb)
+        k_amb = np.zeros_like(k_amb)
+    _check_prompt_out(rep, gpu, Q, K, V, P, scale)
+    cache = persistence.Cache(kept, k_hist, k_amb)
+    for s in range(T):
+        t = P + s
+        o, A, hA, aA, _ = persistence.attend_step(cache, t, Q[t], K, V, scale, window)
+        _check_out(rep, s, gpu.out[s], o)
+        g = int(gpu.evicted[s])
+        if len(A) <= budget:
+            if g != -1:
+                rep.failures.append(f"step {s}: evicted {g} with the cache under budget")
+            cache = persistence.Cache(A, hA, aA)
+            continue
+        rep.decisions += 1
+        i_ref = persistence.victim(A, hA, t, recent)
+        if g == int(A[i_ref]):
+            cache = persistence.remove(A, hA, aA, i_ref)
+            continue
+        where = np.flatnonzero(A == g)
+        cand = persistence.candidates(A, t, recent)
+        lo, hi = _count_bounds(hA, aA)
+        ok = len(where) == 1 and int(where[0]) in set(int(x) for x in cand)
+        if ok:
+            gi = int(where[0])
+            ok = not any((int(hi[k]), int(A[k])) < (int(lo[gi]), g) for k in cand if k != gi)
+        if ok:
+            rep.adopted += 1
+        else:
+            rep.failures.append(f"step {s}: GPU evicted {g}, oracle {int(A[i_ref])}")
+        cache = persistence.remove(A, hA, aA, int(where[0]) if len(where) == 1 else i_ref)
+    if not np.array_equal(np.sort(np.asarray(gpu.final_pos, dtype=np.int64)), np.sort(cache.pos)):
+        rep.failures.append("final kept set differs")
+    if gpu.final_S is not None:
+        _check_history_bits(rep, "final", gpu.final_pos, _as_bits(gpu.final_S), cache.pos, cache.hist, cache.amb)
     return rep

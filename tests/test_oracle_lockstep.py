@@ -104,3 +104,83 @@ def test_hash_checker_accepts_oracle_and_rejects_wrong_victim():
     assert h.min() < h.max()
     g.evicted[0] = near
     assert not lockstep.check_hash(Q, K, V, W, Pq, B, 0.25, g).ok
+
+
+def persist_gpu_unit(tr, P):
+    """A GPU log made from the persistence oracle's own trajectory (histories
+    exported as the raw bits of float64 scores, as the library does)."""
+    return lockstep.GpuUnit(prefill_pos=tr.prefill_kept.copy(), evicted=tr.evicted.copy(), out=tr.out.copy(),
+                            final_pos=tr.final.pos.copy(),
+                            prefill_S=tr.prefill_hist.astype(np.uint64).view(np.float64).copy(),
+                            final_S=tr.final.hist.astype(np.uint64).view(np.float64).copy())
+
+
+def test_persist_checker_accepts_oracle_and_rejects_mistakes():
+    from oracle import persistence
+    rng = np.random.default_rng(11)
+    P, T, d, hh, r, w = 40, 30, 8, 6, 6, 16
+    Q, K, V = (rng.standard_normal((P + T, d)) for _ in range(3))
+    tr = persistence.run_unit(Q, K, V, P, hh, r, w, 0.6)
+    g = persist_gpu_unit(tr, P)
+    rep = lockstep.check_persist(Q, K, V, P, hh, r, w, 0.6, g)
+    assert rep.ok and rep.adopted == 0 and rep.decisions == T, rep.failures
+    # a different victim at one step (a token that stays kept in the oracle)
+    s = int(np.flatnonzero(tr.evicted >= 0)[3])
+    bad = persistence_victim_alternative(Q, K, V, P, hh, r, w, tr, s)
+    g2 = persist_gpu_unit(tr, P)
+    g2.evicted[s] = bad
+    assert not lockstep.check_persist(Q, K, V, P, hh, r, w, 0.6, g2).ok
+    # one flipped history bit in the final export
+    g3 = persist_gpu_unit(tr, P)
+    bits = g3.final_S.view(np.uint64)
+    bits[0] ^= np.uint64(1)
+    assert not lockstep.check_persist(Q, K, V, P, hh, r, w, 0.6, g3).ok
+    # one flipped bit in the prompt export
+    g4 = persist_gpu_unit(tr, P)
+    g4.prefill_S.view(np.uint64)[2] ^= np.uint64(4)
+    assert not lockstep.check_persist(Q, K, V, P, hh, r, w, 0.6, g4).ok
+    # a prompt kept set with one heavy token swapped for a dropped one
+    g5 = persist_gpu_unit(tr, P)
+    heavy_kept = [j for j in tr.prefill_kept if j < P - r]
+    dropped = sorted(set(range(P - r)) - set(tr.prefill_kept.tolist()))
+    cnt = persistence.count(tr.prompt_hist)
+    lowest_dropped = min(dropped, key=lambda j: (cnt[j], j))
+    strongest_kept = max(heavy_kept, key=lambda j: (cnt[j], j))
+    if cnt[lowest_dropped] < cnt[strongest_kept]:
+        g5.prefill_pos[list(g5.prefill_pos).index(strongest_kept)] = lowest_dropped
+        assert not lockstep.check_persist(Q, K, V, P, hh, r, w, 0.6, g5).ok
+
+
+def persistence_victim_alternative(Q, K, V, P, hh, r, w, tr, s):
+    """A candidate at step s other than the oracle's victim, with a higher count."""
+    from oracle import persistence
+    cache, _, _ = persistence.prefill(Q[:P], K[:P], hh, r, w, 0.6)
+    for k in range(s + 1):
+        t = P + k
+        _, A, h, a, _ = persistence.attend_step(cache, t, Q[t], K, V, 0.6, w)
+        i = persistence.victim(A, h, t, r)
+        if k == s:
+            cand = persistence.candidates(A, t, r)
+            c = persistence.count(h)
+            others = [j for j in cand if j != i and c[j] > c[i]]
+            return int(A[others[0]])
+        cache = persistence.remove(A, h, a, i)
+
+
+def test_persist_checker_accepts_ambiguous_choice():
+    """Identical keys: every weight sits exactly on the threshold, so every bit
+    is ambiguous; any candidate is then an admissible victim and is adopted."""
+    from oracle import persistence
+    rng = np.random.default_rng(3)
+    P, T, d, hh, r, w = 30, 10, 8, 4, 8, 8
+    Q = rng.standard_normal((P + T, d))
+    K = np.tile(rng.standard_normal(d), (P + T, 1))
+    V = rng.standard_normal((P + T, d))
+    tr = persistence.run_unit(Q, K, V, P, hh, r, w, 0.5)
+    g = persist_gpu_unit(tr, P)
+    # at step 0 evict the newest candidate instead of the oldest
+    t = P
+    g.evicted[0] = t - r
+    rep = lockstep.check_persist(Q, K, V, P, hh, r, w, 0.5, g, steps=1)
+    assert rep.adopted == 1
+    assert not any("GPU evicted" in f for f in rep.failures), rep.failures

@@ -6,7 +6,12 @@ at that size): a 20% H2O budget is floor(0.1 P) heavy-hitter slots plus
 floor(0.1 P) recent slots; the FastGen local window is floor(0.25 P) and its
 frequency part floor(0.1 P); the HashEvict budget of 50% is floor(0.5 P).
 
-Policy codes match the C header: FULL=0, H2O=1, LOCAL=2, SPECIAL=3, HASH=4.
+Policy codes match the C header: FULL=0, H2O=1, LOCAL=2, SPECIAL=3, HASH=4,
+PERSIST=5.
+
+Beside the five workloads, ``opt30b_decode_persist`` runs the OPT-30B-shaped
+decode under the persistence-count rule (the Scissorhands reading) with the
+same 20% budget, so the two scoring rules are measured on one shape.
 """
 
 from __future__ import annotations
@@ -15,8 +20,9 @@ import dataclasses
 from dataclasses import dataclass, field
 from typing import Dict, List, Tuple
 
-FULL, H2O, LOCAL, SPECIAL, HASH = 0, 1, 2, 3, 4
-POLICY_NAMES = {FULL: "full", H2O: "h2o", LOCAL: "local", SPECIAL: "special", HASH: "hash"}
+FULL, H2O, LOCAL, SPECIAL, HASH, PERSIST = 0, 1, 2, 3, 4, 5
+POLICY_NAMES = {FULL: "full", H2O: "h2o", LOCAL: "local", SPECIAL: "special", HASH: "hash",
+                PERSIST: "persist"}
 
 
 @dataclass(frozen=True)
@@ -30,13 +36,14 @@ class Workload:
     dtype: str                 # storage dtype of q/k/v: "f32" | "f16" | "bf16"
     prompt: int                # P
     steps: int                 # T decode steps
-    family: str                # "h2o" | "fastgen" | "hash"
+    family: str                # "h2o" | "fastgen" | "hash" | "persist"
     structure: str             # "dirs4" | "zipf_dir" | "clusters"
     heavy: int = 0             # H2O heavy-hitter slots (family h2o)
     recent: int = 0            # H2O recent window (family h2o)
     local_window: int = 0      # FastGen LOCAL window W (also the FREQ+LOCAL recent part)
     freq_heavy: int = 0        # FastGen FREQ+LOCAL heavy part
     hash_budget: int = 0       # HashEvict budget B
+    history_window: int = 0    # persistence heads: steps of pivotal history counted (1..64)
     sketch_bits: int = 32
     vocab: int = 32000
     special_ids: Tuple[int, ...] = (0, 1, 2, 3)
@@ -68,6 +75,8 @@ class Workload:
         H = self.heads
         if self.family == "h2o":
             return [H2O] * H, [self.heavy] * H, [self.recent] * H
+        if self.family == "persist":
+            return [PERSIST] * H, [self.heavy] * H, [self.recent] * H
         if self.family == "hash":
             return [HASH] * H, [self.hash_budget] * H, [0] * H
         if self.family == "fastgen":
@@ -87,6 +96,11 @@ class Workload:
                     heavy.append(0); recent.append(0)
             return pol, heavy, recent
         raise ValueError(self.family)
+
+    def window_table(self, layer: int = 0) -> List[int]:
+        """History window per head of one layer (persistence heads; 0 elsewhere)."""
+        pol = self.policy_table(layer)[0]
+        return [self.history_window if p == PERSIST else 0 for p in pol]
 
     def keep_ids(self) -> List[int]:
         return sorted(set(self.special_ids) | set(self.punct_ids))
@@ -133,7 +147,14 @@ _add(Workload(
     prompt=8192, steps=1024, family="hash", structure="clusters", **_hash(8192),
     description="HashEvict: batch 16, 32 heads, d=128, bf16, P=8192, T=1024, budget 50%, 32-bit sketches"))
 
+_add(Workload(
+    name="opt30b_decode_persist", index=6, layers=48, batch=32, heads=56, head_dim=128, dtype="bf16",
+    prompt=2048, steps=256, family="persist", structure="zipf_dir", history_window=64, **_h2o20(2048),
+    description="OPT-30B-shaped decode under the persistence-count rule: 48 layers, batch 32, 56 heads, "
+                "d=128, bf16, P=2048, T=256, 20% budget (204 + 204), 64-step history"))
+
 ORDER = ["tiny_h2o", "opt6.7b_layer_h2o", "opt30b_decode_h2o", "llama65b_fastgen", "hashevict_lsh"]
+NEXT = ["opt30b_decode_persist"]
 
 
 def get(name: str) -> Workload:
@@ -149,7 +170,7 @@ def scaled(name: str, **over) -> Workload:
     w = WORKLOADS[name]
     P = over.get("prompt", w.prompt)
     derived: Dict[str, int] = {}
-    if w.family == "h2o" and w.name != "tiny_h2o":
+    if w.family in ("h2o", "persist") and w.name != "tiny_h2o":
         derived = _h2o20(P)
     elif w.family == "fastgen":
         derived = _fastgen(P)
