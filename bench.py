@@ -39,12 +39,14 @@ DEFAULT_WORKLOAD = "opt30b_decode_h2o"
 def _oracle_unit(args):
     """One unit through the float64 oracle (prefill + every decode step)."""
     import numpy as np
-    from oracle import fastgen, h2o, hashevict
+    from oracle import fastgen, h2o, hashevict, persistence
     kind, Q, K, V, P, a, b, scale, extra = args
     Q, K, V = (np.asarray(x, dtype=np.float64) for x in (Q, K, V))
     t0 = time.perf_counter()
     if kind == "h2o":
         h2o.run_unit(Q, K, V, P, a, b, scale)
+    elif kind == "persist":
+        persistence.run_unit(Q, K, V, P, a, b, extra, scale)
     elif kind == "hash":
         hashevict.run_unit(Q, K, V, np.asarray(extra, dtype=np.float64), P, a, scale)
     else:
@@ -73,6 +75,8 @@ def cpu_baseline(w, n_units: int, workers: int):
             Q, K, V = (x.astype(np.float32) for x in unit_sequence(inp, 0, h))
             if w.family == "h2o":
                 tasks.append(("h2o", Q, K, V, w.prompt, hv[h], rc[h], scale, None))
+            elif w.family == "persist":
+                tasks.append(("persist", Q, K, V, w.prompt, hv[h], rc[h], scale, w.window_table(0)[h]))
             elif w.family == "hash":
                 tasks.append(("hash", Q, K, V, w.prompt, hv[h], 0, scale, inp.proj.float().numpy()))
             else:
@@ -104,7 +108,8 @@ def decode_bytes_per_layer_step(w, ids=None) -> float:
     """Algorithmic bytes of one layer's decode step, averaged over the T steps:
     per unit, the kept K and V rows read (n slots x d x s x 2), the per-slot
     metadata the policy needs (H2O: score read and write at the 4-byte float32
-    minimum plus the position, 12 B; HashEvict: sketch and position, 8 B), the
+    minimum plus the position, 12 B; persistence counts: the 64-bit history
+    read and written plus the position, 20 B; HashEvict: sketch and position, 8 B), the
     step's q, k, v, the new token's K/V write and the fp32 output.  n is the
     unit's kept count at that step: B for H2O and HashEvict, W for the local
     window, t for the full cache, and for the special policy the number of
@@ -116,6 +121,9 @@ def decode_bytes_per_layer_step(w, ids=None) -> float:
     if w.family == "h2o":
         B = w.heavy + w.recent
         return w.units_per_layer * (B * d * s * 2 + B * 12 + io)
+    if w.family == "persist":
+        B = w.heavy + w.recent
+        return w.units_per_layer * (B * d * s * 2 + B * 20 + io)
     if w.family == "hash":
         B = w.hash_budget
         return w.units_per_layer * (B * d * s * 2 + B * 8 + io + 4)
@@ -170,15 +178,22 @@ def prefill_flops_per_layer(w, prompt_out: bool) -> float:
     """Algorithmic prefill flops of one layer: one causal Q K^T pass (2 d flops
     per query-key pair with key <= query) for the row statistics and one for
     the column sums of every heavy-hitter head, plus one P V pass per unit when
-    the prompt output is produced."""
+    the prompt output is produced.  A persistence head needs its last `window`
+    rows twice (their row statistics, then their bits)."""
     pairs = w.prompt * (w.prompt + 1) / 2
     pol = w.policy_table(0)[0]
     h2o_units = w.batch * sum(1 for p in pol if p == 1)
     units = w.batch * w.heads
     per = 2.0 * w.head_dim * pairs
+    persist = 0.0
+    for p, win in zip(pol, w.window_table(0)):
+        if p == 5:
+            rows = min(win, w.prompt)
+            tail_pairs = rows * w.prompt - rows * (rows - 1) / 2     # sum of (i + 1) over the last rows
+            persist += w.batch * 2.0 * w.head_dim * tail_pairs
     if prompt_out:
-        return per * (2 * units + h2o_units)
-    return per * 2 * h2o_units
+        return per * (2 * units + h2o_units) + persist
+    return per * 2 * h2o_units + 2 * persist
 
 
 def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, cold: bool = False,
@@ -208,6 +223,8 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
         kw.update(keep_ids=w.keep_ids(), vocab=w.vocab)
     if 4 in pol:
         kw.update(proj=inputs[0].proj)
+    if 5 in pol:
+        kw.update(history=np.tile(np.array(w.window_table(0), dtype=np.int32), w.layers))
     kv = KVCache(w.layers, w.batch, w.heads, w.head_dim, w.context, inputs[0].prompt_q.dtype,
                  *tabs, device=dev, **kw)
     ids = [x.ids for x in inputs]
@@ -337,7 +354,7 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         workers = min(16, len(os.sched_getaffinity(0)))
-        n_units = a.cpu_units or {"h2o": 256, "fastgen": 64, "hash": 32}[w.family]
+        n_units = a.cpu_units or {"h2o": 256, "persist": 256, "fastgen": 64, "hash": 32}[w.family]
         cpu = cpu_baseline(w, n_units, workers)
         print(f"[bench] cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
 
@@ -359,7 +376,9 @@ def main():
                    "budget": {"h2o": f"{w.heavy} heavy + {w.recent} recent",
                               "fastgen": f"per head: full / local {w.local_window} / special+punct / "
                                          f"{w.freq_heavy} frequency + {w.local_window} local",
-                              "hash": f"{w.hash_budget} slots, {w.sketch_bits}-bit sketches"}[w.family]},
+                              "hash": f"{w.hash_budget} slots, {w.sketch_bits}-bit sketches",
+                              "persist": f"{w.heavy} heavy + {w.recent} recent by persistence count over "
+                                         f"{w.history_window} steps"}[w.family]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(w.name),
                      "kernel": kernel, "bytes_per_launch": bytes_launch,

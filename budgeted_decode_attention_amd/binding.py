@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libkvevict.so")
 
 KVE_OK, KVE_EINVAL, KVE_ESTATE, KVE_ENOMEM, KVE_EDEVICE, KVE_EUNSUPPORTED = range(6)
 KVE_F32, KVE_F16, KVE_BF16 = 0, 1, 2
-KVE_FULL, KVE_H2O, KVE_LOCAL, KVE_SPECIAL, KVE_HASH = 0, 1, 2, 3, 4
+KVE_FULL, KVE_H2O, KVE_LOCAL, KVE_SPECIAL, KVE_HASH, KVE_PERSIST = 0, 1, 2, 3, 4, 5
 
 DTYPE_CODES = {torch.float32: KVE_F32, torch.float16: KVE_F16, torch.bfloat16: KVE_BF16}
 CODE_DTYPES = {v: k for k, v in DTYPE_CODES.items()}
@@ -45,6 +45,7 @@ class kve_config(ctypes.Structure):
         ("recent", ctypes.POINTER(ctypes.c_int32)),
         ("vocab", ctypes.c_int32), ("keep_token_bitmap", ctypes.POINTER(ctypes.c_uint32)),
         ("sketch_bits", ctypes.c_int32), ("lsh_proj_bf16", ctypes.POINTER(ctypes.c_uint16)),
+        ("history", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -109,8 +110,11 @@ def keep_bitmap(keep_ids: Sequence[int], vocab: int) -> np.ndarray:
 
 def make_config(layers: int, batch: int, heads: int, head_dim: int, max_context: int, dtype: torch.dtype,
                 policy, heavy, recent, softmax_scale: float = 0.0, keep_ids: Sequence[int] = (),
-                vocab: int = 0, proj: Optional[torch.Tensor] = None):
-    """Returns (kve_config, keepalive) -- keepalive holds the host tables."""
+                vocab: int = 0, proj: Optional[torch.Tensor] = None, history=None):
+    """Returns (kve_config, keepalive) -- keepalive holds the host tables.
+
+    history: per-head history windows [layers * heads] (PERSIST heads), or None.
+    """
     pol = np.ascontiguousarray(np.asarray(policy, dtype=np.int32).reshape(-1))
     hv = np.ascontiguousarray(np.asarray(heavy, dtype=np.int32).reshape(-1))
     rc = np.ascontiguousarray(np.asarray(recent, dtype=np.int32).reshape(-1))
@@ -136,6 +140,10 @@ def make_config(layers: int, batch: int, heads: int, head_dim: int, max_context:
         keep.append(bits)
         cfg.sketch_bits = int(p.shape[-1])
         cfg.lsh_proj_bf16 = bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16))
+    if history is not None:
+        hw = np.ascontiguousarray(np.asarray(history, dtype=np.int32).reshape(-1))
+        keep.append(hw)
+        cfg.history = hw.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     return cfg, keep
 
 
@@ -193,14 +201,14 @@ class KVCache:
     def __init__(self, layers: int, batch: int, heads: int, head_dim: int, max_context: int,
                  dtype: torch.dtype, policy, heavy, recent, softmax_scale: float = 0.0,
                  keep_ids: Sequence[int] = (), vocab: int = 0, proj: Optional[torch.Tensor] = None,
-                 device="cuda"):
+                 history=None, device="cuda"):
         self.layers, self.batch, self.heads, self.head_dim = layers, batch, heads, head_dim
         dev = torch.device(device)
         if dev.type == "cuda" and dev.index is None:
             dev = torch.device("cuda", torch.cuda.current_device())
         self.max_context, self.dtype, self.device = max_context, dtype, dev
         self.cfg, self._keep = make_config(layers, batch, heads, head_dim, max_context, dtype, policy, heavy,
-                                           recent, softmax_scale, keep_ids, vocab, proj)
+                                           recent, softmax_scale, keep_ids, vocab, proj, history)
         self.workspace_bytes = kvevict_workspace_size(self.cfg)
         self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
         self.handle = kvevict_create(self.cfg, self.workspace)

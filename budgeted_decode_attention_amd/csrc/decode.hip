@@ -5,6 +5,9 @@
 // the statistics that drive a greedy eviction; the lowest-scoring token
 // outside the recent window leaves and the new token takes its slot.  FastGen
 // review page: the same step under per-head positional policies.
+// Scissorhands summary page (persistence of importance), as read here: the
+// same step with the score replaced by the number of recent steps at which a
+// token's weight reached the uniform weight 1 / |A|.
 //
 // Layout: slot rows of d elements, 16 bytes per lane; LPR lanes cover one row
 // (a row group) and the workgroup covers NT / LPR rows per load wave.  Logits
@@ -143,14 +146,16 @@ __device__ inline void stash_groups(const float* acc, float* red) {
   for (int j = 0; j < R::EPL; ++j) red[rg * D + col * R::EPL + j] = acc[j];
 }
 
-// The head's policy after attention: H2O score update and victim, or the
-// positional rule; writes token t's key/value/score/position into its slot.
-// wts[r] = exp(l_r - M) for the n kept slots (read for H2O heads only),
-// e_new = exp(l_t - M), invL = 1 / (sum of every weight).  Control flow is
-// uniform over the workgroup; contains barriers.
+// The head's policy after attention: H2O score update and victim, the
+// persistence-count update and victim, or the positional rule; writes token
+// t's key/value/score/position into its slot.  wts[r] = exp(l_r - M) for the
+// n kept slots (read for H2O and PERSIST heads only), e_new = exp(l_t - M),
+// L = the sum of every weight, invL = 1 / L.  Control flow is uniform over
+// the workgroup; contains barriers.
 template <int DT, int D>
 __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const DecodeIO& io, const HeadMeta& m,
-                                   int u, int n, const float* wts, float e_new, double invL, MinKey* kscr) {
+                                   int u, int n, const float* wts, float e_new, double L, double invL,
+                                   MinKey* kscr) {
   using R = Rows<DT, D>;
   const int tid = threadIdx.x;
   const int t = io.t;
@@ -194,6 +199,54 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
     if (n >= m.heavy + m.recent) {
       if (best.slot == n) {
         evicted = t;                           // the new token itself scores lowest
+      } else {
+        wslot = best.slot;
+        evicted = best.pos;
+      }
+    } else {
+      wslot = n;
+    }
+  } else if (m.policy == PERSIST) {
+    // history bit k = pivotal k steps ago; pivotal: weight / L >= 1 / (n + 1),
+    // tested as w (n + 1) >= L in float64 (exact for equal weights)
+    const int lim = t - m.recent;
+    const unsigned long long wm = m.window >= 64 ? ~0ull : ((1ull << m.window) - 1ull);
+    const double nA = (double)(n + 1);
+    unsigned long long* Hs = reinterpret_cast<unsigned long long*>(c.S) + slot0;
+    MinKey best{INFINITY, INT32_MAX, INT32_MAX};
+    for (int r0 = tid; r0 < n; r0 += 4 * kNT) {
+      unsigned long long hv[4];
+      int pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i * kNT;
+        hv[i] = r < n ? Hs[r] : 0ull;
+        pv[i] = r < n ? c.pos[slot0 + r] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i * kNT;
+        if (r < n) {
+          const unsigned long long piv = (double)wts[r] * nA >= L ? 1ull : 0ull;
+          const unsigned long long h = ((hv[i] << 1) | piv) & wm;
+          Hs[r] = h;
+          if (pv[i] <= lim) {
+            const MinKey k{(double)__popcll(h), pv[i], r};
+            if (key_less(k, best)) best = k;
+          }
+        }
+      }
+    }
+    const unsigned long long h_new = (double)e_new * nA >= L ? 1ull : 0ull;
+    s_new = __longlong_as_double((long long)h_new);
+    if (tid == 0 && t <= lim) {
+      const MinKey k{(double)h_new, t, n};
+      if (key_less(k, best)) best = k;
+    }
+    best = block_argmin<kNT>(best, kscr);      // barriers inside: history updates done
+    if (n >= m.heavy + m.recent) {
+      if (best.slot == n) {
+        evicted = t;
       } else {
         wslot = best.slot;
         evicted = best.pos;
@@ -299,7 +352,7 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
     for (int g = 0; g < R::RPI; ++g) s += red[g * D + i];
     io.out[(size_t)u * D + i] = (float)((double)s * invL);
   }
-  policy_step<DT, D>(sh, c, io, m, u, n, wts, with_new ? wts[n] : 0.f, invL, kscr);
+  policy_step<DT, D>(sh, c, io, m, u, n, wts, with_new ? wts[n] : 0.f, L, invL, kscr);
 }
 
 // ------------------------------------------------------------------ split
@@ -327,7 +380,8 @@ __global__ KVE_DECODE_ATTR void decode_partial_kernel(Shape sh, LayerCache c, De
   float qf[R::EPL];
   St<DT>::unpack(ld16((const char*)io.q + ((size_t)u * D + col * R::EPL) * R::ES), qf);
 
-  row_logits<DT, D>(Kb, qf, sh.scale, c0, c1, lg, m.policy == H2O ? sp.logits + slot0 : nullptr);
+  const bool keep_logits = m.policy == H2O || m.policy == PERSIST;   // the combine needs every weight
+  row_logits<DT, D>(Kb, qf, sh.scale, c0, c1, lg, keep_logits ? sp.logits + slot0 : nullptr);
   __syncthreads();
   const int len = c1 - c0;
   float mx = -INFINITY;
@@ -404,7 +458,7 @@ __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, De
   const float e_new = with_new ? expf(s_new - M) : 0.f;
   for (int ch = tid; ch < nch; ch += kNT) gf[ch] = expf(part[ch * (D + 2) + D] - M);
   double ls = 0.0;
-  if (m.policy == H2O) {
+  if (m.policy == H2O || m.policy == PERSIST) {
     // exact weights of every kept slot, recomputed from the stored logits
     const float* lgs = sp.logits + slot0;
     for (int r0 = tid; r0 < n; r0 += 4 * kNT) {
@@ -437,7 +491,7 @@ __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, De
     }
     io.out[(size_t)u * D + i] = (float)((double)s * invL);
   }
-  policy_step<DT, D>(sh, c, io, m, u, n, wts, e_new, invL, kscr);
+  policy_step<DT, D>(sh, c, io, m, u, n, wts, e_new, L, invL, kscr);
 }
 
 hipError_t set_lds(const void* fn, size_t lds) {

@@ -81,7 +81,8 @@ int elem_size(int dtype) { return dtype == KVE_F32 ? 4 : 2; }
 
 int head_capacity(int policy, int heavy, int recent, int max_context) {
   switch (policy) {
-    case KVE_H2O: return heavy + recent;
+    case KVE_H2O:
+    case KVE_PERSIST: return heavy + recent;
     case KVE_LOCAL: return recent;
     case KVE_HASH: return heavy;
     default: return max_context;       // FULL, SPECIAL
@@ -95,9 +96,10 @@ struct LayerInfo {
   bool uniform = true;   // every head of the layer has the same capacity
   int chunk = 0;         // split-decode chunk (slots)
   int nch = 0;           // chunks per unit
-  bool any_h2o = false, any_hash = false, any_special = false;
+  bool any_h2o = false, any_hash = false, any_special = false, any_persist = false;
   int max_hash_budget = 0;
-  std::vector<int32_t> h2o_units, hash_units;
+  int max_window = 0;    // largest history window of the layer's PERSIST heads
+  std::vector<int32_t> h2o_units, hash_units, persist_units;
 };
 
 kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
@@ -130,6 +132,20 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
             return fail(KVE_EINVAL, "layer %d head %d: heavy + recent exceeds max_context", l, h);
           li.any_h2o = true;
           break;
+        case KVE_PERSIST: {
+          if (hv < 0 || rc < 0 || hv + rc < 1)
+            return fail(KVE_EINVAL, "layer %d head %d: PERSIST needs heavy, recent >= 0 and heavy + recent >= 1", l,
+                        h);
+          if (hv + rc > c->max_context)
+            return fail(KVE_EINVAL, "layer %d head %d: heavy + recent exceeds max_context", l, h);
+          if (!c->history) return fail(KVE_EINVAL, "PERSIST heads need the history table");
+          const int w = c->history[i];
+          if (w < 1 || w > 64)
+            return fail(KVE_EINVAL, "layer %d head %d: history window %d outside [1, 64]", l, h, w);
+          li.any_persist = true;
+          li.max_window = std::max(li.max_window, w);
+          break;
+        }
         case KVE_LOCAL:
           if (hv != 0 || rc < 1 || rc > c->max_context)
             return fail(KVE_EINVAL, "layer %d head %d: LOCAL needs heavy = 0 and 1 <= recent <= max_context", l, h);
@@ -163,6 +179,7 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
         const int p = c->policy[l * c->heads + h];
         if (p == KVE_H2O) li.h2o_units.push_back(b * c->heads + h);
         if (p == KVE_HASH) li.hash_units.push_back(b * c->heads + h);
+        if (p == KVE_PERSIST) li.persist_units.push_back(b * c->heads + h);
       }
   }
   const SplitPolicy sp = split_policy();
@@ -202,7 +219,7 @@ struct Layer {
   kve::LayerCache cache{};
   kve::SplitScratch split{};   // chunk == 0: fused path
   LayerInfo info;
-  kve::UnitList h2o{nullptr, 0}, hash{nullptr, 0};
+  kve::UnitList h2o{nullptr, 0}, hash{nullptr, 0}, persist{nullptr, 0};
   int position = -1;   // next decode position; -1 before prefill
 };
 
@@ -275,6 +292,7 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
     lc.cap = (int32_t)cap;
     int32_t* h2o_ids = li.h2o_units.empty() ? nullptr : pl.take<int32_t>(li.h2o_units.size());
     int32_t* hash_ids = li.hash_units.empty() ? nullptr : pl.take<int32_t>(li.hash_units.size());
+    int32_t* persist_ids = li.persist_units.empty() ? nullptr : pl.take<int32_t>(li.persist_units.size());
     if (ctx) {
       Layer& L = ctx->layers[l];
       L.cache = lc;
@@ -282,6 +300,7 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
       L.info = li;
       L.h2o = {h2o_ids, (int32_t)li.h2o_units.size()};
       L.hash = {hash_ids, (int32_t)li.hash_units.size()};
+      L.persist = {persist_ids, (int32_t)li.persist_units.size()};
     }
   }
   return pl.off;
@@ -339,6 +358,7 @@ kve_status kvevict_create(const kve_config* cfg, void* d_workspace, size_t bytes
   ctx->cfg.policy = ctx->cfg.heavy = ctx->cfg.recent = nullptr;
   ctx->cfg.keep_token_bitmap = nullptr;
   ctx->cfg.lsh_proj_bf16 = nullptr;
+  ctx->cfg.history = nullptr;
   const float scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / std::sqrt((float)cfg->head_dim);
   ctx->shape = {cfg->batch, cfg->heads, cfg->head_dim, cfg->dtype, scale};
   ctx->layers.resize(cfg->layers);
@@ -350,7 +370,8 @@ kve_status kvevict_create(const kve_config* cfg, void* d_workspace, size_t bytes
   std::vector<kve::HeadMeta> meta((size_t)cfg->layers * cfg->heads);
   for (size_t i = 0; i < meta.size(); ++i) {
     const int p = cfg->policy[i], hv = cfg->heavy[i], rc = cfg->recent[i];
-    meta[i] = {p, hv, rc, head_capacity(p, hv, rc, cfg->max_context)};
+    const int w = p == KVE_PERSIST ? cfg->history[i] : 0;
+    meta[i] = {p, hv, rc, head_capacity(p, hv, rc, cfg->max_context), w};
   }
   s = dev(hipMemcpy(ctx->meta, meta.data(), meta.size() * sizeof(kve::HeadMeta), hipMemcpyHostToDevice),
           "copy head table");
@@ -368,6 +389,9 @@ kve_status kvevict_create(const kve_config* cfg, void* d_workspace, size_t bytes
     if (s == KVE_OK && L.hash.n)
       s = dev(hipMemcpy((void*)L.hash.ids, L.info.hash_units.data(), L.hash.n * 4, hipMemcpyHostToDevice),
               "copy unit list");
+    if (s == KVE_OK && L.persist.n)
+      s = dev(hipMemcpy((void*)L.persist.ids, L.info.persist_units.data(), L.persist.n * 4,
+                        hipMemcpyHostToDevice), "copy unit list");
   }
   if (s != KVE_OK) {
     delete ctx;
@@ -395,21 +419,31 @@ kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t P, const void* q
   hipStream_t st = (hipStream_t)stream;
   const kve::Shape& sh = h->shape;
   hipError_t e = hipSuccess;
-  // Scores (H2O heads): row statistics, then column sums.  16-bit inputs use
-  // the matrix-core kernels, fp32 inputs the vector-ALU ones.  The optional
-  // prompt output covers every unit and writes the row statistics with it.
+  // Scores (H2O heads): row statistics, then column sums.  Pivotal histories
+  // (PERSIST heads): row statistics of the last `window` rows, then their
+  // bits.  16-bit inputs use the matrix-core kernels, fp32 inputs the
+  // vector-ALU ones.  The optional prompt output covers every unit and writes
+  // the row statistics with it.
   const kve::UnitList all{nullptr, sh.units()};
   const bool mfma = sh.dtype != KVE_F32;
   if (out) {
     e = mfma ? kve::launch_prefill_attend_mfma(sh, P, all, q, k, v, h->lse, out, st)
              : kve::launch_prefill_rowstats_valu(sh, P, all, q, k, v, h->lse, out, st);
-  } else if (L.h2o.n) {
-    e = mfma ? kve::launch_prefill_rowstats_mfma(sh, P, L.h2o, q, k, h->lse, st)
-             : kve::launch_prefill_rowstats_valu(sh, P, L.h2o, q, k, v, h->lse, nullptr, st);
+  } else {
+    if (L.h2o.n)
+      e = mfma ? kve::launch_prefill_rowstats_mfma(sh, P, L.h2o, q, k, h->lse, 0, st)
+               : kve::launch_prefill_rowstats_valu(sh, P, L.h2o, q, k, v, h->lse, nullptr, st);
+    if (e == hipSuccess && L.persist.n)
+      e = mfma ? kve::launch_prefill_rowstats_mfma(sh, P, L.persist, q, k, h->lse,
+                                                   std::max(0, P - L.info.max_window), st)
+               : kve::launch_prefill_rowstats_valu(sh, P, L.persist, q, k, v, h->lse, nullptr, st);
   }
   if (e == hipSuccess && L.h2o.n)
     e = mfma ? kve::launch_prefill_colsum_mfma(sh, P, L.h2o, q, k, h->lse, h->colsum, st)
              : kve::launch_prefill_colsum_valu(sh, P, L.h2o, q, k, h->lse, h->colsum, st);
+  if (e == hipSuccess && L.persist.n)
+    e = mfma ? kve::launch_prefill_persist_mfma(sh, P, L.persist, q, k, h->lse, L.cache.meta, h->colsum, st)
+             : kve::launch_prefill_persist_valu(sh, P, L.persist, q, k, h->lse, L.cache.meta, h->colsum, st);
   if (e == hipSuccess)
     e = kve::launch_prefill_select(sh, L.cache, P, h->colsum, k, v, token_ids, h->bitmap, h->cfg.vocab, st);
   if (e == hipSuccess && L.hash.n) {

@@ -9,21 +9,23 @@
 namespace kve {
 
 enum Dtype : int32_t { F32 = 0, F16 = 1, BF16 = 2 };
-enum Policy : int32_t { FULL = 0, H2O = 1, LOCAL = 2, SPECIAL = 3, HASH = 4 };
+enum Policy : int32_t { FULL = 0, H2O = 1, LOCAL = 2, SPECIAL = 3, HASH = 4, PERSIST = 5 };
 
 // Per-head policy record, device-resident, one per head of a layer.
 struct HeadMeta {
   int32_t policy;
-  int32_t heavy;   // H2O: heavy slots; HASH: budget
-  int32_t recent;  // H2O: recent window; LOCAL: window
+  int32_t heavy;   // H2O, PERSIST: heavy slots; HASH: budget
+  int32_t recent;  // H2O, PERSIST: recent window; LOCAL: window
   int32_t cap;     // slots this head may occupy (<= the layer's stride)
+  int32_t window;  // PERSIST: steps of pivotal history (1..64)
 };
 
 // One layer's cache, carved from the workspace.
 struct LayerCache {
   void* K;              // [U][cap][d] storage dtype
   void* V;              // [U][cap][d]
-  double* S;            // [U][cap] accumulated scores (H2O heads)
+  double* S;            // [U][cap] accumulated scores (H2O heads); the 64-bit
+                        // pivotal histories in the same bytes (PERSIST heads)
   int32_t* pos;         // [U][cap] position per slot, -1 = empty
   uint32_t* sk;         // [U][cap] key sketches (HASH heads), or null
   int32_t* count;       // [U] occupied slots
@@ -55,9 +57,10 @@ hipError_t launch_prefill_rowstats_valu(const Shape& sh, int P, UnitList units, 
 hipError_t launch_prefill_colsum_valu(const Shape& sh, int P, UnitList units, const void* q,
                                       const void* k, const float* lse, double* colsum,
                                       hipStream_t st);
-// The same two passes on the matrix cores (16-bit dtypes only).
+// The same two passes on the matrix cores (16-bit dtypes only).  rowstats
+// covers the 128-query blocks that hold rows >= q_from (0: every row).
 hipError_t launch_prefill_rowstats_mfma(const Shape& sh, int P, UnitList units, const void* q,
-                                        const void* k, float* lse, hipStream_t st);
+                                        const void* k, float* lse, int q_from, hipStream_t st);
 // Row statistics and the causal attention output out[u][i][:] (fp32) on the
 // matrix cores (16-bit dtypes only).
 hipError_t launch_prefill_attend_mfma(const Shape& sh, int P, UnitList units, const void* q,
@@ -66,6 +69,16 @@ hipError_t launch_prefill_attend_mfma(const Shape& sh, int P, UnitList units, co
 hipError_t launch_prefill_colsum_mfma(const Shape& sh, int P, UnitList units, const void* q,
                                       const void* k, const float* lse, double* colsum,
                                       hipStream_t st);
+// Pivotal histories of the prompt for the listed PERSIST units, into the
+// colsum array as 64-bit patterns: bit P - 1 - i of key j is set iff row i,
+// with max(j, P - window) <= i < P, gives key j a weight >= 1 / (i + 1).
+// Needs lse for those rows.  meta: the layer's head table (window per head).
+hipError_t launch_prefill_persist_mfma(const Shape& sh, int P, UnitList units, const void* q,
+                                       const void* k, const float* lse, const HeadMeta* meta,
+                                       double* bits, hipStream_t st);
+hipError_t launch_prefill_persist_valu(const Shape& sh, int P, UnitList units, const void* q,
+                                       const void* k, const float* lse, const HeadMeta* meta,
+                                       double* bits, hipStream_t st);
 // Chooses the kept prompt positions per the head's policy and fills the cache.
 hipError_t launch_prefill_select(const Shape& sh, const LayerCache& c, int P, const double* colsum,
                                  const void* k, const void* v, const int32_t* ids,

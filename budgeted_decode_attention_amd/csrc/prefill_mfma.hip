@@ -15,6 +15,10 @@
 //             weights exp2(s * scale * log2e - lse2) are summed per key in
 //             float32 within a tile and in float64 across tiles.  No atomics:
 //             each workgroup owns its columns.
+//   persist:  the colsum structure over only the last `window` queries,
+//             collecting for each key the bits "weight >= 1 / (i + 1)" of
+//             rows i (the persistence reading of the Scissorhands page) by
+//             one wave ballot per 16 x 16 block instead of summing weights.
 //   attend:   rowstats plus the causal attention output o_i = sum_j p_ij v_j
 //             (the optional prompt output), as O^T = V^T P^T on the matrix
 //             cores: the weights a lane forms for its query are already a B
@@ -360,13 +364,40 @@ __device__ inline void colsum_fold(const f32x4 (&acc)[2], int i0, int nb, int j0
     }
 }
 
-template <int DT, int D>
+// Bits of one 16 x 16 block: for this lane's key (mb, r) and the 16 queries
+// i0 + nb * 16 + 0..15, the history bits at ages P - 1 - query.  Every lane
+// takes part in the ballots.
+__device__ inline void persist_fold(const f32x4 (&acc)[2], int i0, int nb, int j0, int P, int wlo, int g,
+                                    int c16, const Scale2& c2, float lh, float ll, float th,
+                                    uint64_t (&bits)[2][4]) {
+  const int qi = i0 + nb * 16 + c16;
+  const int age15 = P - 1 - (i0 + nb * 16 + 15);   // age of the block's last query
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = acc[mb][r];
+      float x = fmaf(s, c2.hi, -lh);
+      x = fmaf(s, c2.lo, x) - ll;
+      const int kj = j0 + mb * 16 + g * 4 + r;
+      const bool piv = qi < P && qi >= kj && qi >= wlo && x >= th;
+      const uint64_t b = __ballot(piv);
+      // lanes 16 g .. 16 g + 15 voted for this key; bit c <-> query c of the block
+      const uint32_t q16 = (uint32_t)(b >> (16 * g)) & 0xFFFFu;
+      const uint64_t rev = (uint64_t)(__builtin_bitreverse32(q16) >> 16);   // bit 15 - c
+      if (age15 >= 64 || age15 <= -16) continue;
+      bits[mb][r] |= age15 >= 0 ? rev << age15 : rev >> (-age15);
+    }
+}
+
+template <int DT, int D, bool BITS>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(KVE_PREFILL_WAVES_PER_EU)))
 void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void* k, const float* lse,
-                        double* colsum) {
+                        double* colsum, const HeadMeta* meta) {
   constexpr int KS = D / 32;
   __shared__ __attribute__((aligned(16))) char Qs[2][Tile<D>::kBytes];
   __shared__ float Lh[2][kTile], Ll[2][kTile];  // lse in log2 units, float pair
+  __shared__ float Th[2][kTile];                // BITS: -log2(i + 1)
   const int u = ul.ids ? ul.ids[blockIdx.x] : blockIdx.x;
   const int kb = blockIdx.y;                    // key block 0 (the heaviest) first
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -398,15 +429,20 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
     hi = (float)L2;
     lo = (float)(L2 - (double)hi);
   };
-  const int i_first = kb * kBlk;
+  // BITS: only rows i >= wlo count, starting from the 64-aligned tile that holds the first
+  const int wlo = BITS ? P - meta[u % sh.heads].window : 0;
+  const int i_first = BITS ? max(kb * kBlk, wlo) & ~(kTile - 1) : kb * kBlk;
+  auto thr = [&](int i) { return (float)(-log2((double)(i + 1))); };
+  uint64_t bits[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
   TileRegs<D> nxt;
-  float nh = 0.f, nl = 0.f;
+  float nh = 0.f, nl = 0.f, nt = 0.f;
   load_tile<D>(nxt, qbase, i_first, P);
   store_tile<D>(nxt, Qs[0]);
   if (threadIdx.x < kTile) {
     lse2(i_first + threadIdx.x, nh, nl);
     Lh[0][threadIdx.x] = nh;
     Ll[0][threadIdx.x] = nl;
+    if (BITS) Th[0][threadIdx.x] = thr(i_first + threadIdx.x);
   }
   __syncthreads();
   for (int it = 0, i0 = i_first; i0 < P; ++it, i0 += kTile) {
@@ -414,7 +450,10 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
     const bool more = i0 + kTile < P;
     if (more) {
       load_tile<D>(nxt, qbase, i0 + kTile, P);
-      if (threadIdx.x < kTile) lse2(i0 + kTile + threadIdx.x, nh, nl);
+      if (threadIdx.x < kTile) {
+        lse2(i0 + kTile + threadIdx.x, nh, nl);
+        if (BITS) nt = thr(i0 + kTile + threadIdx.x);
+      }
     }
     if (i0 + kTile - 1 >= j0) {                 // some query of the tile follows a key of the wave
       const bool edge = i0 < j0 + 32 || i0 + kTile > P;
@@ -433,7 +472,8 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
           for (int mb = 0; mb < 2; ++mb) acc[mb] = Mfma<DT>::run(kf[mb][ks], b, acc[mb]);
         }
         const float lh = Lh[buf][nb * 16 + c16], ll = Ll[buf][nb * 16 + c16];
-        if (edge) colsum_fold<true>(acc, i0, nb, j0, P, g, c16, c2, lh, ll, part);
+        if (BITS) persist_fold(acc, i0, nb, j0, P, wlo, g, c16, c2, lh, ll, Th[buf][nb * 16 + c16], bits);
+        else if (edge) colsum_fold<true>(acc, i0, nb, j0, P, g, c16, c2, lh, ll, part);
         else colsum_fold<false>(acc, i0, nb, j0, P, g, c16, c2, lh, ll, part);
       }
 #pragma unroll
@@ -446,9 +486,21 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
       if (threadIdx.x < kTile) {
         Lh[buf ^ 1][threadIdx.x] = nh;
         Ll[buf ^ 1][threadIdx.x] = nl;
+        if (BITS) Th[buf ^ 1][threadIdx.x] = nt;
       }
     }
     __syncthreads();
+  }
+  if (BITS) {
+    // the 16 lanes that share a key hold the same bits
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kj = j0 + mb * 16 + g * 4 + r;
+        if (c16 == 0 && kj < P) reinterpret_cast<uint64_t*>(colsum)[(size_t)u * P + kj] = bits[mb][r];
+      }
+    return;
   }
   // sum over the 16 lanes (queries) that share each key
 #pragma unroll
@@ -650,31 +702,34 @@ hipError_t attend_t(const Shape& sh, int P, UnitList ul, const void* q, const vo
 }
 
 template <int DT, int D>
-hipError_t rowstats_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, float* lse,
+hipError_t rowstats_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, float* lse, int q_from,
                       hipStream_t st) {
-  dim3 grid(ul.n, (P + kBlk - 1) / kBlk);
+  // blockIdx.y = 0 is the last query block, so the first nqb - q_from / kBlk blocks cover rows >= q_from
+  dim3 grid(ul.n, (P + kBlk - 1) / kBlk - q_from / kBlk);
   hipLaunchKernelGGL((rowstats_mfma_kernel<DT, D>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse);
   return hipGetLastError();
 }
 
-template <int DT, int D>
+template <int DT, int D, bool BITS>
 hipError_t colsum_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, const float* lse,
-                    double* colsum, hipStream_t st) {
+                    double* colsum, const HeadMeta* meta, hipStream_t st) {
   dim3 grid(ul.n, (P + kBlk - 1) / kBlk);
-  hipLaunchKernelGGL((colsum_mfma_kernel<DT, D>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse, colsum);
+  hipLaunchKernelGGL((colsum_mfma_kernel<DT, D, BITS>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse, colsum,
+                     meta);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_rowstats_mfma(const Shape& sh, int P, UnitList ul, const void* q, const void* k,
-                                        float* lse, hipStream_t st) {
+                                        float* lse, int q_from, hipStream_t st) {
   if (ul.n <= 0) return hipSuccess;
+  if (q_from < 0 || q_from >= P) return hipErrorInvalidValue;
   switch (sh.dtype * 1000 + sh.d) {
-    case F16 * 1000 + 64: return rowstats_t<F16, 64>(sh, P, ul, q, k, lse, st);
-    case F16 * 1000 + 128: return rowstats_t<F16, 128>(sh, P, ul, q, k, lse, st);
-    case BF16 * 1000 + 64: return rowstats_t<BF16, 64>(sh, P, ul, q, k, lse, st);
-    case BF16 * 1000 + 128: return rowstats_t<BF16, 128>(sh, P, ul, q, k, lse, st);
+    case F16 * 1000 + 64: return rowstats_t<F16, 64>(sh, P, ul, q, k, lse, q_from, st);
+    case F16 * 1000 + 128: return rowstats_t<F16, 128>(sh, P, ul, q, k, lse, q_from, st);
+    case BF16 * 1000 + 64: return rowstats_t<BF16, 64>(sh, P, ul, q, k, lse, q_from, st);
+    case BF16 * 1000 + 128: return rowstats_t<BF16, 128>(sh, P, ul, q, k, lse, q_from, st);
   }
   return hipErrorInvalidValue;
 }
@@ -695,10 +750,23 @@ hipError_t launch_prefill_colsum_mfma(const Shape& sh, int P, UnitList ul, const
                                       const float* lse, double* colsum, hipStream_t st) {
   if (ul.n <= 0) return hipSuccess;
   switch (sh.dtype * 1000 + sh.d) {
-    case F16 * 1000 + 64: return colsum_t<F16, 64>(sh, P, ul, q, k, lse, colsum, st);
-    case F16 * 1000 + 128: return colsum_t<F16, 128>(sh, P, ul, q, k, lse, colsum, st);
-    case BF16 * 1000 + 64: return colsum_t<BF16, 64>(sh, P, ul, q, k, lse, colsum, st);
-    case BF16 * 1000 + 128: return colsum_t<BF16, 128>(sh, P, ul, q, k, lse, colsum, st);
+    case F16 * 1000 + 64: return colsum_t<F16, 64, false>(sh, P, ul, q, k, lse, colsum, nullptr, st);
+    case F16 * 1000 + 128: return colsum_t<F16, 128, false>(sh, P, ul, q, k, lse, colsum, nullptr, st);
+    case BF16 * 1000 + 64: return colsum_t<BF16, 64, false>(sh, P, ul, q, k, lse, colsum, nullptr, st);
+    case BF16 * 1000 + 128: return colsum_t<BF16, 128, false>(sh, P, ul, q, k, lse, colsum, nullptr, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_persist_mfma(const Shape& sh, int P, UnitList ul, const void* q, const void* k,
+                                       const float* lse, const HeadMeta* meta, double* bits, hipStream_t st) {
+  if (ul.n <= 0) return hipSuccess;
+  if (!meta) return hipErrorInvalidValue;
+  switch (sh.dtype * 1000 + sh.d) {
+    case F16 * 1000 + 64: return colsum_t<F16, 64, true>(sh, P, ul, q, k, lse, bits, meta, st);
+    case F16 * 1000 + 128: return colsum_t<F16, 128, true>(sh, P, ul, q, k, lse, bits, meta, st);
+    case BF16 * 1000 + 64: return colsum_t<BF16, 64, true>(sh, P, ul, q, k, lse, bits, meta, st);
+    case BF16 * 1000 + 128: return colsum_t<BF16, 128, true>(sh, P, ul, q, k, lse, bits, meta, st);
   }
   return hipErrorInvalidValue;
 }

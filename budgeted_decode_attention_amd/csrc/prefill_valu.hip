@@ -6,7 +6,10 @@
 //   colsum:   per key column j, c_j = sum_{i>=j} exp(s_ij - lse_i), the
 //             accumulated attention each prompt token received (H2O review
 //             page, proposed method: the per-step attention statistics that
-//             the greedy eviction ranks).
+//             the greedy eviction ranks);
+//   persist:  per key column j, the bits "exp(s_ij - lse_i) >= 1 / (i + 1)"
+//             of the last `window` rows, bit P - 1 - i (the persistence
+//             reading of the Scissorhands page).
 //
 // Both passes form every dot product in the same order (fmaf over d = 0..D-1
 // on exact input values), so both see bit-identical logits.  lse is stored as
@@ -180,6 +183,64 @@ __global__ __launch_bounds__(kNT) void colsum_valu_kernel(Shape sh, int P, UnitL
 }
 
 template <int DT, int D>
+__global__ __launch_bounds__(kNT) void persist_valu_kernel(Shape sh, int P, UnitList ul, const void* q,
+                                                            const void* k, const float* lse,
+                                                            const HeadMeta* meta, double* bits) {
+  constexpr int ES = elem_bytes<DT>();
+  __shared__ float Ks[kRB * (D + 1)];
+  __shared__ float Qs[kKT * (D + 1)];
+  __shared__ float Lh[kKT], Ll[kKT];
+  __shared__ unsigned long long part_s[kNT];
+  const int u = ul.ids ? ul.ids[blockIdx.y] : blockIdx.y;
+  const int col0 = blockIdx.x * kRB;
+  const size_t base = (size_t)u * P * D * ES;
+  const int tid = threadIdx.x;
+  const int wlo = P - meta[u % sh.heads].window;
+  stage_rows<DT, D>(Ks, (const char*)k + base, col0, kRB, P);
+  const int jc = tid % kRB;
+  const int grp = tid / kRB;
+  unsigned long long acc = 0;
+  for (int i0 = max(col0, wlo); i0 < P; i0 += kKT) {
+    __syncthreads();
+    stage_rows<DT, D>(Qs, (const char*)q + base, i0, kKT, P);
+    if (tid < kKT) {
+      const size_t li = ((size_t)u * P + min(i0 + tid, P - 1)) * 2;
+      Lh[tid] = lse[li];
+      Ll[tid] = lse[li + 1];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ii = 0; ii < kKT / 4; ++ii) {
+      const int i = grp * (kKT / 4) + ii;
+      const int qi = i0 + i;
+      float s = 0.f;
+      for (int e = 0; e < D; ++e) s = fmaf(Qs[i * (D + 1) + e], Ks[jc * (D + 1) + e], s);
+      s *= sh.scale;
+      if (qi < P && qi >= col0 + jc) {
+        // weight >= 1 / (i + 1)  <=>  s - lse >= -log(i + 1)
+        const double x = ((double)s - (double)Lh[i]) - (double)Ll[i];
+        if (x >= -log((double)(qi + 1))) acc |= 1ull << (P - 1 - qi);
+      }
+    }
+  }
+  part_s[tid] = acc;
+  __syncthreads();
+  if (tid < kRB && col0 + tid < P) {
+    unsigned long long b = 0;
+    for (int g = 0; g < kNT / kRB; ++g) b |= part_s[g * kRB + tid];
+    reinterpret_cast<unsigned long long*>(bits)[(size_t)u * P + col0 + tid] = b;
+  }
+}
+
+template <int DT, int D>
+hipError_t persist_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, const float* lse,
+                     const HeadMeta* meta, double* bits, hipStream_t st) {
+  dim3 grid((P + kRB - 1) / kRB, ul.n);
+  hipLaunchKernelGGL((persist_valu_kernel<DT, D>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse, meta, bits);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
 hipError_t rowstats_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, const void* v,
                       float* lse, float* out, hipStream_t st) {
   dim3 grid((P + kRB - 1) / kRB, ul.n);
@@ -219,6 +280,25 @@ hipError_t launch_prefill_colsum_valu(const Shape& sh, int P, UnitList ul, const
     case F16 * 1000 + 128: return colsum_t<F16, 128>(sh, P, ul, q, k, lse, colsum, st);
     case BF16 * 1000 + 64: return colsum_t<BF16, 64>(sh, P, ul, q, k, lse, colsum, st);
     case BF16 * 1000 + 128: return colsum_t<BF16, 128>(sh, P, ul, q, k, lse, colsum, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kve
+
+namespace kve {
+
+hipError_t launch_prefill_persist_valu(const Shape& sh, int P, UnitList ul, const void* q, const void* k,
+                                       const float* lse, const HeadMeta* meta, double* bits, hipStream_t st) {
+  if (ul.n <= 0) return hipSuccess;
+  if (!meta) return hipErrorInvalidValue;
+  switch (sh.dtype * 1000 + sh.d) {
+    case F32 * 1000 + 64: return persist_t<F32, 64>(sh, P, ul, q, k, lse, meta, bits, st);
+    case F32 * 1000 + 128: return persist_t<F32, 128>(sh, P, ul, q, k, lse, meta, bits, st);
+    case F16 * 1000 + 64: return persist_t<F16, 64>(sh, P, ul, q, k, lse, meta, bits, st);
+    case F16 * 1000 + 128: return persist_t<F16, 128>(sh, P, ul, q, k, lse, meta, bits, st);
+    case BF16 * 1000 + 64: return persist_t<BF16, 64>(sh, P, ul, q, k, lse, meta, bits, st);
+    case BF16 * 1000 + 128: return persist_t<BF16, 128>(sh, P, ul, q, k, lse, meta, bits, st);
   }
   return hipErrorInvalidValue;
 }

@@ -8,6 +8,9 @@
 //   LOCAL    [P - W, P), position j in slot j mod W (FastGen review page).
 //   FULL     [0, P).
 //   SPECIAL  positions whose token id is in the keep bitmap (FastGen page).
+//   PERSIST  as H2O with the rank key = the persistence count (set bits of
+//            the token's 64-bit pivotal history, Scissorhands persistence
+//            reading); the slot keeps the history bits themselves.
 //   HASH     skipped here (prompt replay kernel).
 //
 // The heavy threshold is found by a radix select over the float64 score bit
@@ -43,8 +46,11 @@ __device__ inline int block_flag_scan(bool flag, int* total, int* scratch) {
   return before + in_wave;
 }
 
-__device__ inline uint64_t score_key(const double* c, int j) {
-  return (uint64_t)__double_as_longlong(c[j]);
+// Rank key of prompt position j: the float64 score bits (H2O) or the number
+// of set history bits (PERSIST); larger keys rank higher either way.
+__device__ inline uint64_t score_key(const double* c, int j, bool count) {
+  const uint64_t b = (uint64_t)__double_as_longlong(c[j]);
+  return count ? (uint64_t)__popcll(b) : b;
 }
 
 template <int DT, int D>
@@ -69,8 +75,9 @@ __global__ __launch_bounds__(kNT) void select_kernel(Shape sh, LayerCache c, int
   const size_t slot0 = (size_t)u * c.cap;
   const double* cu = colsum ? colsum + (size_t)u * P : nullptr;
 
-  // ---- H2O heavy threshold
-  const bool h2o = m.policy == H2O;
+  // ---- heavy threshold (H2O and PERSIST heads)
+  const bool persist = m.policy == PERSIST;
+  const bool h2o = m.policy == H2O || persist;
   const int B = m.heavy + m.recent;
   const bool select_heavy = h2o && P > B && m.heavy > 0;
   const int nc = h2o ? P - m.recent : 0;    // candidate positions [0, nc)
@@ -85,7 +92,7 @@ __global__ __launch_bounds__(kNT) void select_kernel(Shape sh, LayerCache c, int
       const uint64_t prefix = sh_prefix;
       const uint64_t hmask = pass == 0 ? 0ull : (~0ull << (shift + 8));   // bytes already fixed
       for (int j = tid; j < nc; j += kNT) {
-        const uint64_t key = score_key(cu, j);
+        const uint64_t key = score_key(cu, j, persist);
         const bool match = (key & hmask) == (prefix & hmask);
         if (match) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(kNT) void select_kernel(Shape sh, LayerCache c, int
     int seen = 0;
     for (int base = nc - 1; base >= 0 && seen < want; base -= kNT) {
       const int j = base - tid;
-      const bool eq = j >= 0 && score_key(cu, j) == T;
+      const bool eq = j >= 0 && score_key(cu, j, persist) == T;
       int total;
       const int before = block_flag_scan(eq, &total, iscr);
       if (eq && seen + before + 1 == want) sh_cut = j;
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(kNT) void select_kernel(Shape sh, LayerCache c, int
         if (P <= B || j >= nc) {
           keep = true;
         } else if (select_heavy) {
-          const uint64_t key = score_key(cu, j);
+          const uint64_t key = score_key(cu, j, persist);
           keep = key > T || (key == T && j >= cut);
         }
       }

@@ -14,7 +14,7 @@
  *     cheap dynamic greedy rule on each decode step's attention statistics,
  *     balancing recency and relevance.
  *   - Scissorhands summary page (Abstract): the cache is held at a fixed budget
- *     and keeps the tokens that were pivotal.
+ *     and keeps the tokens that were pivotal (persistence of importance).
  *   - FastGen review page ("Model Tells You What to Discard"), Abstract and
  *     proposed-method list, Figure 2 caption: per-head policies -- full cache,
  *     local window, special (+ punctuation) tokens only, frequency (H2O scores)
@@ -80,8 +80,21 @@ typedef enum { KVE_F32 = 0, KVE_F16 = 1, KVE_BF16 = 2 } kve_dtype;
  *               Hamming distance from the query's sketch (oldest first on
  *               equal distance) is replaced by token t; the query then attends
  *               the cache with t in it.  The prompt is replayed through the
- *               same rule from the cache [0, B). */
-typedef enum { KVE_FULL = 0, KVE_H2O = 1, KVE_LOCAL = 2, KVE_SPECIAL = 3, KVE_HASH = 4 } kve_policy;
+ *               same rule from the cache [0, B).
+ *   KVE_PERSIST persistence of importance (Scissorhands page, Abstract; the
+ *               rule is a reading of its hypothesis): a token is pivotal at a
+ *               step if that step's query gives it a weight >= 1/|A|, |A| the
+ *               number of keys the query attends (prompt row i: i + 1; decode
+ *               step: kept tokens + 1).  Each kept token carries its pivotal
+ *               bits of the last `history` steps (1..64); its count is their
+ *               number.  Otherwise as KVE_H2O with the count in place of the
+ *               accumulated score: heavy + recent slots, the lowest count
+ *               outside the recent window is evicted (oldest first on equal
+ *               counts), and the prompt keeps [P - recent, P) plus the
+ *               `heavy` earlier tokens with the highest counts over the last
+ *               `history` prompt rows (the newer first on equal counts). */
+typedef enum { KVE_FULL = 0, KVE_H2O = 1, KVE_LOCAL = 2, KVE_SPECIAL = 3, KVE_HASH = 4,
+               KVE_PERSIST = 5 } kve_policy;
 
 typedef struct {
   int32_t layers;              /* >= 1; each layer has its own caches and position counter */
@@ -94,8 +107,8 @@ typedef struct {
   /* Host tables, [layers * heads], copied at create; row = layer, column = head.
    * The policy of a head is shared by every sequence of the batch. */
   const int32_t* policy;       /* kve_policy */
-  const int32_t* heavy;        /* H2O: heavy slots >= 0; HASH: budget B >= 1; others: 0 */
-  const int32_t* recent;       /* H2O: recent window >= 0 with heavy + recent >= 1;
+  const int32_t* heavy;        /* H2O, PERSIST: heavy slots >= 0; HASH: budget B >= 1; others: 0 */
+  const int32_t* recent;       /* H2O, PERSIST: recent window >= 0 with heavy + recent >= 1;
                                   LOCAL: window W >= 1; others: 0 */
   /* SPECIAL heads only (else may be NULL/0): host bitmap of kept token ids,
    * bit (id & 31) of word id >> 5; ids outside [0, vocab) are not kept. */
@@ -107,6 +120,9 @@ typedef struct {
    * set iff the exact value of sum_i W[i][b] x[i] is > 0. */
   int32_t sketch_bits;                 /* 32 */
   const uint16_t* lsh_proj_bf16;       /* [layers][head_dim][sketch_bits] */
+  /* PERSIST heads only (else may be NULL): host [layers * heads] history
+   * window in steps, 1..64; entries of other heads are ignored. */
+  const int32_t* history;
 } kve_config;
 
 /* Bytes of device workspace the configuration needs (including 256-byte
@@ -131,7 +147,8 @@ kve_status kvevict_destroy(kve_handle h);
  * H2O heads score every prompt token by the column sums of the causal softmax
  * (the weight each later prompt query gives it, its own row included) and keep
  * the recent window plus the best-scoring earlier tokens (H2O page, proposed
- * method).  HASH heads replay the prompt (HashEvict page).  Positional
+ * method).  PERSIST heads count the pivotal prompt rows among the last
+ * `history` ones instead.  HASH heads replay the prompt (HashEvict page).  Positional
  * policies keep what their rule names (FastGen page). */
 kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t prompt_len,
                            const void* q, const void* k, const void* v,
@@ -153,8 +170,9 @@ kve_status kvevict_decode_step(kve_handle h, int32_t layer,
  * pos_out: [batch][heads][capacity] int32 position held by each slot, -1 for
  * an empty slot.  count_out: [batch][heads] int32 number of occupied slots.
  * scores_out: [batch][heads][capacity] float64 accumulated score per slot
- * (H2O heads; other heads export 0), or NULL.  `capacity` is
- * kvevict_capacity(h, layer). */
+ * (H2O heads; PERSIST heads store the 64-bit pivotal history in the same 8
+ * bytes, bit k = pivotal k steps before the latest one; other heads export
+ * 0), or NULL.  `capacity` is kvevict_capacity(h, layer). */
 kve_status kvevict_kept_indices(kve_handle h, int32_t layer, int32_t* pos_out,
                                 int32_t* count_out, double* scores_out, void* stream);
 

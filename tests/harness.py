@@ -12,12 +12,12 @@ import torch
 from budgeted_decode_attention_amd import KVCache
 from oracle import lockstep
 from workloads import configs
-from workloads.configs import FULL, H2O, HASH, LOCAL, SPECIAL, Workload
+from workloads.configs import FULL, H2O, HASH, LOCAL, PERSIST, SPECIAL, Workload
 from workloads.generate import LayerInputs, generate_layer, unit_ids, unit_sequence
 
 
 def make_cache(w: Workload, inp: LayerInputs, policy=None, heavy=None, recent=None, max_context=None,
-               layers: int = 1) -> KVCache:
+               layers: int = 1, history=None) -> KVCache:
     pol, hv, rc = w.policy_table(0)
     pol = pol if policy is None else policy
     hv = hv if heavy is None else heavy
@@ -29,6 +29,9 @@ def make_cache(w: Workload, inp: LayerInputs, policy=None, heavy=None, recent=No
         kw.update(keep_ids=w.keep_ids(), vocab=w.vocab)
     if HASH in list(pol):
         kw.update(proj=inp.proj)
+    if PERSIST in list(pol):
+        hw = [w.history_window if p == PERSIST else 0 for p in pol] if history is None else history
+        kw.update(history=np.tile(np.array(hw, dtype=np.int32), layers))
     return KVCache(layers, w.batch, w.heads, w.head_dim, max_context or w.context,
                    inp.prompt_q.dtype, tables[0], tables[1], tables[2], **kw)
 
@@ -80,7 +83,7 @@ def gpu_unit(r: GpuRun, b: int, h: int) -> lockstep.GpuUnit:
 
 
 def check_unit(w: Workload, inp_cpu: LayerInputs, r: GpuRun, b: int, h: int, policy=None, heavy=None,
-               recent=None, scale=None) -> lockstep.UnitReport:
+               recent=None, scale=None, history=None) -> lockstep.UnitReport:
     pol, hv, rc = w.policy_table(0)
     p = pol[h] if policy is None else policy[h]
     hh = hv[h] if heavy is None else heavy[h]
@@ -95,6 +98,9 @@ def check_unit(w: Workload, inp_cpu: LayerInputs, r: GpuRun, b: int, h: int, pol
     elif p == HASH:
         Wp = inp_cpu.proj.float().double().cpu().numpy()
         rep = lockstep.check_hash(Q, K, V, Wp, P, hh, sc, g, steps=T)
+    elif p == PERSIST:
+        win = w.history_window if history is None else history[h]
+        rep = lockstep.check_persist(Q, K, V, P, hh, rr, win, sc, g, steps=T)
     else:
         rep = lockstep.check_fastgen(p, Q, K, V, P, sc, g, heavy=hh, recent=rr,
                                      ids=unit_ids(inp_cpu, b), keep_ids=w.keep_ids(), steps=T)
@@ -111,7 +117,8 @@ def check_all(w: Workload, inp_cpu: LayerInputs, r: GpuRun, units: Optional[Iter
     return total
 
 
-def check_invariants(w: Workload, r: GpuRun, P: int, policy=None, heavy=None, recent=None) -> List[str]:
+def check_invariants(w: Workload, r: GpuRun, P: int, policy=None, heavy=None, recent=None,
+                     history=None) -> List[str]:
     """Properties that hold at any size: budgets, recent windows, unique in-range positions."""
     pol, hv, rc = w.policy_table(0)
     pol = pol if policy is None else policy
@@ -137,6 +144,16 @@ def check_invariants(w: Workload, r: GpuRun, P: int, policy=None, heavy=None, re
                     bad.append(f"b={b} h={h}: recent window not kept")
                 if not (r.final_S[b, h, :n] > 0).all():
                     bad.append(f"b={b} h={h}: non-positive score")
+            elif p == PERSIST:
+                win = w.history_window if history is None else history[h]
+                if n > hv[h] + rc[h]:
+                    bad.append(f"b={b} h={h}: over budget")
+                win_r = set(range(max(0, t_last - rc[h] + 1), t_last + 1))
+                if not win_r <= set(pos.tolist()):
+                    bad.append(f"b={b} h={h}: recent window not kept")
+                bits = np.ascontiguousarray(r.final_S[b, h, :n]).view(np.uint64)
+                if win < 64 and (bits >> np.uint64(win)).any():
+                    bad.append(f"b={b} h={h}: history bits beyond the window")
             elif p == LOCAL:
                 if sorted(pos.tolist()) != list(range(max(0, t_last - rc[h] + 1), t_last + 1)):
                     bad.append(f"b={b} h={h}: local window wrong")

@@ -102,3 +102,21 @@ def test_calls_on_a_null_handle_fail_cleanly():
     assert lib.kvevict_capacity(None, 0) == -1 and lib.kvevict_position(None, 0) == -1
     for s in range(6):
         assert lib.kvevict_status_string(s)
+
+
+@pytest.mark.parametrize("history,status", [
+    (None, binding.KVE_EINVAL),                 # PERSIST heads need the table
+    ([0, 0, 0], binding.KVE_EINVAL),            # window < 1
+    ([65, 1, 1], binding.KVE_EINVAL),           # window > 64
+    ([64, 0, 0], binding.KVE_OK),               # other heads' entries are ignored
+    ([1, 7, 9], binding.KVE_OK),
+])
+def test_persist_needs_a_history_window(history, status):
+    c, keep = cfg(policy=[5, 1, 1], history=history)
+    assert status_of(c)[0] == status
+
+
+def test_persist_capacity_is_heavy_plus_recent():
+    a, ka = cfg(policy=[5, 5, 5], history=[8, 8, 8])
+    b, kb = cfg()
+    assert status_of(a) == status_of(b)   # same slots and workspace as the H2O table

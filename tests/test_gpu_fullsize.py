@@ -59,6 +59,11 @@ def test_opt30b_layer_full_size():
     run_full("opt30b_decode_h2o", 8)
 
 
+def test_opt30b_persist_layer_full_size():
+    rep = run_full("opt30b_decode_persist", 6)
+    assert rep.decisions == 6 * 256
+
+
 def test_llama65b_fastgen_full_size():
     run_full("llama65b_fastgen", 8, heads_of=[FULL, H2O, LOCAL, SPECIAL])
 

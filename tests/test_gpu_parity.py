@@ -14,7 +14,7 @@ import torch
 
 from tests import harness
 from workloads import configs
-from workloads.configs import FULL, H2O, HASH, LOCAL, SPECIAL
+from workloads.configs import FULL, H2O, HASH, LOCAL, PERSIST, SPECIAL
 from workloads.generate import generate_layer
 
 pytestmark = pytest.mark.gpu
@@ -30,19 +30,20 @@ def decode_path(request, monkeypatch):
     return request.param
 
 
-def run_and_check(w, policy=None, heavy=None, recent=None, prompt_out=False, seed=0, units=None):
+def run_and_check(w, policy=None, heavy=None, recent=None, prompt_out=False, seed=0, units=None,
+                  history=None):
     import os
     print(f"\n[parity] split_above={os.environ.get('KVEVICT_SPLIT_ABOVE', '-')} {w.name} B={w.batch} H={w.heads} d={w.head_dim} {w.dtype} P={w.prompt} "
           f"T={w.steps} seed={seed}", flush=True)
     inp = generate_layer(w, 0, "cpu", seed)
-    kv = harness.make_cache(w, inp, policy, heavy, recent)
+    kv = harness.make_cache(w, inp, policy, heavy, recent, history=history)
     r = harness.run_layer(kv, inp.to("cuda"), want_prompt_out=prompt_out)
-    rep = harness.check_all(w, inp, r, units, policy=policy, heavy=heavy, recent=recent)
+    rep = harness.check_all(w, inp, r, units, policy=policy, heavy=heavy, recent=recent, history=history)
     print(f"[parity] decisions={rep.decisions} adopted={rep.adopted} max_out={rep.max_out_rel:.2e} "
           f"max_prompt_out={rep.max_prompt_out_rel:.2e} max_S={rep.max_score_rel:.2e} "
           f"min_gap={rep.min_gap:.2e}", flush=True)
     assert rep.ok, rep.failures[:10]
-    bad = harness.check_invariants(w, r, inp.prompt_q.shape[2], policy, heavy, recent)
+    bad = harness.check_invariants(w, r, inp.prompt_q.shape[2], policy, heavy, recent, history)
     assert not bad, bad[:10]
     kv.close()
     return rep, r
@@ -144,3 +145,60 @@ def test_deterministic_across_runs(decode_path):
     a, b = runs
     for f in ("out", "evicted", "final_pos", "final_S", "prefill_S"):
         assert np.array_equal(getattr(a, f), getattr(b, f)), f
+
+
+# ---- persistence counts (Scissorhands reading)
+
+def test_persist_bf16_scaled(decode_path):
+    w = configs.scaled("opt30b_decode_persist", batch=2, heads=3, prompt=700, steps=80)
+    assert (w.heavy, w.recent, w.history_window) == (70, 70, 64)
+    rep, _ = run_and_check(w)
+    assert rep.decisions == 6 * 80
+
+
+def test_persist_fp16_d64_and_mixed_windows(decode_path):
+    """d = 64 fp16, windows 1, 17, 64 and one H2O head in the same layer."""
+    w = dataclasses.replace(configs.scaled("opt30b_decode_persist", batch=2, heads=4, prompt=300, steps=60),
+                            dtype="f16", head_dim=64)
+    run_and_check(w, policy=[PERSIST, PERSIST, H2O, PERSIST], heavy=[30, 20, 30, 10], recent=[30, 5, 30, 40],
+                  history=[1, 17, 0, 64])
+
+
+def test_persist_fp32(decode_path):
+    w = dataclasses.replace(configs.scaled("opt30b_decode_persist", batch=1, heads=3, prompt=150, steps=40),
+                            dtype="f32")
+    run_and_check(w, prompt_out=True, history=[64, 9, 33])
+
+
+@pytest.mark.parametrize("P,T,hh,rc,win", [(1, 30, 4, 4, 64), (5, 40, 8, 8, 3), (90, 30, 12, 0, 64),
+                                           (90, 30, 0, 12, 10), (64, 64, 16, 16, 64), (257, 20, 100, 27, 40),
+                                           (130, 40, 20, 20, 64)])
+def test_persist_edge_shapes(P, T, hh, rc, win, decode_path):
+    """One-token prompt, prompt shorter than the budget, no recent window (the
+    new token may leave at once), no heavy part, tile-aligned and ragged
+    prompts, a window reaching across a 128-query block boundary."""
+    w = configs.scaled("opt30b_decode_persist", batch=1, heads=2, prompt=P, steps=T)
+    run_and_check(w, policy=[PERSIST] * 2, heavy=[hh] * 2, recent=[rc] * 2, history=[win] * 2)
+
+
+def test_persist_identical_keys_is_a_sliding_window(decode_path):
+    """Every key equal: every decode weight is exactly 1 / |A| (pivotal at
+    every step), so once the cache is full the oldest candidate leaves at each
+    step.  The prompt fits the budget and the 4-step window has forgotten the
+    prompt rows (whose weights are uniform only up to rounding) before the
+    first eviction."""
+    P, T, hh, rc, win = 60, 60, 8, 70, 4
+    B = hh + rc
+    w = configs.scaled("opt30b_decode_persist", batch=1, heads=2, prompt=P, steps=T)
+    inp = generate_layer(w, 0, "cpu", 0)
+    inp.prompt_k[:] = inp.prompt_k[:, :, :1]
+    inp.dec_k[:] = inp.prompt_k[:, :, 0].unsqueeze(0)
+    kv = harness.make_cache(w, inp, policy=[PERSIST] * 2, heavy=[hh] * 2, recent=[rc] * 2, history=[win] * 2)
+    r = harness.run_layer(kv, inp.to("cuda"))
+    kv.close()
+    for h in range(2):
+        assert sorted(r.prefill_pos[0, h, :P].tolist()) == list(range(P))
+        assert r.evicted[:, 0, h].tolist() == [P + s - B if P + s >= B else -1 for s in range(T)]
+        assert sorted(r.final_pos[0, h, :B].tolist()) == list(range(P + T - B, P + T))
+        bits = np.ascontiguousarray(r.final_S[0, h, :B]).view(np.uint64)
+        assert (bits == np.uint64(15)).sum() == B - 3    # all but the three newest hold 4 set bits
