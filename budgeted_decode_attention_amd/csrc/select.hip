@@ -85,12 +85,13 @@ __global__ __launch_bounds__(kNT) void select_kernel(Shape sh, LayerCache c, int
   int cut = 0;                              // ties with key == T kept iff position >= cut
   if (select_heavy) {
     if (tid == 0) { sh_prefix = 0; sh_want = m.heavy; }
-    for (int pass = 0; pass < 8; ++pass) {
+    // persistence counts are at most 64: only the lowest byte can differ
+    for (int pass = persist ? 7 : 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
       hist[tid] = 0;
       __syncthreads();
       const uint64_t prefix = sh_prefix;
-      const uint64_t hmask = pass == 0 ? 0ull : (~0ull << (shift + 8));   // bytes already fixed
+      const uint64_t hmask = pass == 0 ? 0ull : (~0ull << (shift + 8));   // bytes already fixed (zero when skipped)
       for (int j = tid; j < nc; j += kNT) {
         const uint64_t key = score_key(cu, j, persist);
         const bool match = (key & hmask) == (prefix & hmask);
