@@ -13,7 +13,9 @@
 //   colsum:   workgroup = (unit, 128 keys); waves hold 32 keys each as A
 //             fragments; 64-query tiles of Q (and their lse) are staged in LDS;
 //             weights exp2(s * scale * log2e - lse2) are summed per key in
-//             float32 within a tile and in float64 across tiles.  No atomics:
+//             float32 within a tile and in float64 across tiles; after a
+//             wave's first tile the row pass keeps its running offset unless
+//             a weight could overflow.  No atomics:
 //             each workgroup owns its columns.
 //   persist:  the colsum structure over only the last `window` queries,
 //             collecting for each key the bits "weight >= 1 / (i + 1)" of
@@ -268,6 +270,34 @@ __device__ inline void rowstats_fold(const f32x4 (&acc)[4][2], int k0, int q0, i
   }
 }
 
+// Interior tile after a wave's first: weights against the running offset mc,
+// with no new maximum (one vector operation less per pair).  The offset only
+// has to keep every weight finite; if any lane's tile sum reaches 2^100 the
+// wave keeps its state unchanged and returns false, and the caller folds the
+// tile with rowstats_fold, which raises the offset.
+__device__ inline bool rowstats_fold_lazy(const f32x4 (&acc)[4][2], const Scale2& c2, const float (&mc)[2],
+                                          double (&l)[2]) {
+  float sums[2];
+  bool big = false;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    float sum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float s = acc[mb][nb][r];
+        sum += exp2_fast(fmaf(s, c2.lo, fmaf(s, c2.hi, -mc[nb])));
+      }
+    sums[nb] = sum;
+    big |= !(sum < 0x1p100f);                  // also catches inf / NaN
+  }
+  if (__ballot(big) != 0) return false;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) l[nb] += (double)sums[nb];
+  return true;
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(KVE_PREFILL_WAVES_PER_EU)))
 void rowstats_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void* k, float* lse) {
@@ -320,7 +350,7 @@ void rowstats_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const voi
         }
       }
       if (k0 + kTile > q0 || k0 + kTile > P) rowstats_fold<true>(acc, k0, q0, P, g, c16, c2, mc, l);
-      else rowstats_fold<false>(acc, k0, q0, P, g, c16, c2, mc, l);
+      else if (k0 == 0 || !rowstats_fold_lazy(acc, c2, mc, l)) rowstats_fold<false>(acc, k0, q0, P, g, c16, c2, mc, l);
     }
     if (more) store_tile<D>(nxt, Ks[(it + 1) & 1]);   // that buffer was last read before the previous barrier
     __syncthreads();
@@ -343,23 +373,23 @@ void rowstats_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const voi
 // ------------------------------------------------------------------ colsum
 // Adds one 64-query tile's weights exp2(s * c2 - lse2) into part (this lane's
 // keys).  EDGE: some query precedes a key of the wave or lies past P.
+// The low word of lse2 enters as the factor fl = 2^-ll on the weight, taken
+// by the accumulating fused multiply-add.
 template <bool EDGE>
 __device__ inline void colsum_fold(const f32x4 (&acc)[2], int i0, int nb, int j0, int P, int g, int c16,
-                                   const Scale2& c2, float lh, float ll, float (&part)[2][4]) {
+                                   const Scale2& c2, float lh, float fl, float (&part)[2][4]) {
   const int qi = i0 + nb * 16 + c16;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float s = acc[mb][r];
-      float x = fmaf(s, c2.hi, -lh);
-      x = fmaf(s, c2.lo, x) - ll;
-      const float p = exp2_fast(x);
+      const float p = exp2_fast(fmaf(s, c2.lo, fmaf(s, c2.hi, -lh)));
       if (EDGE) {
         const int kj = j0 + mb * 16 + g * 4 + r;
-        part[mb][r] += (qi < P && qi >= kj) ? p : 0.f;
+        part[mb][r] = (qi < P && qi >= kj) ? fmaf(p, fl, part[mb][r]) : part[mb][r];
       } else {
-        part[mb][r] += p;
+        part[mb][r] = fmaf(p, fl, part[mb][r]);
       }
     }
 }
@@ -397,6 +427,7 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
   constexpr int KS = D / 32;
   __shared__ __attribute__((aligned(16))) char Qs[2][Tile<D>::kBytes];
   __shared__ float Lh[2][kTile], Ll[2][kTile];  // lse in log2 units, float pair
+  __shared__ float Lf[2][kTile];                // 2^-Ll
   __shared__ float Th[2][kTile];                // BITS: -log2(i + 1)
   const int u = ul.ids ? ul.ids[blockIdx.x] : blockIdx.x;
   const int kb = blockIdx.y;                    // key block 0 (the heaviest) first
@@ -442,6 +473,7 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
     lse2(i_first + threadIdx.x, nh, nl);
     Lh[0][threadIdx.x] = nh;
     Ll[0][threadIdx.x] = nl;
+    Lf[0][threadIdx.x] = exp2f(-nl);
     if (BITS) Th[0][threadIdx.x] = thr(i_first + threadIdx.x);
   }
   __syncthreads();
@@ -471,10 +503,10 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) acc[mb] = Mfma<DT>::run(kf[mb][ks], b, acc[mb]);
         }
-        const float lh = Lh[buf][nb * 16 + c16], ll = Ll[buf][nb * 16 + c16];
-        if (BITS) persist_fold(acc, i0, nb, j0, P, wlo, g, c16, c2, lh, ll, Th[buf][nb * 16 + c16], bits);
-        else if (edge) colsum_fold<true>(acc, i0, nb, j0, P, g, c16, c2, lh, ll, part);
-        else colsum_fold<false>(acc, i0, nb, j0, P, g, c16, c2, lh, ll, part);
+        const float lh = Lh[buf][nb * 16 + c16];
+        if (BITS) persist_fold(acc, i0, nb, j0, P, wlo, g, c16, c2, lh, Ll[buf][nb * 16 + c16], Th[buf][nb * 16 + c16], bits);
+        else if (edge) colsum_fold<true>(acc, i0, nb, j0, P, g, c16, c2, lh, Lf[buf][nb * 16 + c16], part);
+        else colsum_fold<false>(acc, i0, nb, j0, P, g, c16, c2, lh, Lf[buf][nb * 16 + c16], part);
       }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -486,6 +518,7 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
       if (threadIdx.x < kTile) {
         Lh[buf ^ 1][threadIdx.x] = nh;
         Ll[buf ^ 1][threadIdx.x] = nl;
+        Lf[buf ^ 1][threadIdx.x] = exp2f(-nl);
         if (BITS) Th[buf ^ 1][threadIdx.x] = nt;
       }
     }

@@ -202,3 +202,20 @@ def test_persist_identical_keys_is_a_sliding_window(decode_path):
         assert sorted(r.final_pos[0, h, :B].tolist()) == list(range(P + T - B, P + T))
         bits = np.ascontiguousarray(r.final_S[0, h, :B]).view(np.uint64)
         assert (bits == np.uint64(15)).sum() == B - 3    # all but the three newest hold 4 set bits
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_logit_jump_after_first_tile(dtype):
+    """A key far past the first 64-key tile whose logit with every later
+    query exceeds everything before it by ~200 (log2 units): the row pass must
+    leave its running offset and refold that tile at the new maximum."""
+    w = dataclasses.replace(configs.scaled("opt30b_decode_h2o", batch=1, heads=2, prompt=300, steps=20),
+                            dtype=dtype)
+    inp = generate_layer(w, 0, "cpu", 5)
+    u = torch.zeros(w.head_dim)
+    u[3] = 1.0
+    amp = 40.0 if dtype == "bf16" else 30.0          # |s| / sqrt(d) * log2(e): 204 (bf16), 115 (f16)
+    inp.prompt_k[0, :, 150] = (amp * u).to(inp.prompt_k.dtype)
+    inp.prompt_q[0, :, 151:] += (amp * u).to(inp.prompt_q.dtype)
+    rep, _ = run_and_check(w)
+    assert rep.ok
