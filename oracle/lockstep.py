@@ -29,6 +29,12 @@ clear and set, and accepts a GPU choice that some setting of them explains.
 The GPU's exported histories must equal the oracle's on every unambiguous
 bit; at the prompt the oracle then takes the GPU's ambiguous bits, so the
 replay continues from the GPU's state.
+
+Profiled (adaptive) units: the GPU's composite choice is accepted if every
+composite it passed over recovers less than threshold + 1e-5 and the chosen
+one at least threshold - 1e-5 (recoveries are sums of float32 weights); the
+replay then follows the GPU's choice with the H2O tie band for the frequent
+part, protected tokens exact.
 """
 
 from __future__ import annotations
@@ -38,7 +44,7 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-from . import fastgen, h2o, hashevict, persistence
+from . import adaptive, fastgen, h2o, hashevict, persistence
 from .attention import attend, causal_attention
 
 TIE_BAND = 1e-6
@@ -367,4 +373,87 @@ def check_persist(Q, K, V, P: int, heavy: int, recent: int, window: int, scale: 
         rep.failures.append("final kept set differs")
     if gpu.final_S is not None:
         _check_history_bits(rep, "final", gpu.final_pos, _as_bits(gpu.final_S), cache.pos, cache.hist, cache.amb)
+    return rep
+
+
+RECOVERY_BAND = 1e-5
+
+
+def check_adaptive(Q, K, V, ids, P: int, special, punct, heavy: int, recent: int, scale: float, rows: int,
+                   threshold: float, gpu: GpuUnit, gpu_choice: int, steps: Optional[int] = None) -> UnitReport:
+    """FastGen profiling + the chosen composite, in lockstep."""
+    rep = UnitReport()
+    T = len(gpu.evicted) if steps is None else steps
+    comps = adaptive.composites(special, punct, heavy, recent)
+    k_ref, rec = adaptive.profile(Q[:P], K[:P], ids, comps, scale, rows, threshold)
+    g = int(gpu_choice)
+    if g != k_ref:
+        passed = [j for j in (1, 2, 3, 4) if j < g]
+        ok = g in comps and all(rec.get(j, 0.0) < threshold + RECOVERY_BAND for j in passed)
+        ok = ok and (g == adaptive.C_FULL or rec.get(g, 0.0) >= threshold - RECOVERY_BAND)
+        if ok:
+            rep.adopted += 1
+        else:
+            rep.failures.append(f"profile: GPU chose C{g}, oracle C{k_ref} (recoveries {rec})")
+            if g not in comps:
+                return rep
+    comp = comps[g]
+    c = h2o.prefill_column_scores(Q[:P], K[:P], scale)
+    ref = adaptive.prompt_kept(comp, c, ids, P)
+    gpos = np.sort(np.asarray(gpu.prefill_pos, dtype=np.int64))
+    if not np.array_equal(gpos, ref):
+        prot = {j for j in range(P) if int(ids[j]) in comp.protected}
+        free = [j for j in range(P) if j not in prot]
+        window = {j for j in free if j >= P - comp.recent}
+        older = [j for j in free if j < P - comp.recent]
+        quota = comp.heavy + comp.recent - len(window)
+        got = set(gpos.tolist())
+        ok = not comp.full and len(free) > comp.heavy + comp.recent and (prot | window) <= got
+        heavy_got = [j for j in got if j in set(older)]
+        ok = ok and len(heavy_got) == quota and len(got) == len(prot) + len(window) + quota
+        if ok and quota > 0:
+            ranked = np.sort(c[older])[::-1]
+            thr = ranked[quota - 1]
+            ok = all(j in got for j in older if c[j] > thr * (1 + TIE_BAND))
+            ok = ok and not any(j in got for j in older if c[j] < thr * (1 - TIE_BAND))
+        if ok:
+            rep.adopted += 1
+        else:
+            rep.failures.append("prefill: kept set outside the near-tie band")
+    kept = gpos
+    S = c[kept].copy()
+    _check_prompt_out(rep, gpu, Q, K, V, P, scale)
+    for s_ in range(T):
+        t = P + s_
+        A = np.append(kept, t).astype(np.int64)
+        p, o = attend(Q[t], K[A], V[A], scale)
+        _check_out(rep, s_, gpu.out[s_], o)
+        S_A = np.append(S, 0.0) + p
+        gv = int(gpu.evicted[s_])
+        free = np.array([int(ids[j]) not in comp.protected for j in A])
+        if comp.full or int(ids[t]) in comp.protected or free.sum() <= comp.heavy + comp.recent:
+            if gv != -1:
+                rep.failures.append(f"step {s_}: evicted {gv}, none expected")
+            kept, S = A, S_A
+            continue
+        rep.decisions += 1
+        cand = np.array([i for i in range(len(A)) if free[i] and A[i] <= t - comp.recent], dtype=np.int64)
+        i_ref = int(min(cand, key=lambda i: (S_A[i], A[i])))
+        where = np.flatnonzero(A == gv)
+        if gv != int(A[i_ref]):
+            if accept_h2o_victim(A, S_A, cand, i_ref, gv):
+                rep.adopted += 1
+            else:
+                rep.failures.append(f"step {s_}: GPU evicted {gv}, oracle {int(A[i_ref])}")
+        v = int(where[0]) if len(where) == 1 else i_ref
+        keep = np.ones(len(A), dtype=bool)
+        keep[v] = False
+        kept, S = A[keep], S_A[keep]
+    if not np.array_equal(np.sort(np.asarray(gpu.final_pos, dtype=np.int64)), np.sort(kept)):
+        rep.failures.append("final kept set differs")
+    if gpu.final_S is not None and not comp.full:
+        gmap = {int(p_): float(v_) for p_, v_ in zip(gpu.final_pos, gpu.final_S)}
+        ref_S = {int(j): float(v_) for j, v_ in zip(kept, S)}
+        free_pos = [int(j) for j in kept if int(ids[j]) not in comp.protected and int(j) in gmap]
+        _check_scores(rep, "final", free_pos, [gmap[j] for j in free_pos], free_pos, [ref_S[j] for j in free_pos])
     return rep

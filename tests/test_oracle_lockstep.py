@@ -184,3 +184,54 @@ def test_persist_checker_accepts_ambiguous_choice():
     rep = lockstep.check_persist(Q, K, V, P, hh, r, w, 0.5, g, steps=1)
     assert rep.adopted == 1
     assert not any("GPU evicted" in f for f in rep.failures), rep.failures
+
+
+def adaptive_case(seed=2, P=40, T=30, d=8):
+    from oracle import adaptive
+    rng = np.random.default_rng(seed)
+    N = P + T
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    ids = rng.integers(0, 8, N)
+    return Q, K, V, ids
+
+
+def adaptive_gpu_unit(tr):
+    import numpy as np
+    fin = np.array(tr.final_kept)
+    S = np.where(tr.protected_final, np.inf, tr.final_scores)
+    return lockstep.GpuUnit(prefill_pos=tr.prefill_kept.copy(), evicted=tr.evicted.copy(), out=tr.out.copy(),
+                            final_pos=fin, final_S=S)
+
+
+def test_adaptive_checker_accepts_oracle_and_rejects_mistakes():
+    from oracle import adaptive
+    Q, K, V, ids = adaptive_case()
+    P, hh, rc, R = 40, 4, 6, 16
+    for T_ in (0.0, 0.5, 0.9, 2.0):                         # several choices
+        tr = adaptive.run_unit(Q, K, V, ids, P, [0], [1, 2], hh, rc, 0.5, R, T_)
+        g = adaptive_gpu_unit(tr)
+        rep = lockstep.check_adaptive(Q, K, V, ids, P, [0], [1, 2], hh, rc, 0.5, R, T_, g, tr.choice)
+        assert rep.ok and rep.adopted == 0, (T_, rep.failures)
+    # a choice that skips a composite reaching the threshold
+    tr = adaptive.run_unit(Q, K, V, ids, P, [0], [1, 2], hh, rc, 0.5, R, 0.0)
+    assert tr.choice == adaptive.C_SPECIAL
+    tr3 = adaptive.run_unit(Q, K, V, ids, P, [0], [1, 2], hh, rc, 0.5, R, 2.0)
+    rep = lockstep.check_adaptive(Q, K, V, ids, P, [0], [1, 2], hh, rc, 0.5, R, 0.0, adaptive_gpu_unit(tr3), 5)
+    assert not rep.ok
+    # a wrong victim under the frequent+local composite (threshold = its recovery, so it is chosen)
+    rec = tr3.recoveries
+    assert rec[3] < rec[4]
+    T4 = rec[4]
+    trl = adaptive.run_unit(Q, K, V, ids, P, [0], [1, 2], hh, rc, 0.5, R, T4)
+    assert trl.choice == adaptive.C_LOCAL
+    g = adaptive_gpu_unit(trl)
+    assert lockstep.check_adaptive(Q, K, V, ids, P, [0], [1, 2], hh, rc, 0.5, R, T4, g, 4).ok
+    s = int(np.flatnonzero(trl.evicted >= 0)[2])
+    bad = next(int(j) for j in trl.prefill_kept if int(j) != int(trl.evicted[s]) and ids[j] not in (0, 1, 2)
+               and int(j) < P - rc)
+    g.evicted[s] = bad
+    assert not lockstep.check_adaptive(Q, K, V, ids, P, [0], [1, 2], hh, rc, 0.5, R, T4, g, 4).ok
+    # an in-band choice: the threshold a hair above C4's recovery makes C5 the oracle's choice,
+    # and C4 is then accepted (adopted) as within the recovery band
+    rep = lockstep.check_adaptive(Q, K, V, ids, P, [0], [1, 2], hh, rc, 0.5, R, T4 + 1e-7, adaptive_gpu_unit(trl), 4)
+    assert rep.adopted == 1 and not any("profile" in f for f in rep.failures)
