@@ -20,14 +20,14 @@ LIB_PATH = os.path.join(HERE, "libkvevict.so")
 
 KVE_OK, KVE_EINVAL, KVE_ESTATE, KVE_ENOMEM, KVE_EDEVICE, KVE_EUNSUPPORTED = range(6)
 KVE_F32, KVE_F16, KVE_BF16 = 0, 1, 2
-KVE_FULL, KVE_H2O, KVE_LOCAL, KVE_SPECIAL, KVE_HASH, KVE_PERSIST = 0, 1, 2, 3, 4, 5
+KVE_FULL, KVE_H2O, KVE_LOCAL, KVE_SPECIAL, KVE_HASH, KVE_PERSIST, KVE_ADAPTIVE = 0, 1, 2, 3, 4, 5, 6
 
 DTYPE_CODES = {torch.float32: KVE_F32, torch.float16: KVE_F16, torch.bfloat16: KVE_BF16}
 CODE_DTYPES = {v: k for k, v in DTYPE_CODES.items()}
 
 EXPORTED = ("kvevict_workspace_size", "kvevict_create", "kvevict_destroy", "kvevict_prefill",
-            "kvevict_decode_step", "kvevict_kept_indices", "kvevict_capacity", "kvevict_position",
-            "kvevict_status_string", "kvevict_last_error")
+            "kvevict_decode_step", "kvevict_kept_indices", "kvevict_unit_policies", "kvevict_capacity",
+            "kvevict_position", "kvevict_status_string", "kvevict_last_error")
 
 
 class KVEvictError(RuntimeError):
@@ -46,6 +46,9 @@ class kve_config(ctypes.Structure):
         ("vocab", ctypes.c_int32), ("keep_token_bitmap", ctypes.POINTER(ctypes.c_uint32)),
         ("sketch_bits", ctypes.c_int32), ("lsh_proj_bf16", ctypes.POINTER(ctypes.c_uint16)),
         ("history", ctypes.POINTER(ctypes.c_int32)),
+        ("special_token_bitmap", ctypes.POINTER(ctypes.c_uint32)),
+        ("punct_token_bitmap", ctypes.POINTER(ctypes.c_uint32)),
+        ("profile_rows", ctypes.c_int32), ("profile_threshold", ctypes.c_float),
     ]
 
 
@@ -69,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvevict_prefill": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp]),
         "kvevict_decode_step": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
         "kvevict_kept_indices": (i32, [vp, i32, vp, vp, vp, vp]),
+        "kvevict_unit_policies": (i32, [vp, i32, vp, vp]),
         "kvevict_capacity": (i32, [vp, i32]),
         "kvevict_position": (i32, [vp, i32]),
         "kvevict_status_string": (ctypes.c_char_p, [i32]),
@@ -110,10 +114,13 @@ def keep_bitmap(keep_ids: Sequence[int], vocab: int) -> np.ndarray:
 
 def make_config(layers: int, batch: int, heads: int, head_dim: int, max_context: int, dtype: torch.dtype,
                 policy, heavy, recent, softmax_scale: float = 0.0, keep_ids: Sequence[int] = (),
-                vocab: int = 0, proj: Optional[torch.Tensor] = None, history=None):
+                vocab: int = 0, proj: Optional[torch.Tensor] = None, history=None,
+                special_ids: Optional[Sequence[int]] = None, punct_ids: Optional[Sequence[int]] = None,
+                profile_rows: int = 0, profile_threshold: float = 0.0):
     """Returns (kve_config, keepalive) -- keepalive holds the host tables.
 
     history: per-head history windows [layers * heads] (PERSIST heads), or None.
+    special_ids, punct_ids, profile_rows, profile_threshold: ADAPTIVE heads.
     """
     pol = np.ascontiguousarray(np.asarray(policy, dtype=np.int32).reshape(-1))
     hv = np.ascontiguousarray(np.asarray(heavy, dtype=np.int32).reshape(-1))
@@ -144,6 +151,15 @@ def make_config(layers: int, batch: int, heads: int, head_dim: int, max_context:
         hw = np.ascontiguousarray(np.asarray(history, dtype=np.int32).reshape(-1))
         keep.append(hw)
         cfg.history = hw.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    if special_ids is not None or punct_ids is not None:
+        if not vocab:
+            raise ValueError("special_ids / punct_ids need vocab")
+        cfg.vocab = vocab
+        for field, ids_ in (("special_token_bitmap", special_ids or ()), ("punct_token_bitmap", punct_ids or ())):
+            bm = keep_bitmap(ids_, vocab)
+            keep.append(bm)
+            setattr(cfg, field, bm.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)))
+        cfg.profile_rows, cfg.profile_threshold = profile_rows, profile_threshold
     return cfg, keep
 
 
@@ -181,6 +197,11 @@ def kvevict_kept_indices(h, layer: int, pos_out, count_out, scores_out=None, str
                                                _stream(stream)), "kvevict_kept_indices")
 
 
+def kvevict_unit_policies(h, layer: int, choice_out, stream=None) -> None:
+    _check(load_library().kvevict_unit_policies(h, layer, _ptr(choice_out), _stream(stream)),
+           "kvevict_unit_policies")
+
+
 def kvevict_capacity(h, layer: int) -> int:
     return int(load_library().kvevict_capacity(h, layer))
 
@@ -201,14 +222,16 @@ class KVCache:
     def __init__(self, layers: int, batch: int, heads: int, head_dim: int, max_context: int,
                  dtype: torch.dtype, policy, heavy, recent, softmax_scale: float = 0.0,
                  keep_ids: Sequence[int] = (), vocab: int = 0, proj: Optional[torch.Tensor] = None,
-                 history=None, device="cuda"):
+                 history=None, special_ids=None, punct_ids=None, profile_rows: int = 0,
+                 profile_threshold: float = 0.0, device="cuda"):
         self.layers, self.batch, self.heads, self.head_dim = layers, batch, heads, head_dim
         dev = torch.device(device)
         if dev.type == "cuda" and dev.index is None:
             dev = torch.device("cuda", torch.cuda.current_device())
         self.max_context, self.dtype, self.device = max_context, dtype, dev
         self.cfg, self._keep = make_config(layers, batch, heads, head_dim, max_context, dtype, policy, heavy,
-                                           recent, softmax_scale, keep_ids, vocab, proj, history)
+                                           recent, softmax_scale, keep_ids, vocab, proj, history, special_ids,
+                                           punct_ids, profile_rows, profile_threshold)
         self.workspace_bytes = kvevict_workspace_size(self.cfg)
         self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
         self.handle = kvevict_create(self.cfg, self.workspace)
@@ -255,6 +278,12 @@ class KVCache:
         out = self._tensor(out, shp, torch.float32, "out")
         evicted = self._tensor(evicted, (self.batch, self.heads), torch.int32, "evicted")
         kvevict_decode_step(self.handle, layer, q, k, v, token_ids, out, evicted, stream)
+        return out
+
+    def unit_policies(self, layer: int, stream=None) -> torch.Tensor:
+        """[batch, heads] int32: the composite each profiled unit chose (0 for other policies)."""
+        out = torch.empty((self.batch, self.heads), dtype=torch.int32, device=self.device)
+        kvevict_unit_policies(self.handle, layer, out, stream)
         return out
 
     def kept_indices(self, layer: int, with_scores: bool = True, stream=None):

@@ -155,4 +155,14 @@ __device__ inline bool token_kept(const uint32_t* bitmap, int vocab, int id) {
   return (bitmap[id >> 5] >> (id & 31)) & 1u;
 }
 
+// Whether token `id` is protected under id mode `mode`.
+__device__ inline bool id_protected(int mode, const IdSets& s, int id) {
+  switch (mode) {
+    case IDS_SPECIAL: return token_kept(s.special, s.vocab, id);
+    case IDS_SPECIAL_PUNCT: return token_kept(s.special, s.vocab, id) || token_kept(s.punct, s.vocab, id);
+    case IDS_KEEP: return token_kept(s.keep, s.vocab, id);
+  }
+  return false;
+}
+
 }  // namespace kve

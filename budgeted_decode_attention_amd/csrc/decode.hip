@@ -164,7 +164,11 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
   int evicted = -1;
   double s_new = 0.0;
   if (m.policy == H2O) {
+    // With protected ids (a profiled composite) protected tokens carry score
+    // +inf, so they are never the minimum, and only unprotected tokens count
+    // against heavy + recent (npcount[u]).
     const int lim = t - m.recent;              // candidates: position <= t - recent
+    const bool prot_new = m.ids != IDS_NONE && id_protected(m.ids, io.sets, io.ids[u / sh.heads]);
     MinKey best{INFINITY, INT32_MAX, INT32_MAX};
     // four slots per thread per round: their score/position loads are issued
     // together, so a large cache costs n / (4 NT) load latencies, not n / NT
@@ -190,13 +194,16 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
         }
       }
     }
-    s_new = (double)e_new * invL;
-    if (tid == 0 && t <= lim) {
+    s_new = prot_new ? (double)INFINITY : (double)e_new * invL;
+    if (tid == 0 && t <= lim && !prot_new) {
       const MinKey k{s_new, t, n};
       if (key_less(k, best)) best = k;
     }
     best = block_argmin<kNT>(best, kscr);      // barriers inside: S[] updates done
-    if (n >= m.heavy + m.recent) {
+    const int held = m.ids == IDS_NONE ? n : c.npcount[u];   // unprotected tokens kept before t
+    if (prot_new) {
+      wslot = n;
+    } else if (held >= m.heavy + m.recent && best.s < INFINITY) {
       if (best.slot == n) {
         evicted = t;                           // the new token itself scores lowest
       } else {
@@ -205,6 +212,7 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
       }
     } else {
       wslot = n;
+      if (tid == 0 && m.ids != IDS_NONE) c.npcount[u] = held + 1;
     }
   } else if (m.policy == PERSIST) {
     // history bit k = pivotal k steps ago; pivotal: weight / L >= 1 / (n + 1),
@@ -264,7 +272,7 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
   } else if (m.policy == FULL) {
     wslot = n;
   } else if (m.policy == SPECIAL) {
-    if (token_kept(io.keep_bitmap, io.vocab, io.ids[u / sh.heads])) wslot = n;
+    if (id_protected(m.ids, io.sets, io.ids[u / sh.heads])) wslot = n;
     else evicted = t;
   }
   if (wslot >= 0) {
@@ -301,7 +309,7 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
   const int tid = threadIdx.x;
   const int col = tid % R::LPR;
   const int rg = tid / R::LPR;
-  const HeadMeta m = c.meta[u % sh.heads];
+  const HeadMeta m = c.meta[u];
   const int n = c.count[u];
   const int with_new = m.policy == HASH ? 0 : 1;  // HASH: token t is already in a slot
   const size_t slot0 = (size_t)u * c.cap;
@@ -373,7 +381,7 @@ __global__ KVE_DECODE_ATTR void decode_partial_kernel(Shape sh, LayerCache c, De
   const int c1 = min(n, c0 + sp.chunk);
   const int tid = threadIdx.x;
   const int col = tid % R::LPR;
-  const HeadMeta m = c.meta[u % sh.heads];
+  const HeadMeta m = c.meta[u];
   const size_t slot0 = (size_t)u * c.cap;
   const char* Kb = (const char*)c.K + slot0 * D * R::ES;
   const char* Vb = (const char*)c.V + slot0 * D * R::ES;
@@ -427,7 +435,7 @@ __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, De
   const int tid = threadIdx.x;
   const int col = tid % R::LPR;
   const int rg = tid / R::LPR;
-  const HeadMeta m = c.meta[u % sh.heads];
+  const HeadMeta m = c.meta[u];
   const int n = c.count[u];
   const int with_new = m.policy == HASH ? 0 : 1;
   const int nch = (n + sp.chunk - 1) / sp.chunk;

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
   __shared__ uint64_t kscr[kNT / kWave];
   const int u = ul.ids[blockIdx.x];
   const int tid = threadIdx.x;
-  const HeadMeta m = c.meta[u % sh.heads];
+  const HeadMeta m = c.meta[u];
   const int B = m.heavy;
   const int n0 = min(P, B);
   uint32_t* ssk = lds;
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kNT) void hash_evict_kernel(Shape sh, LayerCache c,
   __shared__ float xs[2][D];
   const int u = ul.ids[blockIdx.x];
   const int tid = threadIdx.x;
-  const HeadMeta m = c.meta[u % sh.heads];
+  const HeadMeta m = c.meta[u];
   const int B = m.heavy;
   stage_proj<D>(Ws, c.proj);
   for (int i = tid; i < 2 * D; i += kNT)

@@ -85,7 +85,7 @@ int head_capacity(int policy, int heavy, int recent, int max_context) {
     case KVE_PERSIST: return heavy + recent;
     case KVE_LOCAL: return recent;
     case KVE_HASH: return heavy;
-    default: return max_context;       // FULL, SPECIAL
+    default: return max_context;       // FULL, SPECIAL, ADAPTIVE (protected tokens accumulate)
   }
 }
 
@@ -96,10 +96,11 @@ struct LayerInfo {
   bool uniform = true;   // every head of the layer has the same capacity
   int chunk = 0;         // split-decode chunk (slots)
   int nch = 0;           // chunks per unit
-  bool any_h2o = false, any_hash = false, any_special = false, any_persist = false;
+  bool any_h2o = false, any_hash = false, any_special = false, any_persist = false, any_adaptive = false;
   int max_hash_budget = 0;
   int max_window = 0;    // largest history window of the layer's PERSIST heads
-  std::vector<int32_t> h2o_units, hash_units, persist_units;
+  int ad_heavy = -1, ad_recent = -1;   // the layer's ADAPTIVE heads' frequent slots and local window
+  std::vector<int32_t> h2o_units, hash_units, persist_units, adaptive_units;
 };
 
 kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
@@ -118,7 +119,7 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
   const long long units = (long long)c->batch * c->heads;
   if (units > (1 << 24)) return fail(KVE_EUNSUPPORTED, "more than 2^24 units per layer");
   info->assign(c->layers, LayerInfo());
-  bool need_bitmap = false, need_proj = false;
+  bool need_bitmap = false, need_proj = false, need_ids_tables = false;
   for (int l = 0; l < c->layers; ++l) {
     LayerInfo& li = (*info)[l];
     for (int h = 0; h < c->heads; ++h) {
@@ -158,6 +159,17 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
           li.max_hash_budget = std::max(li.max_hash_budget, hv);
           need_proj = true;
           break;
+        case KVE_ADAPTIVE:
+          if (hv < 0 || rc < 0 || hv + rc > c->max_context)
+            return fail(KVE_EINVAL, "layer %d head %d: ADAPTIVE needs 0 <= heavy, recent and heavy + recent <= "
+                        "max_context", l, h);
+          if (li.ad_heavy >= 0 && (hv != li.ad_heavy || rc != li.ad_recent))
+            return fail(KVE_EUNSUPPORTED, "layer %d: ADAPTIVE heads of one layer must share heavy and recent", l);
+          li.ad_heavy = hv;
+          li.ad_recent = rc;
+          li.any_adaptive = true;
+          need_ids_tables = true;
+          break;
         case KVE_FULL:
         case KVE_SPECIAL:
           if (hv != 0 || rc != 0)
@@ -180,6 +192,7 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
         if (p == KVE_H2O) li.h2o_units.push_back(b * c->heads + h);
         if (p == KVE_HASH) li.hash_units.push_back(b * c->heads + h);
         if (p == KVE_PERSIST) li.persist_units.push_back(b * c->heads + h);
+        if (p == KVE_ADAPTIVE) li.adaptive_units.push_back(b * c->heads + h);
       }
   }
   const SplitPolicy sp = split_policy();
@@ -200,6 +213,12 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
     return fail(KVE_EINVAL, "SPECIAL heads need keep_token_bitmap and vocab >= 1");
   if (need_proj && (!c->lsh_proj_bf16 || c->sketch_bits != 32))
     return fail(KVE_EUNSUPPORTED, "HASH heads need lsh_proj_bf16 and sketch_bits = 32");
+  if (need_ids_tables) {
+    if (!c->special_token_bitmap || !c->punct_token_bitmap || c->vocab < 1)
+      return fail(KVE_EINVAL, "ADAPTIVE heads need special_token_bitmap, punct_token_bitmap and vocab >= 1");
+    if (c->profile_rows < 1 || !std::isfinite(c->profile_threshold))
+      return fail(KVE_EINVAL, "ADAPTIVE heads need profile_rows >= 1 and a finite profile_threshold");
+  }
   return KVE_OK;
 }
 
@@ -219,7 +238,7 @@ struct Layer {
   kve::LayerCache cache{};
   kve::SplitScratch split{};   // chunk == 0: fused path
   LayerInfo info;
-  kve::UnitList h2o{nullptr, 0}, hash{nullptr, 0}, persist{nullptr, 0};
+  kve::UnitList h2o{nullptr, 0}, hash{nullptr, 0}, persist{nullptr, 0}, adaptive{nullptr, 0};
   int position = -1;   // next decode position; -1 before prefill
 };
 
@@ -229,14 +248,19 @@ struct kve_ctx {
   kve_config cfg{};
   kve::Shape shape{};
   std::vector<Layer> layers;
-  kve::HeadMeta* meta = nullptr;       // device [layers][heads]
-  uint32_t* bitmap = nullptr;          // device
+  kve::HeadMeta* meta = nullptr;       // device [layers][U]
+  uint32_t* bitmap = nullptr;          // device keep set (SPECIAL heads)
+  uint32_t* special = nullptr;         // device special / punctuation sets (ADAPTIVE heads)
+  uint32_t* punct = nullptr;
+  double* mass = nullptr;              // device [U][max_context] (ADAPTIVE layers)
   uint16_t* proj = nullptr;            // device [layers][d][32]
   float* lse = nullptr;                // device [U][max_context][2]
   double* colsum = nullptr;            // device [U][max_context]
   uint32_t* qsk = nullptr;             // device [U][max_context]
   uint32_t* ksk = nullptr;             // device [U][max_context]
   bool sync_check = false;
+
+  kve::IdSets sets() const { return {bitmap, special, punct, cfg.vocab}; }
 };
 
 
@@ -247,13 +271,18 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
     const size_t U = (size_t)c->batch * c->heads;
   const size_t d = c->head_dim, es = elem_size(c->dtype);
   const size_t N = c->max_context;
-  bool any_hash = false, any_special = false;
+  bool any_hash = false, any_special = false, any_adaptive = false;
   for (const auto& li : info) {
     any_hash |= li.any_hash;
     any_special |= li.any_special;
+    any_adaptive |= li.any_adaptive;
   }
-  auto* meta = pl.take<kve::HeadMeta>((size_t)c->layers * c->heads);
-  auto* bitmap = any_special ? pl.take<uint32_t>(((size_t)c->vocab + 31) / 32) : nullptr;
+  const size_t words = ((size_t)c->vocab + 31) / 32;
+  auto* meta = pl.take<kve::HeadMeta>((size_t)c->layers * U);
+  auto* bitmap = any_special ? pl.take<uint32_t>(words) : nullptr;
+  auto* special = any_adaptive ? pl.take<uint32_t>(words) : nullptr;
+  auto* punct = any_adaptive ? pl.take<uint32_t>(words) : nullptr;
+  auto* mass = any_adaptive ? pl.take<double>(U * N) : nullptr;
   auto* proj = any_hash ? pl.take<uint16_t>((size_t)c->layers * d * 32) : nullptr;
   auto* lse = pl.take<float>(U * N * 2);
   auto* colsum = pl.take<double>(U * N);
@@ -271,6 +300,9 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
   if (ctx) {
     ctx->meta = meta;
     ctx->bitmap = bitmap;
+    ctx->special = special;
+    ctx->punct = punct;
+    ctx->mass = mass;
     ctx->proj = proj;
     ctx->lse = lse;
     ctx->colsum = colsum;
@@ -287,12 +319,14 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
     lc.pos = pl.take<int32_t>(U * cap);
     lc.sk = li.any_hash ? pl.take<uint32_t>(U * cap) : nullptr;
     lc.count = pl.take<int32_t>(U);
-    lc.meta = meta ? meta + (size_t)l * c->heads : nullptr;
+    lc.npcount = pl.take<int32_t>(U);
+    lc.meta = meta ? meta + (size_t)l * U : nullptr;
     lc.proj = proj ? proj + (size_t)l * d * 32 : nullptr;
     lc.cap = (int32_t)cap;
     int32_t* h2o_ids = li.h2o_units.empty() ? nullptr : pl.take<int32_t>(li.h2o_units.size());
     int32_t* hash_ids = li.hash_units.empty() ? nullptr : pl.take<int32_t>(li.hash_units.size());
     int32_t* persist_ids = li.persist_units.empty() ? nullptr : pl.take<int32_t>(li.persist_units.size());
+    int32_t* adaptive_ids = li.adaptive_units.empty() ? nullptr : pl.take<int32_t>(li.adaptive_units.size());
     if (ctx) {
       Layer& L = ctx->layers[l];
       L.cache = lc;
@@ -301,6 +335,7 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
       L.h2o = {h2o_ids, (int32_t)li.h2o_units.size()};
       L.hash = {hash_ids, (int32_t)li.hash_units.size()};
       L.persist = {persist_ids, (int32_t)li.persist_units.size()};
+      L.adaptive = {adaptive_ids, (int32_t)li.adaptive_units.size()};
     }
   }
   return pl.off;
@@ -359,6 +394,7 @@ kve_status kvevict_create(const kve_config* cfg, void* d_workspace, size_t bytes
   ctx->cfg.keep_token_bitmap = nullptr;
   ctx->cfg.lsh_proj_bf16 = nullptr;
   ctx->cfg.history = nullptr;
+  ctx->cfg.special_token_bitmap = ctx->cfg.punct_token_bitmap = nullptr;
   const float scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / std::sqrt((float)cfg->head_dim);
   ctx->shape = {cfg->batch, cfg->heads, cfg->head_dim, cfg->dtype, scale};
   ctx->layers.resize(cfg->layers);
@@ -367,17 +403,29 @@ kve_status kvevict_create(const kve_config* cfg, void* d_workspace, size_t bytes
   ctx->sync_check = env && env[0] == '1';
 
   // tables to the device
-  std::vector<kve::HeadMeta> meta((size_t)cfg->layers * cfg->heads);
-  for (size_t i = 0; i < meta.size(); ++i) {
-    const int p = cfg->policy[i], hv = cfg->heavy[i], rc = cfg->recent[i];
-    const int w = p == KVE_PERSIST ? cfg->history[i] : 0;
-    meta[i] = {p, hv, rc, head_capacity(p, hv, rc, cfg->max_context), w};
-  }
+  // one record per unit: units of a head share the head's entry (profiled
+  // units get theirs at prefill)
+  const size_t U = (size_t)cfg->batch * cfg->heads;
+  std::vector<kve::HeadMeta> meta((size_t)cfg->layers * U);
+  for (int l = 0; l < cfg->layers; ++l)
+    for (size_t u = 0; u < U; ++u) {
+      const size_t i = (size_t)l * cfg->heads + u % cfg->heads;
+      const int p = cfg->policy[i], hv = cfg->heavy[i], rc = cfg->recent[i];
+      const int w = p == KVE_PERSIST ? cfg->history[i] : 0;
+      const int ids = p == KVE_SPECIAL ? kve::IDS_KEEP : kve::IDS_NONE;
+      meta[(size_t)l * U + u] = {p, hv, rc, head_capacity(p, hv, rc, cfg->max_context), w, ids, 0};
+    }
   s = dev(hipMemcpy(ctx->meta, meta.data(), meta.size() * sizeof(kve::HeadMeta), hipMemcpyHostToDevice),
           "copy head table");
   if (s == KVE_OK && ctx->bitmap)
     s = dev(hipMemcpy(ctx->bitmap, cfg->keep_token_bitmap, ((size_t)cfg->vocab + 31) / 32 * 4,
                       hipMemcpyHostToDevice), "copy keep bitmap");
+  if (s == KVE_OK && ctx->special)
+    s = dev(hipMemcpy(ctx->special, cfg->special_token_bitmap, ((size_t)cfg->vocab + 31) / 32 * 4,
+                      hipMemcpyHostToDevice), "copy special bitmap");
+  if (s == KVE_OK && ctx->punct)
+    s = dev(hipMemcpy(ctx->punct, cfg->punct_token_bitmap, ((size_t)cfg->vocab + 31) / 32 * 4,
+                      hipMemcpyHostToDevice), "copy punctuation bitmap");
   if (s == KVE_OK && ctx->proj)
     s = dev(hipMemcpy(ctx->proj, cfg->lsh_proj_bf16, (size_t)cfg->layers * cfg->head_dim * 32 * 2,
                       hipMemcpyHostToDevice), "copy projection");
@@ -391,6 +439,9 @@ kve_status kvevict_create(const kve_config* cfg, void* d_workspace, size_t bytes
               "copy unit list");
     if (s == KVE_OK && L.persist.n)
       s = dev(hipMemcpy((void*)L.persist.ids, L.info.persist_units.data(), L.persist.n * 4,
+                        hipMemcpyHostToDevice), "copy unit list");
+    if (s == KVE_OK && L.adaptive.n)
+      s = dev(hipMemcpy((void*)L.adaptive.ids, L.info.adaptive_units.data(), L.adaptive.n * 4,
                         hipMemcpyHostToDevice), "copy unit list");
   }
   if (s != KVE_OK) {
@@ -415,7 +466,8 @@ kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t P, const void* q
     return fail(KVE_EINVAL, "prompt_len %d outside [1, %d]", P, h->cfg.max_context);
   if (!q || !k || !v) return fail(KVE_EINVAL, "q, k and v are required");
   Layer& L = h->layers[layer];
-  if (L.info.any_special && !token_ids) return fail(KVE_EINVAL, "token_ids required (layer has SPECIAL heads)");
+  if ((L.info.any_special || L.info.any_adaptive) && !token_ids)
+    return fail(KVE_EINVAL, "token_ids required (layer has SPECIAL or ADAPTIVE heads)");
   hipStream_t st = (hipStream_t)stream;
   const kve::Shape& sh = h->shape;
   hipError_t e = hipSuccess;
@@ -437,6 +489,9 @@ kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t P, const void* q
       e = mfma ? kve::launch_prefill_rowstats_mfma(sh, P, L.persist, q, k, h->lse,
                                                    std::max(0, P - L.info.max_window), st)
                : kve::launch_prefill_rowstats_valu(sh, P, L.persist, q, k, v, h->lse, nullptr, st);
+    if (e == hipSuccess && L.adaptive.n)
+      e = mfma ? kve::launch_prefill_rowstats_mfma(sh, P, L.adaptive, q, k, h->lse, 0, st)
+               : kve::launch_prefill_rowstats_valu(sh, P, L.adaptive, q, k, v, h->lse, nullptr, st);
   }
   if (e == hipSuccess && L.h2o.n)
     e = mfma ? kve::launch_prefill_colsum_mfma(sh, P, L.h2o, q, k, h->lse, h->colsum, st)
@@ -444,8 +499,18 @@ kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t P, const void* q
   if (e == hipSuccess && L.persist.n)
     e = mfma ? kve::launch_prefill_persist_mfma(sh, P, L.persist, q, k, h->lse, L.cache.meta, h->colsum, st)
              : kve::launch_prefill_persist_valu(sh, P, L.persist, q, k, h->lse, L.cache.meta, h->colsum, st);
+  // Profiled units: column sums with the profiled rows' mass, then the choice
+  if (e == hipSuccess && L.adaptive.n) {
+    const int rows = std::min(P, h->cfg.profile_rows);
+    e = mfma ? kve::launch_prefill_colsum_mass_mfma(sh, P, L.adaptive, q, k, h->lse, h->colsum, h->mass, rows, st)
+             : kve::launch_prefill_colsum_mass_valu(sh, P, L.adaptive, q, k, h->lse, h->colsum, h->mass, rows, st);
+    const kve::Profile pf{rows, h->cfg.profile_threshold, L.info.ad_heavy, L.info.ad_recent};
+    if (e == hipSuccess)
+      e = kve::launch_prefill_adaptive(sh, L.cache, L.adaptive, P, h->colsum, h->mass, pf, k, v, token_ids,
+                                       h->sets(), st);
+  }
   if (e == hipSuccess)
-    e = kve::launch_prefill_select(sh, L.cache, P, h->colsum, k, v, token_ids, h->bitmap, h->cfg.vocab, st);
+    e = kve::launch_prefill_select(sh, L.cache, P, h->colsum, k, v, token_ids, h->sets(), st);
   if (e == hipSuccess && L.hash.n) {
     e = kve::launch_sketch_rows(sh, L.hash, q, P, 0, P, L.cache.proj, h->qsk, st);
     if (e == hipSuccess) e = kve::launch_sketch_rows(sh, L.hash, k, P, 0, P, L.cache.proj, h->ksk, st);
@@ -467,13 +532,14 @@ kve_status kvevict_decode_step(kve_handle h, int32_t layer, const void* q, const
   if (L.position >= h->cfg.max_context)
     return fail(KVE_ESTATE, "layer %d: position %d reached max_context", layer, L.position);
   if (!q || !k || !v || !out) return fail(KVE_EINVAL, "q, k, v and out are required");
-  if (L.info.any_special && !token_ids) return fail(KVE_EINVAL, "token_ids required (layer has SPECIAL heads)");
+  if ((L.info.any_special || L.info.any_adaptive) && !token_ids)
+    return fail(KVE_EINVAL, "token_ids required (layer has SPECIAL or ADAPTIVE heads)");
   hipStream_t st = (hipStream_t)stream;
   const kve::Shape& sh = h->shape;
   hipError_t e = hipSuccess;
   if (L.hash.n) e = kve::launch_hash_evict(sh, L.cache, L.hash, L.position, q, k, v, evicted_pos, st);
   if (e == hipSuccess) {
-    const kve::DecodeIO io{q, k, v, token_ids, h->bitmap, h->cfg.vocab, out, evicted_pos, L.position};
+    const kve::DecodeIO io{q, k, v, token_ids, h->sets(), out, evicted_pos, L.position};
     e = kve::launch_decode(sh, L.cache, io, L.split.chunk ? &L.split : nullptr, st);
   }
   if (e != hipSuccess) return dev(e, "decode launch");
@@ -497,6 +563,21 @@ kve_status kvevict_kept_indices(kve_handle h, int32_t layer, int32_t* pos_out, i
     e = hipMemcpyAsync(scores_out, L.cache.S, U * cap * 8, hipMemcpyDeviceToDevice, st);
   if (e != hipSuccess) return dev(e, "kept_indices copy");
   return finish(h, st, "kept_indices");
+}
+
+kve_status kvevict_unit_policies(kve_handle h, int32_t layer, int32_t* choice_out, void* stream) {
+  kve_status s = check_layer(h, layer);
+  if (s != KVE_OK) return s;
+  if (!choice_out) return fail(KVE_EINVAL, "choice_out is required");
+  const Layer& L = h->layers[layer];
+  if (L.position < 0) return fail(KVE_ESTATE, "layer %d has no cache yet", layer);
+  hipStream_t st = (hipStream_t)stream;
+  const size_t U = h->shape.units();
+  // the `choice` field of each unit record, strided copy
+  hipError_t e = hipMemcpy2DAsync(choice_out, sizeof(int32_t), &L.cache.meta[0].choice, sizeof(kve::HeadMeta),
+                                  sizeof(int32_t), U, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return dev(e, "unit_policies copy");
+  return finish(h, st, "unit_policies");
 }
 
 int32_t kvevict_capacity(kve_handle h, int32_t layer) {

@@ -9,15 +9,30 @@
 namespace kve {
 
 enum Dtype : int32_t { F32 = 0, F16 = 1, BF16 = 2 };
-enum Policy : int32_t { FULL = 0, H2O = 1, LOCAL = 2, SPECIAL = 3, HASH = 4, PERSIST = 5 };
+enum Policy : int32_t { FULL = 0, H2O = 1, LOCAL = 2, SPECIAL = 3, HASH = 4, PERSIST = 5, ADAPTIVE = 6 };
 
-// Per-head policy record, device-resident, one per head of a layer.
+// Which token ids a unit protects (keeps for good): none, the special set,
+// special or punctuation, or the SPECIAL policy's keep set.
+enum IdMode : int32_t { IDS_NONE = 0, IDS_SPECIAL = 1, IDS_SPECIAL_PUNCT = 2, IDS_KEEP = 3 };
+
+// Per-unit policy record, device-resident, one per unit of a layer (units of
+// a head share it unless profiling chose per unit).
 struct HeadMeta {
-  int32_t policy;
+  int32_t policy;  // effective policy (ADAPTIVE only until the prefill chooses)
   int32_t heavy;   // H2O, PERSIST: heavy slots; HASH: budget
   int32_t recent;  // H2O, PERSIST: recent window; LOCAL: window
-  int32_t cap;     // slots this head may occupy (<= the layer's stride)
+  int32_t cap;     // slots this unit may occupy (<= the layer's stride)
   int32_t window;  // PERSIST: steps of pivotal history (1..64)
+  int32_t ids;     // IdMode: protected ids (SPECIAL: kept ids; H2O: never evicted)
+  int32_t choice;  // profiled units: chosen composite 1..5 (0: not profiled)
+};
+
+// Token-id sets as device bitmaps over [0, vocab).
+struct IdSets {
+  const uint32_t* keep;      // SPECIAL heads' keep set
+  const uint32_t* special;   // profiled heads: special tokens
+  const uint32_t* punct;     // profiled heads: punctuation
+  int32_t vocab;
 };
 
 // One layer's cache, carved from the workspace.
@@ -29,7 +44,8 @@ struct LayerCache {
   int32_t* pos;         // [U][cap] position per slot, -1 = empty
   uint32_t* sk;         // [U][cap] key sketches (HASH heads), or null
   int32_t* count;       // [U] occupied slots
-  const HeadMeta* meta; // [heads]
+  int32_t* npcount;     // [U] occupied slots holding unprotected tokens (H2O units with protected ids)
+  HeadMeta* meta;       // [U] (written by the prefill for profiled units)
   const uint16_t* proj; // [d][bits] bf16 projection (HASH), or null
   int32_t cap;          // slot stride per unit
 };
@@ -79,10 +95,30 @@ hipError_t launch_prefill_persist_mfma(const Shape& sh, int P, UnitList units, c
 hipError_t launch_prefill_persist_valu(const Shape& sh, int P, UnitList units, const void* q,
                                        const void* k, const float* lse, const HeadMeta* meta,
                                        double* bits, hipStream_t st);
-// Chooses the kept prompt positions per the head's policy and fills the cache.
+// Column sums (as launch_prefill_colsum_mfma) plus, per key, the mass the last
+// `rows` prompt rows give it: mass[u][j] = sum_{i >= max(j, P - rows)} weight.
+hipError_t launch_prefill_colsum_mass_mfma(const Shape& sh, int P, UnitList units, const void* q,
+                                           const void* k, const float* lse, double* colsum,
+                                           double* mass, int rows, hipStream_t st);
+hipError_t launch_prefill_colsum_mass_valu(const Shape& sh, int P, UnitList units, const void* q,
+                                           const void* k, const float* lse, double* colsum,
+                                           double* mass, int rows, hipStream_t st);
+// Chooses the kept prompt positions per the unit's policy and fills the cache.
 hipError_t launch_prefill_select(const Shape& sh, const LayerCache& c, int P, const double* colsum,
-                                 const void* k, const void* v, const int32_t* ids,
-                                 const uint32_t* keep_bitmap, int32_t vocab, hipStream_t st);
+                                 const void* k, const void* v, const int32_t* ids, const IdSets& sets,
+                                 hipStream_t st);
+// Profiled units: recovered mass of each composite over the last `rows` rows,
+// the first reaching `threshold` (else the full cache) becomes the unit's
+// policy (meta[u] rewritten), and its kept set fills the cache.
+struct Profile {
+  int32_t rows;
+  float threshold;
+  int32_t heavy, recent;     // frequent slots and local window of the composites
+};
+hipError_t launch_prefill_adaptive(const Shape& sh, const LayerCache& c, UnitList units, int P,
+                                   const double* colsum, const double* mass, const Profile& pf,
+                                   const void* k, const void* v, const int32_t* ids, const IdSets& sets,
+                                   hipStream_t st);
 
 // ---- HashEvict
 // Packed sign sketches of `n` rows of x (row stride d) under proj, per unit
@@ -105,8 +141,7 @@ struct DecodeIO {
   const void* k;            // [U][d]
   const void* v;            // [U][d]
   const int32_t* ids;       // [batch] or null
-  const uint32_t* keep_bitmap;
-  int32_t vocab;
+  IdSets sets;
   float* out;               // [U][d]
   int32_t* evicted;         // [U] or null
   int32_t t;                // position of the new token

@@ -394,6 +394,23 @@ __device__ inline void colsum_fold(const f32x4 (&acc)[2], int i0, int nb, int j0
     }
 }
 
+// colsum_fold with masks, also adding the weights of rows >= wlo into pm.
+__device__ inline void mass_fold(const f32x4 (&acc)[2], int i0, int nb, int j0, int P, int wlo, int g, int c16,
+                                 const Scale2& c2, float lh, float fl, float (&part)[2][4], float (&pm)[2][4]) {
+  const int qi = i0 + nb * 16 + c16;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = acc[mb][r];
+      const float p = exp2_fast(fmaf(s, c2.lo, fmaf(s, c2.hi, -lh))) * fl;
+      const int kj = j0 + mb * 16 + g * 4 + r;
+      const bool ok = qi < P && qi >= kj;
+      part[mb][r] += ok ? p : 0.f;
+      pm[mb][r] += (ok && qi >= wlo) ? p : 0.f;
+    }
+}
+
 // Bits of one 16 x 16 block: for this lane's key (mb, r) and the 16 queries
 // i0 + nb * 16 + 0..15, the history bits at ages P - 1 - query.  Every lane
 // takes part in the ballots.
@@ -420,10 +437,13 @@ __device__ inline void persist_fold(const f32x4 (&acc)[2], int i0, int nb, int j
     }
 }
 
-template <int DT, int D, bool BITS>
+// MODE 0: column sums; 1: persistence bits; 2: column sums plus, per key, the
+// mass of the last `rows` prompt rows (into mass).
+template <int DT, int D, int MODE>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(KVE_PREFILL_WAVES_PER_EU)))
 void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void* k, const float* lse,
-                        double* colsum, const HeadMeta* meta) {
+                        double* colsum, const HeadMeta* meta, double* mass, int rows) {
+  constexpr bool BITS = MODE == 1;
   constexpr int KS = D / 32;
   __shared__ __attribute__((aligned(16))) char Qs[2][Tile<D>::kBytes];
   __shared__ float Lh[2][kTile], Ll[2][kTile];  // lse in log2 units, float pair
@@ -447,11 +467,11 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
     for (int ks = 0; ks < KS; ++ks)
       kf[mb][ks] = kj < P ? ld16(kbase + ((size_t)kj * D + ks * 32 + g * 8) * 2) : make_uint4(0, 0, 0, 0);
   }
-  double cs[2][4];
+  double cs[2][4], ms[2][4];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) cs[mb][r] = 0.0;
+    for (int r = 0; r < 4; ++r) cs[mb][r] = ms[mb][r] = 0.0;
 
   // lse of one query, in log2 units as a float pair
   auto lse2 = [&](int i, float& hi, float& lo) {
@@ -461,7 +481,7 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
     lo = (float)(L2 - (double)hi);
   };
   // BITS: only rows i >= wlo count, starting from the 64-aligned tile that holds the first
-  const int wlo = BITS ? P - meta[u % sh.heads].window : 0;
+  const int wlo = BITS ? P - meta[u].window : (MODE == 2 ? P - rows : 0);
   const int i_first = BITS ? max(kb * kBlk, wlo) & ~(kTile - 1) : kb * kBlk;
   auto thr = [&](int i) { return (float)(-log2((double)(i + 1))); };
   uint64_t bits[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
@@ -489,11 +509,12 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
     }
     if (i0 + kTile - 1 >= j0) {                 // some query of the tile follows a key of the wave
       const bool edge = i0 < j0 + 32 || i0 + kTile > P;
-      float part[2][4];
+      float part[2][4], pm[2][4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part[mb][r] = 0.f;
+        for (int r = 0; r < 4; ++r) part[mb][r] = pm[mb][r] = 0.f;
+      const bool in_rows = MODE == 2 && i0 + kTile > wlo;   // the tile reaches the profiled rows
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -505,13 +526,17 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
         }
         const float lh = Lh[buf][nb * 16 + c16];
         if (BITS) persist_fold(acc, i0, nb, j0, P, wlo, g, c16, c2, lh, Ll[buf][nb * 16 + c16], Th[buf][nb * 16 + c16], bits);
+        else if (in_rows) mass_fold(acc, i0, nb, j0, P, wlo, g, c16, c2, lh, Lf[buf][nb * 16 + c16], part, pm);
         else if (edge) colsum_fold<true>(acc, i0, nb, j0, P, g, c16, c2, lh, Lf[buf][nb * 16 + c16], part);
         else colsum_fold<false>(acc, i0, nb, j0, P, g, c16, c2, lh, Lf[buf][nb * 16 + c16], part);
       }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) cs[mb][r] += (double)part[mb][r];
+        for (int r = 0; r < 4; ++r) {
+          cs[mb][r] += (double)part[mb][r];
+          if (MODE == 2) ms[mb][r] += (double)pm[mb][r];
+        }
     }
     if (more) {
       store_tile<D>(nxt, Qs[buf ^ 1]);          // that buffer was last read before the previous barrier
@@ -545,6 +570,12 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
       for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
       const int kj = j0 + mb * 16 + g * 4 + r;
       if (c16 == 0 && kj < P) colsum[(size_t)u * P + kj] = v;
+      if (MODE == 2) {
+        double w = ms[mb][r];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) w += __shfl_xor(w, o);
+        if (c16 == 0 && kj < P) mass[(size_t)u * P + kj] = w;
+      }
     }
 }
 
@@ -743,12 +774,12 @@ hipError_t rowstats_t(const Shape& sh, int P, UnitList ul, const void* q, const 
   return hipGetLastError();
 }
 
-template <int DT, int D, bool BITS>
+template <int DT, int D, int MODE>
 hipError_t colsum_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, const float* lse,
-                    double* colsum, const HeadMeta* meta, hipStream_t st) {
+                    double* colsum, const HeadMeta* meta, double* mass, int rows, hipStream_t st) {
   dim3 grid(ul.n, (P + kBlk - 1) / kBlk);
-  hipLaunchKernelGGL((colsum_mfma_kernel<DT, D, BITS>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse, colsum,
-                     meta);
+  hipLaunchKernelGGL((colsum_mfma_kernel<DT, D, MODE>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse, colsum,
+                     meta, mass, rows);
   return hipGetLastError();
 }
 
@@ -783,10 +814,10 @@ hipError_t launch_prefill_colsum_mfma(const Shape& sh, int P, UnitList ul, const
                                       const float* lse, double* colsum, hipStream_t st) {
   if (ul.n <= 0) return hipSuccess;
   switch (sh.dtype * 1000 + sh.d) {
-    case F16 * 1000 + 64: return colsum_t<F16, 64, false>(sh, P, ul, q, k, lse, colsum, nullptr, st);
-    case F16 * 1000 + 128: return colsum_t<F16, 128, false>(sh, P, ul, q, k, lse, colsum, nullptr, st);
-    case BF16 * 1000 + 64: return colsum_t<BF16, 64, false>(sh, P, ul, q, k, lse, colsum, nullptr, st);
-    case BF16 * 1000 + 128: return colsum_t<BF16, 128, false>(sh, P, ul, q, k, lse, colsum, nullptr, st);
+    case F16 * 1000 + 64: return colsum_t<F16, 64, 0>(sh, P, ul, q, k, lse, colsum, nullptr, nullptr, 0, st);
+    case F16 * 1000 + 128: return colsum_t<F16, 128, 0>(sh, P, ul, q, k, lse, colsum, nullptr, nullptr, 0, st);
+    case BF16 * 1000 + 64: return colsum_t<BF16, 64, 0>(sh, P, ul, q, k, lse, colsum, nullptr, nullptr, 0, st);
+    case BF16 * 1000 + 128: return colsum_t<BF16, 128, 0>(sh, P, ul, q, k, lse, colsum, nullptr, nullptr, 0, st);
   }
   return hipErrorInvalidValue;
 }
@@ -796,10 +827,28 @@ hipError_t launch_prefill_persist_mfma(const Shape& sh, int P, UnitList ul, cons
   if (ul.n <= 0) return hipSuccess;
   if (!meta) return hipErrorInvalidValue;
   switch (sh.dtype * 1000 + sh.d) {
-    case F16 * 1000 + 64: return colsum_t<F16, 64, true>(sh, P, ul, q, k, lse, bits, meta, st);
-    case F16 * 1000 + 128: return colsum_t<F16, 128, true>(sh, P, ul, q, k, lse, bits, meta, st);
-    case BF16 * 1000 + 64: return colsum_t<BF16, 64, true>(sh, P, ul, q, k, lse, bits, meta, st);
-    case BF16 * 1000 + 128: return colsum_t<BF16, 128, true>(sh, P, ul, q, k, lse, bits, meta, st);
+    case F16 * 1000 + 64: return colsum_t<F16, 64, 1>(sh, P, ul, q, k, lse, bits, meta, nullptr, 0, st);
+    case F16 * 1000 + 128: return colsum_t<F16, 128, 1>(sh, P, ul, q, k, lse, bits, meta, nullptr, 0, st);
+    case BF16 * 1000 + 64: return colsum_t<BF16, 64, 1>(sh, P, ul, q, k, lse, bits, meta, nullptr, 0, st);
+    case BF16 * 1000 + 128: return colsum_t<BF16, 128, 1>(sh, P, ul, q, k, lse, bits, meta, nullptr, 0, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kve
+
+namespace kve {
+
+hipError_t launch_prefill_colsum_mass_mfma(const Shape& sh, int P, UnitList ul, const void* q, const void* k,
+                                           const float* lse, double* colsum, double* mass, int rows,
+                                           hipStream_t st) {
+  if (ul.n <= 0) return hipSuccess;
+  if (!mass || rows < 1) return hipErrorInvalidValue;
+  switch (sh.dtype * 1000 + sh.d) {
+    case F16 * 1000 + 64: return colsum_t<F16, 64, 2>(sh, P, ul, q, k, lse, colsum, nullptr, mass, rows, st);
+    case F16 * 1000 + 128: return colsum_t<F16, 128, 2>(sh, P, ul, q, k, lse, colsum, nullptr, mass, rows, st);
+    case BF16 * 1000 + 64: return colsum_t<BF16, 64, 2>(sh, P, ul, q, k, lse, colsum, nullptr, mass, rows, st);
+    case BF16 * 1000 + 128: return colsum_t<BF16, 128, 2>(sh, P, ul, q, k, lse, colsum, nullptr, mass, rows, st);
   }
   return hipErrorInvalidValue;
 }

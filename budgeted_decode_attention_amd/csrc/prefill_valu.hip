@@ -136,22 +136,26 @@ __global__ __launch_bounds__(kNT) void rowstats_valu_kernel(Shape sh, int P, Uni
   }
 }
 
+// With `mass` non-null also mass[u][j] = the part of the sum from rows >= P - rows.
 template <int DT, int D>
 __global__ __launch_bounds__(kNT) void colsum_valu_kernel(Shape sh, int P, UnitList ul, const void* q,
-                                                           const void* k, const float* lse, double* colsum) {
+                                                           const void* k, const float* lse, double* colsum,
+                                                           double* mass, int rows) {
   constexpr int ES = elem_bytes<DT>();
   __shared__ float Ks[kRB * (D + 1)];
   __shared__ float Qs[kKT * (D + 1)];
   __shared__ float Lh[kKT], Ll[kKT];
   __shared__ double part_s[kNT];
+  __shared__ double mpart_s[kNT];
   const int u = ul.ids ? ul.ids[blockIdx.y] : blockIdx.y;
   const int col0 = blockIdx.x * kRB;
+  const int wlo = P - rows;
   const size_t base = (size_t)u * P * D * ES;
   const int tid = threadIdx.x;
   stage_rows<DT, D>(Ks, (const char*)k + base, col0, kRB, P);
   const int jc = tid % kRB;                  // key column in the block
   const int grp = tid / kRB;                 // which 8 rows of each query tile
-  double acc = 0.0;
+  double acc = 0.0, macc = 0.0;
   for (int i0 = col0; i0 < P; i0 += kKT) {
     __syncthreads();
     stage_rows<DT, D>(Qs, (const char*)q + base, i0, kKT, P);
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(kNT) void colsum_valu_kernel(Shape sh, int P, UnitL
       Ll[tid] = lse[li + 1];
     }
     __syncthreads();
-    float part = 0.f;
+    float part = 0.f, mpart = 0.f;
 #pragma unroll
     for (int ii = 0; ii < kKT / 4; ++ii) {
       const int i = grp * (kKT / 4) + ii;
@@ -169,16 +173,26 @@ __global__ __launch_bounds__(kNT) void colsum_valu_kernel(Shape sh, int P, UnitL
       for (int e = 0; e < D; ++e) s = fmaf(Qs[i * (D + 1) + e], Ks[jc * (D + 1) + e], s);
       s *= sh.scale;
       const bool ok = (i0 + i < P) && (i0 + i >= col0 + jc);
-      if (ok) part += expf((s - Lh[i]) - Ll[i]);
+      if (ok) {
+        const float p = expf((s - Lh[i]) - Ll[i]);
+        part += p;
+        if (i0 + i >= wlo) mpart += p;
+      }
     }
     acc += (double)part;
+    macc += (double)mpart;
   }
   part_s[tid] = acc;
+  mpart_s[tid] = macc;
   __syncthreads();
   if (tid < kRB && col0 + tid < P) {
-    double s = 0.0;
-    for (int g = 0; g < kNT / kRB; ++g) s += part_s[g * kRB + tid];
+    double s = 0.0, m = 0.0;
+    for (int g = 0; g < kNT / kRB; ++g) {
+      s += part_s[g * kRB + tid];
+      m += mpart_s[g * kRB + tid];
+    }
     colsum[(size_t)u * P + col0 + tid] = s;
+    if (mass) mass[(size_t)u * P + col0 + tid] = m;
   }
 }
 
@@ -195,7 +209,7 @@ __global__ __launch_bounds__(kNT) void persist_valu_kernel(Shape sh, int P, Unit
   const int col0 = blockIdx.x * kRB;
   const size_t base = (size_t)u * P * D * ES;
   const int tid = threadIdx.x;
-  const int wlo = P - meta[u % sh.heads].window;
+  const int wlo = P - meta[u].window;
   stage_rows<DT, D>(Ks, (const char*)k + base, col0, kRB, P);
   const int jc = tid % kRB;
   const int grp = tid / kRB;
@@ -250,9 +264,10 @@ hipError_t rowstats_t(const Shape& sh, int P, UnitList ul, const void* q, const 
 
 template <int DT, int D>
 hipError_t colsum_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, const float* lse,
-                    double* colsum, hipStream_t st) {
+                    double* colsum, double* mass, int rows, hipStream_t st) {
   dim3 grid((P + kRB - 1) / kRB, ul.n);
-  hipLaunchKernelGGL((colsum_valu_kernel<DT, D>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse, colsum);
+  hipLaunchKernelGGL((colsum_valu_kernel<DT, D>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse, colsum, mass,
+                     rows);
   return hipGetLastError();
 }
 
@@ -273,13 +288,20 @@ hipError_t launch_prefill_rowstats_valu(const Shape& sh, int P, UnitList ul, con
 
 hipError_t launch_prefill_colsum_valu(const Shape& sh, int P, UnitList ul, const void* q, const void* k,
                                       const float* lse, double* colsum, hipStream_t st) {
+  return launch_prefill_colsum_mass_valu(sh, P, ul, q, k, lse, colsum, nullptr, 1, st);
+}
+
+hipError_t launch_prefill_colsum_mass_valu(const Shape& sh, int P, UnitList ul, const void* q, const void* k,
+                                           const float* lse, double* colsum, double* mass, int rows,
+                                           hipStream_t st) {
+  if (ul.n <= 0) return hipSuccess;
   switch (sh.dtype * 1000 + sh.d) {
-    case F32 * 1000 + 64: return colsum_t<F32, 64>(sh, P, ul, q, k, lse, colsum, st);
-    case F32 * 1000 + 128: return colsum_t<F32, 128>(sh, P, ul, q, k, lse, colsum, st);
-    case F16 * 1000 + 64: return colsum_t<F16, 64>(sh, P, ul, q, k, lse, colsum, st);
-    case F16 * 1000 + 128: return colsum_t<F16, 128>(sh, P, ul, q, k, lse, colsum, st);
-    case BF16 * 1000 + 64: return colsum_t<BF16, 64>(sh, P, ul, q, k, lse, colsum, st);
-    case BF16 * 1000 + 128: return colsum_t<BF16, 128>(sh, P, ul, q, k, lse, colsum, st);
+    case F32 * 1000 + 64: return colsum_t<F32, 64>(sh, P, ul, q, k, lse, colsum, mass, rows, st);
+    case F32 * 1000 + 128: return colsum_t<F32, 128>(sh, P, ul, q, k, lse, colsum, mass, rows, st);
+    case F16 * 1000 + 64: return colsum_t<F16, 64>(sh, P, ul, q, k, lse, colsum, mass, rows, st);
+    case F16 * 1000 + 128: return colsum_t<F16, 128>(sh, P, ul, q, k, lse, colsum, mass, rows, st);
+    case BF16 * 1000 + 64: return colsum_t<BF16, 64>(sh, P, ul, q, k, lse, colsum, mass, rows, st);
+    case BF16 * 1000 + 128: return colsum_t<BF16, 128>(sh, P, ul, q, k, lse, colsum, mass, rows, st);
   }
   return hipErrorInvalidValue;
 }

@@ -12,6 +12,7 @@
 //            the token's 64-bit pivotal history, Scissorhands persistence
 //            reading); the slot keeps the history bits themselves.
 //   HASH     skipped here (prompt replay kernel).
+//   profiled units (ADAPTIVE heads): adaptive_kernel below.
 //
 // The heavy threshold is found by a radix select over the float64 score bit
 // patterns (scores are >= 0, so unsigned order is numeric order): eight
@@ -53,25 +54,100 @@ __device__ inline uint64_t score_key(const double* c, int j, bool count) {
   return count ? (uint64_t)__popcll(b) : b;
 }
 
+// LDS state of one radix selection.
+struct RadixLds {
+  uint32_t hist[256];
+  int iscr[kNT / kWave];
+  uint64_t prefix;
+  int want;
+  int cut;
+};
+
+// The `want` largest keys among positions j in [0, nc) with cand(j), the
+// newer first on equal keys: on return j is selected iff cand(j) and
+// (key > T or (key == T and j >= cut)).  want must not exceed the number of
+// candidates.  Eight 8-bit passes over the key bits (first_pass > 0 when
+// the higher bytes are known to be zero); uniform control flow, barriers.
+template <class Key, class Cand>
+__device__ inline void radix_top(int nc, int want, int first_pass, Key key, Cand cand, RadixLds& r, uint64_t& T,
+                                 int& cut) {
+  const int tid = threadIdx.x;
+  if (tid == 0) { r.prefix = 0; r.want = want; }
+  for (int pass = first_pass; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    r.hist[tid] = 0;
+    __syncthreads();
+    const uint64_t prefix = r.prefix;
+    const uint64_t hmask = pass == 0 ? 0ull : (~0ull << (shift + 8));   // bytes already fixed (zero when skipped)
+    for (int j = tid; j < nc; j += kNT) {
+      if (!cand(j)) continue;
+      const uint64_t kv = key(j);
+      if ((kv & hmask) == (prefix & hmask)) atomicAdd(&r.hist[(kv >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int w = r.want;
+      int b = 255;
+      for (; b > 0; --b) {
+        if ((int)r.hist[b] >= w) break;
+        w -= r.hist[b];
+      }
+      r.want = w;
+      r.prefix = prefix | ((uint64_t)b << shift);
+    }
+    __syncthreads();
+  }
+  T = r.prefix;
+  // the `want` newest candidates with key == T
+  const int w = r.want;
+  if (tid == 0) r.cut = 0;
+  int seen = 0;
+  for (int base = nc - 1; base >= 0 && seen < w; base -= kNT) {
+    const int j = base - tid;
+    const bool eq = j >= 0 && cand(j) && key(j) == T;
+    int total;
+    const int before = block_flag_scan(eq, &total, r.iscr);
+    if (eq && seen + before + 1 == w) r.cut = j;
+    seen += total;
+  }
+  __syncthreads();
+  cut = r.cut;
+}
+
+// Gathers the K/V rows of kept_pos[0, count) into the unit's slots.
 template <int DT, int D>
-__global__ __launch_bounds__(kNT) void select_kernel(Shape sh, LayerCache c, int P, const double* colsum,
-                                                     const void* k, const void* v, const int32_t* ids,
-                                                     const uint32_t* keep_bitmap, int32_t vocab) {
+__device__ inline void gather_rows(const LayerCache& c, int u, int P, const int32_t* kept_pos, int count,
+                                   const void* k, const void* v) {
   constexpr int EPL = St<DT>::EPL;
   constexpr int ES = elem_bytes<DT>();
   constexpr int LPR = D / EPL;
   constexpr int RPI = kNT / LPR;
+  const int tid = threadIdx.x;
+  const size_t slot0 = (size_t)u * c.cap;
+  const size_t src0 = (size_t)u * P * D * ES;
+  char* Kd = (char*)c.K + slot0 * D * ES;
+  char* Vd = (char*)c.V + slot0 * D * ES;
+  const int col = tid % LPR;
+  for (int s = tid / LPR; s < count; s += RPI) {
+    const size_t so = ((size_t)kept_pos[s] * D + col * EPL) * ES;
+    const size_t dof = ((size_t)s * D + col * EPL) * ES;
+    st16(Kd + dof, ld16((const char*)k + src0 + so));
+    st16(Vd + dof, ld16((const char*)v + src0 + so));
+  }
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kNT) void select_kernel(Shape sh, LayerCache c, int P, const double* colsum,
+                                                     const void* k, const void* v, const int32_t* ids,
+                                                     IdSets sets) {
   extern __shared__ int32_t kept_pos[];     // [cap]
-  __shared__ uint32_t hist[256];
+  __shared__ RadixLds rl;
   __shared__ int iscr[kNT / kWave];
-  __shared__ uint64_t sh_prefix;
-  __shared__ int sh_want;
-  __shared__ int sh_cut;
 
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
-  const HeadMeta m = c.meta[u % sh.heads];
-  if (m.policy == HASH) return;
+  const HeadMeta m = c.meta[u];
+  if (m.policy == HASH || m.policy == ADAPTIVE || m.choice != 0) return;   // replay / profiled units
   const size_t slot0 = (size_t)u * c.cap;
   const double* cu = colsum ? colsum + (size_t)u * P : nullptr;
 
@@ -84,47 +160,9 @@ __global__ __launch_bounds__(kNT) void select_kernel(Shape sh, LayerCache c, int
   uint64_t T = 0;
   int cut = 0;                              // ties with key == T kept iff position >= cut
   if (select_heavy) {
-    if (tid == 0) { sh_prefix = 0; sh_want = m.heavy; }
     // persistence counts are at most 64: only the lowest byte can differ
-    for (int pass = persist ? 7 : 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
-      hist[tid] = 0;
-      __syncthreads();
-      const uint64_t prefix = sh_prefix;
-      const uint64_t hmask = pass == 0 ? 0ull : (~0ull << (shift + 8));   // bytes already fixed (zero when skipped)
-      for (int j = tid; j < nc; j += kNT) {
-        const uint64_t key = score_key(cu, j, persist);
-        const bool match = (key & hmask) == (prefix & hmask);
-        if (match) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int want = sh_want;
-        int b = 255;
-        for (; b > 0; --b) {
-          if ((int)hist[b] >= want) break;
-          want -= hist[b];
-        }
-        sh_want = want;
-        sh_prefix = prefix | ((uint64_t)b << shift);
-      }
-      __syncthreads();
-    }
-    T = sh_prefix;
-    // the `want` newest positions with key == T
-    const int want = sh_want;
-    if (tid == 0) sh_cut = 0;
-    int seen = 0;
-    for (int base = nc - 1; base >= 0 && seen < want; base -= kNT) {
-      const int j = base - tid;
-      const bool eq = j >= 0 && score_key(cu, j, persist) == T;
-      int total;
-      const int before = block_flag_scan(eq, &total, iscr);
-      if (eq && seen + before + 1 == want) sh_cut = j;
-      seen += total;
-    }
-    __syncthreads();
-    cut = sh_cut;
+    radix_top(nc, m.heavy, persist ? 7 : 0, [&](int j) { return score_key(cu, j, persist); },
+              [](int) { return true; }, rl, T, cut);
   }
 
   // ---- kept flags and compaction into slots [0, count)
@@ -138,7 +176,7 @@ __global__ __launch_bounds__(kNT) void select_kernel(Shape sh, LayerCache c, int
       } else if (m.policy == LOCAL) {
         keep = j >= P - m.recent;
       } else if (m.policy == SPECIAL) {
-        keep = token_kept(keep_bitmap, vocab, ids[(size_t)(u / sh.heads) * P + j]);
+        keep = id_protected(m.ids, sets, ids[(size_t)(u / sh.heads) * P + j]);
       } else if (h2o) {
         if (P <= B || j >= nc) {
           keep = true;
@@ -166,22 +204,168 @@ __global__ __launch_bounds__(kNT) void select_kernel(Shape sh, LayerCache c, int
   __syncthreads();
 
   // ---- gather K/V rows of the kept positions
-  const size_t src0 = (size_t)u * P * D * ES;
-  char* Kd = (char*)c.K + slot0 * D * ES;
-  char* Vd = (char*)c.V + slot0 * D * ES;
-  const int col = tid % LPR;
-  for (int s = tid / LPR; s < count; s += RPI) {
-    const size_t so = ((size_t)kept_pos[s] * D + col * EPL) * ES;
-    const size_t dof = ((size_t)s * D + col * EPL) * ES;
-    st16(Kd + dof, ld16((const char*)k + src0 + so));
-    st16(Vd + dof, ld16((const char*)v + src0 + so));
+  gather_rows<DT, D>(c, u, P, kept_pos, count, k, v);
+}
+
+// ------------------------------------------------------------------ profiled units
+// FastGen review page, proposed method: a lightweight profile of the prompt's
+// attention picks each head's policy, the composites being tried greedily in
+// the order special -> punctuation -> frequent -> local, with the full cache
+// last.  Per unit: the share a composite recovers is the mass the last R
+// prompt rows give to its end-of-prompt kept set (mass[u][j] holds that mass
+// per key, so a share is a sum over the set divided by R); the first share
+// reaching the threshold picks the composite, which then fills the cache and
+// becomes the unit's policy.  Protected tokens (special or punctuation ids)
+// carry score +inf in the frequent composites, so they are never evicted.
+template <int DT, int D>
+__global__ __launch_bounds__(kNT) void adaptive_kernel(Shape sh, LayerCache c, UnitList ul, int P,
+                                                       const double* colsum, const double* mass, Profile pf,
+                                                       const void* k, const void* v, const int32_t* ids,
+                                                       IdSets sets) {
+  extern __shared__ int32_t kept_pos[];     // [cap]
+  __shared__ RadixLds rl;
+  __shared__ int iscr[kNT / kWave];
+  __shared__ double dscr[kNT / kWave];
+  const int u = ul.ids ? ul.ids[blockIdx.x] : blockIdx.x;
+  const int tid = threadIdx.x;
+  const size_t slot0 = (size_t)u * c.cap;
+  const double* cu = colsum + (size_t)u * P;
+  const double* mu = mass + (size_t)u * P;
+  const int32_t* idu = ids + (size_t)(u / sh.heads) * P;
+  const int R = min(pf.rows, P);
+  const int hh = pf.heavy, W = pf.recent;
+  const double thr = (double)pf.threshold;
+  auto special = [&](int j) { return token_kept(sets.special, sets.vocab, idu[j]); };
+  auto prot = [&](int j) { return special(j) || token_kept(sets.punct, sets.vocab, idu[j]); };
+  auto key = [&](int j) { return (uint64_t)__double_as_longlong(cu[j]); };
+  auto free_ = [&](int j) { return !prot(j); };
+
+  // masses of the id sets, of the whole prompt and of the unprotected window
+  double m1 = 0.0, m2 = 0.0, mall = 0.0, mwin = 0.0, nfree = 0.0, wfree = 0.0;
+  for (int j = tid; j < P; j += kNT) {
+    const double x = mu[j];
+    const bool s1 = special(j), s2 = s1 || token_kept(sets.punct, sets.vocab, idu[j]);
+    mall += x;
+    if (s1) m1 += x;
+    if (s2) {
+      m2 += x;
+    } else {
+      nfree += 1.0;
+      if (j >= P - W) {
+        wfree += 1.0;
+        mwin += x;
+      }
+    }
   }
+  m1 = block_sum<kNT>(m1, dscr);
+  m2 = block_sum<kNT>(m2, dscr);
+  mall = block_sum<kNT>(mall, dscr);
+  mwin = block_sum<kNT>(mwin, dscr);
+  const int nf = (int)block_sum<kNT>(nfree, dscr);
+  const int wf = (int)block_sum<kNT>(wfree, dscr);
+
+  const double inv = 1.0 / R;
+  int choice = 5;
+  uint64_t T3 = 0, T4 = 0;
+  int cut3 = 0, cut4 = 0;
+  const bool all3 = nf <= hh, all4 = nf <= hh + W;   // the prompt fits the unprotected budget
+  const int quota4 = hh + W - wf;                    // older unprotected slots of the local composite
+  if (m1 * inv >= thr) {
+    choice = 1;
+  } else if (m2 * inv >= thr) {
+    choice = 2;
+  } else {
+    double rec3 = mall * inv;
+    if (!all3) {
+      if (hh > 0) radix_top(P, hh, 0, key, free_, rl, T3, cut3);
+      double sel = 0.0;
+      for (int j = tid; j < P; j += kNT)
+        if (hh > 0 && free_(j) && (key(j) > T3 || (key(j) == T3 && j >= cut3))) sel += mu[j];
+      rec3 = (m2 + block_sum<kNT>(sel, dscr)) * inv;
+    }
+    if (rec3 >= thr) {
+      choice = 3;
+    } else {
+      double rec4 = mall * inv;
+      if (!all4) {
+        const int nc = P - W;
+        if (quota4 > 0) radix_top(nc, quota4, 0, key, free_, rl, T4, cut4);
+        double sel = 0.0;
+        for (int j = tid; j < nc; j += kNT)
+          if (quota4 > 0 && free_(j) && (key(j) > T4 || (key(j) == T4 && j >= cut4))) sel += mu[j];
+        rec4 = (m2 + mwin + block_sum<kNT>(sel, dscr)) * inv;
+      }
+      if (rec4 >= thr) choice = 4;
+    }
+  }
+
+  // ---- the chosen composite's kept set, compacted into slots [0, count)
+  int count = 0;
+  double nfk = 0.0;                                  // unprotected tokens kept (frequent composites)
+  for (int j0 = 0; j0 < P; j0 += kNT) {
+    const int j = j0 + tid;
+    bool keep = false, pj = false;
+    if (j < P) {
+      pj = prot(j);
+      switch (choice) {
+        case 1: keep = special(j); break;
+        case 2: keep = pj; break;
+        case 3: keep = pj || all3 || (hh > 0 && (key(j) > T3 || (key(j) == T3 && j >= cut3))); break;
+        case 4:
+          keep = pj || all4 || j >= P - W ||
+                 (quota4 > 0 && (key(j) > T4 || (key(j) == T4 && j >= cut4)));
+          break;
+        default: keep = true;
+      }
+    }
+    int total;
+    const int before = block_flag_scan(keep, &total, iscr);
+    if (keep) {
+      const int slot = count + before;
+      kept_pos[slot] = j;
+      c.pos[slot0 + slot] = j;
+      c.S[slot0 + slot] = (choice == 3 || choice == 4) ? (pj ? (double)INFINITY : cu[j]) : 0.0;
+      if (!pj) nfk += 1.0;
+    }
+    count += total;
+  }
+  nfk = block_sum<kNT>(nfk, dscr);
+  for (int s = count + tid; s < c.cap; s += kNT) {
+    c.pos[slot0 + s] = -1;
+    c.S[slot0 + s] = 0.0;
+  }
+  if (tid == 0) {
+    c.count[u] = count;
+    c.npcount[u] = (int)nfk;
+    HeadMeta m{FULL, 0, 0, c.cap, 0, IDS_NONE, choice};
+    if (choice == 1) { m.policy = SPECIAL; m.ids = IDS_SPECIAL; }
+    if (choice == 2) { m.policy = SPECIAL; m.ids = IDS_SPECIAL_PUNCT; }
+    if (choice == 3) { m.policy = H2O; m.ids = IDS_SPECIAL_PUNCT; m.heavy = hh; }
+    if (choice == 4) { m.policy = H2O; m.ids = IDS_SPECIAL_PUNCT; m.heavy = hh; m.recent = W; }
+    c.meta[u] = m;
+  }
+  __syncthreads();
+  gather_rows<DT, D>(c, u, P, kept_pos, count, k, v);
+}
+
+template <int DT, int D>
+hipError_t adaptive_t(const Shape& sh, const LayerCache& c, UnitList ul, int P, const double* colsum,
+                      const double* mass, const Profile& pf, const void* k, const void* v, const int32_t* ids,
+                      const IdSets& sets, hipStream_t st) {
+  const size_t lds = (size_t)c.cap * sizeof(int32_t);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)adaptive_kernel<DT, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((adaptive_kernel<DT, D>), dim3(ul.n), dim3(kNT), lds, st, sh, c, ul, P, colsum, mass, pf, k, v,
+                     ids, sets);
+  return hipGetLastError();
 }
 
 template <int DT, int D>
 hipError_t select_t(const Shape& sh, const LayerCache& c, int P, const double* colsum, const void* k,
-                    const void* v, const int32_t* ids, const uint32_t* keep_bitmap, int32_t vocab,
-                    hipStream_t st) {
+                    const void* v, const int32_t* ids, const IdSets& sets, hipStream_t st) {
   const size_t lds = (size_t)c.cap * sizeof(int32_t);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)select_kernel<DT, D>,
@@ -189,22 +373,42 @@ hipError_t select_t(const Shape& sh, const LayerCache& c, int P, const double* c
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((select_kernel<DT, D>), dim3(sh.units()), dim3(kNT), lds, st, sh, c, P, colsum, k, v, ids,
-                     keep_bitmap, vocab);
+                     sets);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_select(const Shape& sh, const LayerCache& c, int P, const double* colsum,
-                                 const void* k, const void* v, const int32_t* ids,
-                                 const uint32_t* keep_bitmap, int32_t vocab, hipStream_t st) {
+                                 const void* k, const void* v, const int32_t* ids, const IdSets& sets,
+                                 hipStream_t st) {
   switch (sh.dtype * 1000 + sh.d) {
-    case F32 * 1000 + 64: return select_t<F32, 64>(sh, c, P, colsum, k, v, ids, keep_bitmap, vocab, st);
-    case F32 * 1000 + 128: return select_t<F32, 128>(sh, c, P, colsum, k, v, ids, keep_bitmap, vocab, st);
-    case F16 * 1000 + 64: return select_t<F16, 64>(sh, c, P, colsum, k, v, ids, keep_bitmap, vocab, st);
-    case F16 * 1000 + 128: return select_t<F16, 128>(sh, c, P, colsum, k, v, ids, keep_bitmap, vocab, st);
-    case BF16 * 1000 + 64: return select_t<BF16, 64>(sh, c, P, colsum, k, v, ids, keep_bitmap, vocab, st);
-    case BF16 * 1000 + 128: return select_t<BF16, 128>(sh, c, P, colsum, k, v, ids, keep_bitmap, vocab, st);
+    case F32 * 1000 + 64: return select_t<F32, 64>(sh, c, P, colsum, k, v, ids, sets, st);
+    case F32 * 1000 + 128: return select_t<F32, 128>(sh, c, P, colsum, k, v, ids, sets, st);
+    case F16 * 1000 + 64: return select_t<F16, 64>(sh, c, P, colsum, k, v, ids, sets, st);
+    case F16 * 1000 + 128: return select_t<F16, 128>(sh, c, P, colsum, k, v, ids, sets, st);
+    case BF16 * 1000 + 64: return select_t<BF16, 64>(sh, c, P, colsum, k, v, ids, sets, st);
+    case BF16 * 1000 + 128: return select_t<BF16, 128>(sh, c, P, colsum, k, v, ids, sets, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kve
+
+namespace kve {
+
+hipError_t launch_prefill_adaptive(const Shape& sh, const LayerCache& c, UnitList ul, int P, const double* colsum,
+                                   const double* mass, const Profile& pf, const void* k, const void* v,
+                                   const int32_t* ids, const IdSets& sets, hipStream_t st) {
+  if (ul.n <= 0) return hipSuccess;
+  if (!colsum || !mass || !ids || pf.rows < 1) return hipErrorInvalidValue;
+  switch (sh.dtype * 1000 + sh.d) {
+    case F32 * 1000 + 64: return adaptive_t<F32, 64>(sh, c, ul, P, colsum, mass, pf, k, v, ids, sets, st);
+    case F32 * 1000 + 128: return adaptive_t<F32, 128>(sh, c, ul, P, colsum, mass, pf, k, v, ids, sets, st);
+    case F16 * 1000 + 64: return adaptive_t<F16, 64>(sh, c, ul, P, colsum, mass, pf, k, v, ids, sets, st);
+    case F16 * 1000 + 128: return adaptive_t<F16, 128>(sh, c, ul, P, colsum, mass, pf, k, v, ids, sets, st);
+    case BF16 * 1000 + 64: return adaptive_t<BF16, 64>(sh, c, ul, P, colsum, mass, pf, k, v, ids, sets, st);
+    case BF16 * 1000 + 128: return adaptive_t<BF16, 128>(sh, c, ul, P, colsum, mass, pf, k, v, ids, sets, st);
   }
   return hipErrorInvalidValue;
 }

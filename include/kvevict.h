@@ -92,9 +92,22 @@ typedef enum { KVE_F32 = 0, KVE_F16 = 1, KVE_BF16 = 2 } kve_dtype;
  *               outside the recent window is evicted (oldest first on equal
  *               counts), and the prompt keeps [P - recent, P) plus the
  *               `heavy` earlier tokens with the highest counts over the last
- *               `history` prompt rows (the newer first on equal counts). */
+ *               `history` prompt rows (the newer first on equal counts).
+ *   KVE_ADAPTIVE FastGen profiling (FastGen page, proposed method; the
+ *               profile and composites are a reading): at prefill each unit
+ *               (sequence, head) tries the composites C1 = special tokens,
+ *               C2 = C1 + punctuation, C3 = C2 + `heavy` frequent tokens,
+ *               C4 = C3 + a local window of `recent` tokens, in that order,
+ *               and takes the first whose end-of-prompt kept set receives at
+ *               least `profile_threshold` of the softmax mass of the last
+ *               `profile_rows` prompt rows (averaged over the rows); else
+ *               C5 = the full cache.  Tokens whose id is in the composite's
+ *               id set are kept for good; the others form an H2O cache of
+ *               heavy + recent tokens (C1, C2: none; C3: no window).
+ *               Capacity max_context.  kvevict_unit_policies reports the
+ *               choice. */
 typedef enum { KVE_FULL = 0, KVE_H2O = 1, KVE_LOCAL = 2, KVE_SPECIAL = 3, KVE_HASH = 4,
-               KVE_PERSIST = 5 } kve_policy;
+               KVE_PERSIST = 5, KVE_ADAPTIVE = 6 } kve_policy;
 
 typedef struct {
   int32_t layers;              /* >= 1; each layer has its own caches and position counter */
@@ -107,11 +120,14 @@ typedef struct {
   /* Host tables, [layers * heads], copied at create; row = layer, column = head.
    * The policy of a head is shared by every sequence of the batch. */
   const int32_t* policy;       /* kve_policy */
-  const int32_t* heavy;        /* H2O, PERSIST: heavy slots >= 0; HASH: budget B >= 1; others: 0 */
+  const int32_t* heavy;        /* H2O, PERSIST: heavy slots >= 0; HASH: budget B >= 1;
+                                  ADAPTIVE: frequent slots >= 0; others: 0 */
   const int32_t* recent;       /* H2O, PERSIST: recent window >= 0 with heavy + recent >= 1;
-                                  LOCAL: window W >= 1; others: 0 */
-  /* SPECIAL heads only (else may be NULL/0): host bitmap of kept token ids,
-   * bit (id & 31) of word id >> 5; ids outside [0, vocab) are not kept. */
+                                  LOCAL: window W >= 1; ADAPTIVE: local window >= 0 (the
+                                  ADAPTIVE heads of a layer share heavy and recent); others: 0 */
+  /* SPECIAL and ADAPTIVE heads only (else may be NULL/0): host bitmaps over
+   * token ids, bit (id & 31) of word id >> 5; ids outside [0, vocab) are in
+   * no set.  keep_token_bitmap: the SPECIAL heads' kept ids. */
   int32_t vocab;
   const uint32_t* keep_token_bitmap;   /* [(vocab + 31) / 32] */
   /* HASH heads only (else may be NULL/0): sketch width and the Gaussian
@@ -123,6 +139,14 @@ typedef struct {
   /* PERSIST heads only (else may be NULL): host [layers * heads] history
    * window in steps, 1..64; entries of other heads are ignored. */
   const int32_t* history;
+  /* ADAPTIVE heads only (else may be NULL/0): the special and punctuation id
+   * sets ([(vocab + 31) / 32] words each), the profiled prompt rows (>= 1;
+   * min(profile_rows, P) are used) and the recovered share (finite; above 1
+   * always selects the full cache). */
+  const uint32_t* special_token_bitmap;
+  const uint32_t* punct_token_bitmap;
+  int32_t profile_rows;
+  float profile_threshold;
 } kve_config;
 
 /* Bytes of device workspace the configuration needs (including 256-byte
@@ -141,7 +165,7 @@ kve_status kvevict_destroy(kve_handle h);
 /* Prefill of one layer with a prompt of P = prompt_len tokens (1 <= P <=
  * max_context), resetting that layer's caches and setting its position to P.
  * q, k, v: [batch][heads][P][d] in the storage dtype.  token_ids: [batch][P]
- * int32, required if the layer has a SPECIAL head, else may be NULL.
+ * int32, required if the layer has a SPECIAL or ADAPTIVE head, else may be NULL.
  * out: [batch][heads][P][d] fp32 causal attention of the prompt over itself
  * (uncompressed), or NULL to skip it.
  * H2O heads score every prompt token by the column sums of the causal softmax
@@ -156,7 +180,7 @@ kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t prompt_len,
 
 /* One decode step of one layer at its current position t (then t + 1).
  * q, k, v: [batch][heads][d] storage dtype, the new token's projections.
- * token_ids: [batch] int32 (required if the layer has a SPECIAL head).
+ * token_ids: [batch] int32 (required if the layer has a SPECIAL or ADAPTIVE head).
  * out: [batch][heads][d] fp32 attention output of the step.
  * evicted_pos: [batch][heads] int32, the position that left each unit's cache
  * at this step (for SPECIAL: t itself if not kept), -1 if none; or NULL.
@@ -171,10 +195,18 @@ kve_status kvevict_decode_step(kve_handle h, int32_t layer,
  * an empty slot.  count_out: [batch][heads] int32 number of occupied slots.
  * scores_out: [batch][heads][capacity] float64 accumulated score per slot
  * (H2O heads; PERSIST heads store the 64-bit pivotal history in the same 8
- * bytes, bit k = pivotal k steps before the latest one; other heads export
- * 0), or NULL.  `capacity` is kvevict_capacity(h, layer). */
+ * bytes, bit k = pivotal k steps before the latest one; ADAPTIVE units that
+ * chose C3 or C4 export the score of unprotected tokens and +inf for
+ * protected ones; other heads export 0), or NULL.  `capacity` is kvevict_capacity(h, layer). */
 kve_status kvevict_kept_indices(kve_handle h, int32_t layer, int32_t* pos_out,
                                 int32_t* count_out, double* scores_out, void* stream);
+
+/* The composite each unit of the layer chose at its last prefill (FastGen
+ * profiling, KVE_ADAPTIVE heads): choice_out [batch][heads] int32 receives
+ * 1 = special, 2 = + punctuation, 3 = + frequent, 4 = + local, 5 = full, and
+ * 0 for units of other policies.  Device pointer, stream-ordered; ESTATE
+ * before the layer's prefill. */
+kve_status kvevict_unit_policies(kve_handle h, int32_t layer, int32_t* choice_out, void* stream);
 
 /* Slots per unit in the layer's layout (the largest per-head capacity of the
  * layer), or -1 for a bad handle/layer. */

@@ -12,7 +12,7 @@ import torch
 from budgeted_decode_attention_amd import KVCache
 from oracle import lockstep
 from workloads import configs
-from workloads.configs import FULL, H2O, HASH, LOCAL, PERSIST, SPECIAL, Workload
+from workloads.configs import ADAPTIVE, FULL, H2O, HASH, LOCAL, PERSIST, SPECIAL, Workload
 from workloads.generate import LayerInputs, generate_layer, unit_ids, unit_sequence
 
 
@@ -29,6 +29,9 @@ def make_cache(w: Workload, inp: LayerInputs, policy=None, heavy=None, recent=No
         kw.update(keep_ids=w.keep_ids(), vocab=w.vocab)
     if HASH in list(pol):
         kw.update(proj=inp.proj)
+    if ADAPTIVE in list(pol):
+        kw.update(special_ids=list(w.special_ids), punct_ids=list(w.punct_ids), vocab=w.vocab,
+                  profile_rows=w.profile_rows, profile_threshold=w.profile_threshold)
     if PERSIST in list(pol):
         hw = [w.history_window if p == PERSIST else 0 for p in pol] if history is None else history
         kw.update(history=np.tile(np.array(hw, dtype=np.int32), layers))
@@ -47,6 +50,7 @@ class GpuRun:
     out: np.ndarray              # [T, B, H, d]
     evicted: np.ndarray          # [T, B, H]
     prompt_out: Optional[np.ndarray]
+    choice: Optional[np.ndarray] = None  # [B, H] composite chosen by profiled units (0: not profiled)
 
 
 def run_layer(kv: KVCache, inp: LayerInputs, layer: int = 0, steps: Optional[int] = None,
@@ -62,6 +66,7 @@ def run_layer(kv: KVCache, inp: LayerInputs, layer: int = 0, steps: Optional[int
                ids[:, :P].contiguous() if ids is not None else None, po)
     p0, c0, s0 = kv.kept_indices(layer)
     p0, c0, s0 = p0.cpu(), c0.cpu(), s0.cpu()
+    choice = kv.unit_policies(layer).cpu().numpy()
     out = torch.empty((T, Bt, H, d), dtype=torch.float32, device=dev)
     ev = torch.empty((T, Bt, H), dtype=torch.int32, device=dev)
     for s in range(T):
@@ -70,7 +75,7 @@ def run_layer(kv: KVCache, inp: LayerInputs, layer: int = 0, steps: Optional[int
     p1, c1, s1 = kv.kept_indices(layer)
     torch.cuda.synchronize()
     return GpuRun(p0.numpy(), c0.numpy(), s0.numpy(), p1.cpu().numpy(), c1.cpu().numpy(), s1.cpu().numpy(),
-                  out.cpu().numpy(), ev.cpu().numpy(), po.cpu().numpy() if po is not None else None)
+                  out.cpu().numpy(), ev.cpu().numpy(), po.cpu().numpy() if po is not None else None, choice)
 
 
 def gpu_unit(r: GpuRun, b: int, h: int) -> lockstep.GpuUnit:
@@ -101,6 +106,10 @@ def check_unit(w: Workload, inp_cpu: LayerInputs, r: GpuRun, b: int, h: int, pol
     elif p == PERSIST:
         win = w.history_window if history is None else history[h]
         rep = lockstep.check_persist(Q, K, V, P, hh, rr, win, sc, g, steps=T)
+    elif p == ADAPTIVE:
+        rep = lockstep.check_adaptive(Q, K, V, unit_ids(inp_cpu, b), P, list(w.special_ids), list(w.punct_ids),
+                                      hh, rr, sc, w.profile_rows, w.profile_threshold, g, int(r.choice[b, h]),
+                                      steps=T)
     else:
         rep = lockstep.check_fastgen(p, Q, K, V, P, sc, g, heavy=hh, recent=rr,
                                      ids=unit_ids(inp_cpu, b), keep_ids=w.keep_ids(), steps=T)

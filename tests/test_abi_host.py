@@ -22,7 +22,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     lib = binding.load_library()
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -120,3 +120,23 @@ def test_persist_capacity_is_heavy_plus_recent():
     a, ka = cfg(policy=[5, 5, 5], history=[8, 8, 8])
     b, kb = cfg()
     assert status_of(a) == status_of(b)   # same slots and workspace as the H2O table
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(), binding.KVE_OK),
+    (dict(profile_rows=0), binding.KVE_EINVAL),
+    (dict(profile_threshold=float("inf")), binding.KVE_EINVAL),
+    (dict(heavy=[-1, 10, 10]), binding.KVE_EINVAL),
+    (dict(heavy=[5, 10, 10], recent=[4, 5, 5], policy=[6, 6, 1]), binding.KVE_EUNSUPPORTED),  # mixed budgets
+])
+def test_adaptive_configs(over, status):
+    base = dict(policy=[6, 6, 1], heavy=[10, 10, 10], recent=[5, 5, 5], special_ids=[0, 1], punct_ids=[2],
+                vocab=100, profile_rows=16, profile_threshold=0.9)
+    base.update(over)
+    c, keep = cfg(**base)
+    assert status_of(c)[0] == status
+
+
+def test_adaptive_needs_its_id_sets():
+    c, keep = cfg(policy=[6, 1, 1], vocab=100, keep_ids=[0])
+    assert status_of(c)[0] == binding.KVE_EINVAL

@@ -64,6 +64,11 @@ def test_opt30b_persist_layer_full_size():
     assert rep.decisions == 6 * 256
 
 
+def test_llama65b_fastgen_profiled_full_size():
+    rep = run_full("llama65b_fastgen_profiled", 6)
+    assert rep.decisions > 0
+
+
 def test_llama65b_fastgen_full_size():
     run_full("llama65b_fastgen", 8, heads_of=[FULL, H2O, LOCAL, SPECIAL])
 

@@ -14,7 +14,7 @@ import torch
 
 from tests import harness
 from workloads import configs
-from workloads.configs import FULL, H2O, HASH, LOCAL, PERSIST, SPECIAL
+from workloads.configs import ADAPTIVE, FULL, H2O, HASH, LOCAL, PERSIST, SPECIAL
 from workloads.generate import generate_layer
 
 pytestmark = pytest.mark.gpu
@@ -219,3 +219,35 @@ def test_prefill_logit_jump_after_first_tile(dtype):
     inp.prompt_q[0, :, 151:] += (amp * u).to(inp.prompt_q.dtype)
     rep, _ = run_and_check(w)
     assert rep.ok
+
+
+# ---- FastGen profiling (adaptive composites)
+
+def test_adaptive_bf16_scaled(decode_path):
+    """Ten heads of the five attention kinds, two sequences: every composite
+    is chosen somewhere; lockstep against the oracle's profile and trajectory."""
+    w = configs.scaled("llama65b_fastgen_profiled", batch=2, heads=10, prompt=600, steps=60)
+    rep, r = run_and_check(w)
+    assert set(np.unique(r.choice).tolist()) == {1, 2, 3, 4, 5}, r.choice
+
+
+def test_adaptive_fp16_d64_and_short_prompt(decode_path):
+    w = dataclasses.replace(configs.scaled("llama65b_fastgen_profiled", batch=1, heads=5, prompt=40, steps=50),
+                            dtype="f16", head_dim=64)
+    run_and_check(w)
+
+
+def test_adaptive_fp32_with_prompt_out():
+    w = dataclasses.replace(configs.scaled("llama65b_fastgen_profiled", batch=1, heads=5, prompt=200, steps=30),
+                            dtype="f32")
+    run_and_check(w, prompt_out=True)
+
+
+@pytest.mark.parametrize("thr", [0.0, 2.0])
+def test_adaptive_threshold_extremes(thr, decode_path):
+    """Threshold 0: every unit takes the special-token composite; above 1:
+    every unit keeps the full cache."""
+    w = dataclasses.replace(configs.scaled("llama65b_fastgen_profiled", batch=1, heads=5, prompt=300, steps=40),
+                            profile_threshold=thr)
+    rep, r = run_and_check(w)
+    assert (r.choice == (1 if thr == 0.0 else 5)).all()

@@ -20,9 +20,9 @@ import dataclasses
 from dataclasses import dataclass, field
 from typing import Dict, List, Tuple
 
-FULL, H2O, LOCAL, SPECIAL, HASH, PERSIST = 0, 1, 2, 3, 4, 5
+FULL, H2O, LOCAL, SPECIAL, HASH, PERSIST, ADAPTIVE = 0, 1, 2, 3, 4, 5, 6
 POLICY_NAMES = {FULL: "full", H2O: "h2o", LOCAL: "local", SPECIAL: "special", HASH: "hash",
-                PERSIST: "persist"}
+                PERSIST: "persist", ADAPTIVE: "adaptive"}
 
 
 @dataclass(frozen=True)
@@ -36,14 +36,16 @@ class Workload:
     dtype: str                 # storage dtype of q/k/v: "f32" | "f16" | "bf16"
     prompt: int                # P
     steps: int                 # T decode steps
-    family: str                # "h2o" | "fastgen" | "hash" | "persist"
-    structure: str             # "dirs4" | "zipf_dir" | "clusters"
+    family: str                # "h2o" | "fastgen" | "hash" | "persist" | "adaptive"
+    structure: str             # "dirs4" | "zipf_dir" | "clusters" | "head_kinds"
     heavy: int = 0             # H2O heavy-hitter slots (family h2o)
     recent: int = 0            # H2O recent window (family h2o)
     local_window: int = 0      # FastGen LOCAL window W (also the FREQ+LOCAL recent part)
     freq_heavy: int = 0        # FastGen FREQ+LOCAL heavy part
     hash_budget: int = 0       # HashEvict budget B
     history_window: int = 0    # persistence heads: steps of pivotal history counted (1..64)
+    profile_rows: int = 0      # profiled heads: prompt rows the profile reads
+    profile_threshold: float = 0.0   # profiled heads: attention share a composite must recover
     sketch_bits: int = 32
     vocab: int = 32000
     special_ids: Tuple[int, ...] = (0, 1, 2, 3)
@@ -77,6 +79,8 @@ class Workload:
             return [H2O] * H, [self.heavy] * H, [self.recent] * H
         if self.family == "persist":
             return [PERSIST] * H, [self.heavy] * H, [self.recent] * H
+        if self.family == "adaptive":
+            return [ADAPTIVE] * H, [self.freq_heavy] * H, [self.local_window] * H
         if self.family == "hash":
             return [HASH] * H, [self.hash_budget] * H, [0] * H
         if self.family == "fastgen":
@@ -153,8 +157,16 @@ _add(Workload(
     description="OPT-30B-shaped decode under the persistence-count rule: 48 layers, batch 32, 56 heads, "
                 "d=128, bf16, P=2048, T=256, 20% budget (204 + 204), 64-step history"))
 
+_add(Workload(
+    name="llama65b_fastgen_profiled", index=7, layers=1, batch=8, heads=64, head_dim=128, dtype="bf16",
+    prompt=4096, steps=512, family="adaptive", structure="head_kinds", profile_rows=64,
+    profile_threshold=0.95, heavy_frac_positions=0.01, **_fastgen(4096),
+    description="Llama-65B-shaped FastGen with profiling: batch 8, 64 heads of five attention kinds, d=128, "
+                "bf16, P=4096, T=512; composites special / +punctuation / +409 frequent / +1024 local / full, "
+                "chosen per (sequence, head) at 95% recovered attention over the last 64 prompt rows"))
+
 ORDER = ["tiny_h2o", "opt6.7b_layer_h2o", "opt30b_decode_h2o", "llama65b_fastgen", "hashevict_lsh"]
-NEXT = ["opt30b_decode_persist"]
+NEXT = ["opt30b_decode_persist", "llama65b_fastgen_profiled"]
 
 
 def get(name: str) -> Workload:
@@ -172,7 +184,7 @@ def scaled(name: str, **over) -> Workload:
     derived: Dict[str, int] = {}
     if w.family in ("h2o", "persist") and w.name != "tiny_h2o":
         derived = _h2o20(P)
-    elif w.family == "fastgen":
+    elif w.family in ("fastgen", "adaptive"):
         derived = _fastgen(P)
     elif w.family == "hash":
         derived = _hash(P)

@@ -71,6 +71,53 @@ def _unit_dirs(gen, n: int, d: int, device) -> torch.Tensor:
     return u * (d ** 0.5) / u.norm(dim=-1, keepdim=True)
 
 
+def _zipf_ids(w: Workload, gen, Bt: int, N: int, device) -> torch.Tensor:
+    """Token ids [Bt, N]: Zipf(1.1) ranks over the vocabulary, id = rank - 1."""
+    ranks = torch.arange(1, w.vocab + 1, device=device, dtype=torch.float64) ** -1.1
+    return torch.multinomial(ranks.expand(Bt, -1), N, replacement=True, generator=gen).to(torch.int32)
+
+
+HEAD_KINDS = ("special", "punct", "local", "frequent", "broad")
+
+
+def head_kinds(w: Workload, layer: int = 0):
+    """Kind of each head of a layer under the "head_kinds" structure: a
+    balanced assignment of the five kinds, shuffled with a seed per layer."""
+    rng = np.random.default_rng([w.index, 11, layer])
+    base = [HEAD_KINDS[i % len(HEAD_KINDS)] for i in range(w.heads)]
+    return [base[i] for i in rng.permutation(w.heads)]
+
+
+def _add_head_kinds(w: Workload, gen, q, k, ids, n_pos: int, device, layer: int = 0) -> None:
+    """Per-head attention structures after the FastGen page's Figure 1: heads
+    drawn to special tokens, to special and punctuation tokens, to the recent
+    past, to a few frequently attended positions, or to everything."""
+    Bt, H, N, d = q.shape
+    dirs = _unit_dirs(gen, H, d, device)
+    special = torch.tensor(list(w.special_ids), device=device)
+    sp_punct = torch.tensor(list(w.special_ids) + list(w.punct_ids), device=device)
+    weights = (torch.arange(N, device=device, dtype=torch.float64) + 1.0) ** -1.1
+    pos_angle = 2.0 * np.pi * torch.arange(N, device=device, dtype=torch.float32) / (2.0 * N)
+    for h, kind in enumerate(head_kinds(w, layer)):
+        u = dirs[h]
+        if kind in ("special", "punct"):
+            keep = torch.isin(ids, special if kind == "special" else sp_punct)      # [Bt, N]
+            k[:, h] += 1.5 * keep.unsqueeze(-1).float() * u
+            q[:, h] += 0.5 * u
+        elif kind == "local":
+            # a slowly turning 2-d phase: q_i . k_j grows as |i - j| shrinks
+            amp = 11.0
+            k[:, h, :, 0] += amp * torch.cos(pos_angle)
+            k[:, h, :, 1] += amp * torch.sin(pos_angle)
+            q[:, h, :, 0] += amp * torch.cos(pos_angle)
+            q[:, h, :, 1] += amp * torch.sin(pos_angle)
+        elif kind == "frequent":
+            for b in range(Bt):
+                pos = torch.multinomial(weights, max(1, n_pos), replacement=False, generator=gen)
+                k[b, h, pos] += 1.5 * u
+            q[:, h] += 0.5 * u
+
+
 def generate_layer(w: Workload, layer: int = 0, device="cpu", seed: int = 0) -> LayerInputs:
     device = torch.device(device)
     gen = torch.Generator(device=device)
@@ -111,12 +158,13 @@ def generate_layer(w: Workload, layer: int = 0, device="cpu", seed: int = 0) -> 
             for b in range(Bt):
                 pos = torch.multinomial(weights, n_pos, replacement=False, generator=gen)
                 k[b, :, pos, :] += 3.0 * dirs.unsqueeze(1)
+        elif w.structure == "head_kinds":
+            ids = _zipf_ids(w, gen, Bt, N, device)
+            _add_head_kinds(w, gen, q, k, ids, n_pos, device)
         else:
             raise ValueError(w.structure)
-    if w.family == "fastgen":
-        ranks = torch.arange(1, w.vocab + 1, device=device, dtype=torch.float64) ** -1.1
-        ids = torch.multinomial(ranks.expand(Bt, -1), N, replacement=True,
-                                generator=gen).to(torch.int32)
+    if w.family == "fastgen" or (w.family == "adaptive" and ids is None):
+        ids = _zipf_ids(w, gen, Bt, N, device)
     if w.family == "hash":
         proj = torch.randn((d, w.sketch_bits), generator=gen, device=device,
                            dtype=torch.float32).to(torch.bfloat16)
