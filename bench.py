@@ -39,7 +39,7 @@ DEFAULT_WORKLOAD = "opt30b_decode_h2o"
 def _oracle_unit(args):
     """One unit through the float64 oracle (prefill + every decode step)."""
     import numpy as np
-    from oracle import fastgen, h2o, hashevict, persistence
+    from oracle import adaptive, fastgen, h2o, hashevict, persistence
     kind, Q, K, V, P, a, b, scale, extra = args
     Q, K, V = (np.asarray(x, dtype=np.float64) for x in (Q, K, V))
     t0 = time.perf_counter()
@@ -47,6 +47,9 @@ def _oracle_unit(args):
         h2o.run_unit(Q, K, V, P, a, b, scale)
     elif kind == "persist":
         persistence.run_unit(Q, K, V, P, a, b, extra, scale)
+    elif kind == "adaptive":
+        ids, special, punct, rows, thr = extra
+        adaptive.run_unit(Q, K, V, ids, P, special, punct, a, b, scale, rows, thr)
     elif kind == "hash":
         hashevict.run_unit(Q, K, V, np.asarray(extra, dtype=np.float64), P, a, scale)
     else:
@@ -77,6 +80,10 @@ def cpu_baseline(w, n_units: int, workers: int):
                 tasks.append(("h2o", Q, K, V, w.prompt, hv[h], rc[h], scale, None))
             elif w.family == "persist":
                 tasks.append(("persist", Q, K, V, w.prompt, hv[h], rc[h], scale, w.window_table(0)[h]))
+            elif w.family == "adaptive":
+                tasks.append(("adaptive", Q, K, V, w.prompt, hv[h], rc[h], scale,
+                              (unit_ids(inp, 0), list(w.special_ids), list(w.punct_ids), w.profile_rows,
+                               w.profile_threshold)))
             elif w.family == "hash":
                 tasks.append(("hash", Q, K, V, w.prompt, hv[h], 0, scale, inp.proj.float().numpy()))
             else:
@@ -103,6 +110,40 @@ def cpu_baseline(w, n_units: int, workers: int):
 
 
 # ---------------------------------------------------------------- GPU
+
+def adaptive_bytes_per_layer_step(w, ids, choice) -> float:
+    """As decode_bytes_per_layer_step for profiled units, from each unit's
+    chosen composite: special (1) or special + punctuation (2) ids kept so far;
+    frequent (3) / + local (4): the protected ids so far plus the unprotected
+    part up to its budget (score and position metadata per slot); full (5): t."""
+    import numpy as np
+    s = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    d = w.head_dim
+    io = 3 * d * s + 2 * d * s + 4 * d
+    P, T = w.prompt, w.steps
+    ids = np.asarray(ids)
+    sp = np.isin(ids, np.array(w.special_ids))
+    spp = np.isin(ids, np.array(list(w.special_ids) + list(w.punct_ids)))
+    before = lambda m: np.cumsum(m, axis=1) - m                       # counts strictly before t
+    sp_b, spp_b, free_b = before(sp), before(spp), before(~spp)
+    total = 0.0
+    for b in range(w.batch):
+        for h in range(w.heads):
+            k = int(choice[b, h])
+            for st in range(T):
+                t = P + st
+                if k == 1:
+                    n, meta = int(sp_b[b, t]), 0
+                elif k == 2:
+                    n, meta = int(spp_b[b, t]), 0
+                elif k in (3, 4):
+                    budget = w.freq_heavy + (w.local_window if k == 4 else 0)
+                    n, meta = int(spp_b[b, t]) + min(budget, int(free_b[b, t])), 12
+                else:
+                    n, meta = t, 0
+                total += n * d * s * 2 + n * meta + io
+    return total / T
+
 
 def decode_bytes_per_layer_step(w, ids=None) -> float:
     """Algorithmic bytes of one layer's decode step, averaged over the T steps:
@@ -182,7 +223,7 @@ def prefill_flops_per_layer(w, prompt_out: bool) -> float:
     rows twice (their row statistics, then their bits)."""
     pairs = w.prompt * (w.prompt + 1) / 2
     pol = w.policy_table(0)[0]
-    h2o_units = w.batch * sum(1 for p in pol if p == 1)
+    h2o_units = w.batch * sum(1 for p in pol if p in (1, 6))      # profiled heads need both passes too
     units = w.batch * w.heads
     per = 2.0 * w.head_dim * pairs
     persist = 0.0
@@ -225,6 +266,9 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
         kw.update(proj=inputs[0].proj)
     if 5 in pol:
         kw.update(history=np.tile(np.array(w.window_table(0), dtype=np.int32), w.layers))
+    if 6 in pol:
+        kw.update(special_ids=list(w.special_ids), punct_ids=list(w.punct_ids), vocab=w.vocab,
+                  profile_rows=w.profile_rows, profile_threshold=w.profile_threshold)
     kv = KVCache(w.layers, w.batch, w.heads, w.head_dim, w.context, inputs[0].prompt_q.dtype,
                  *tabs, device=dev, **kw)
     ids = [x.ids for x in inputs]
@@ -311,13 +355,14 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
         cold_us = 1e3 * sum(a.elapsed_time(b) for a, b in cold_samples) / (len(cold_samples) * w.layers)
         del fl
     ids0 = inputs[0].ids.cpu().numpy() if inputs[0].ids is not None else None
+    choice0 = kv.unit_policies(0).cpu().numpy() if 6 in pol else None
     group_ms = [a.elapsed_time(b) for a, b in samples]
     kernel_us = 1e3 * sum(group_ms) / (len(group_ms) * w.layers)
     return {"wall_s": wall, "gen_s": gen_s, "prefill_ms": prefill_ms, "decode_ms": decode_ms,
             "kernel_us": kernel_us, "n_samples": len(group_ms) * w.layers,
             "finite": bool(torch.isfinite(out).all().item()) and (pout is None or bool(torch.isfinite(pout).all().item())),
             "ids0": ids0,
-            "split": kv.capacity(0) > 1024, "cold_us": cold_us}
+            "split": kv.capacity(0) > 1024, "cold_us": cold_us, "choice0": choice0}
 
 
 def main():
@@ -354,7 +399,7 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         workers = min(16, len(os.sched_getaffinity(0)))
-        n_units = a.cpu_units or {"h2o": 256, "persist": 256, "fastgen": 64, "hash": 32}[w.family]
+        n_units = a.cpu_units or {"h2o": 256, "persist": 256, "fastgen": 64, "hash": 32, "adaptive": 32}[w.family]
         cpu = cpu_baseline(w, n_units, workers)
         print(f"[bench] cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
 
@@ -362,7 +407,10 @@ def main():
     pf_flops = prefill_flops_per_layer(w, a.prompt_out) * w.layers
     ms = 1e3 * r["wall_s"] / a.steps
     tokens = w.batch * w.steps
-    bytes_launch = decode_bytes_per_layer_step(w, r["ids0"])
+    if w.family == "adaptive":
+        bytes_launch = adaptive_bytes_per_layer_step(w, r["ids0"], r["choice0"])
+    else:
+        bytes_launch = decode_bytes_per_layer_step(w, r["ids0"])
     achieved = bytes_launch / (r["kernel_us"] * 1e-6) / 1e9
     kernel = ("decode_partial_kernel + decode_combine_kernel" if r["split"] else "decode_fused_kernel")
     if w.family == "hash":
@@ -378,7 +426,10 @@ def main():
                                          f"{w.freq_heavy} frequency + {w.local_window} local",
                               "hash": f"{w.hash_budget} slots, {w.sketch_bits}-bit sketches",
                               "persist": f"{w.heavy} heavy + {w.recent} recent by persistence count over "
-                                         f"{w.history_window} steps"}[w.family]},
+                                         f"{w.history_window} steps",
+                              "adaptive": f"profiled per (sequence, head): special / +punctuation / "
+                                          f"+{w.freq_heavy} frequent / +{w.local_window} local / full at "
+                                          f"{w.profile_threshold:.0%} of the last {w.profile_rows} rows' attention"}[w.family]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(w.name),
                      "kernel": kernel, "bytes_per_launch": bytes_launch,
@@ -387,6 +438,8 @@ def main():
         "detail": {"prefill_ms_per_step": r["prefill_ms"], "decode_ms_per_step": r["decode_ms"],
                    "decode_only_tokens_per_s": tokens / (r["decode_ms"] * 1e-3),
                    "prompt_out": a.prompt_out,
+                   "composites_chosen": ({str(k): int((r["choice0"] == k).sum()) for k in range(1, 6)}
+                                         if r["choice0"] is not None else None),
                    "prefill_algorithmic_tflops": pf_flops / (r["prefill_ms"] * 1e-3) / 1e12,
                    "prefill_frac_of_dense_16bit_mfma_peak": pf_flops / (r["prefill_ms"] * 1e-3) / 2.5e15,
                    "input_generation_s": r["gen_s"], "outputs_finite": r["finite"],
