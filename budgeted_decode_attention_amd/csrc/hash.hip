@@ -13,13 +13,27 @@
 // Ties in distance go to the oldest position.  The prompt is replayed: the
 // cache starts as positions [0, B) and each prompt position i >= B replaces
 // the farthest key from sketch(q_i).
+//
+// Sketch widths of 16, 32 and 64 bits (the page only asks for a projection
+// far narrower than the head dimension): one lane per bit, 32-bit words for
+// 16 and 32 bits, 64-bit words for 64.
 #include "common.hpp"
 
 namespace kve {
 namespace {
 
 constexpr int kNT = 256;
-constexpr int kMaxBits = 32;
+
+template <int BITS> struct SkWord { using T = uint32_t; };
+template <> struct SkWord<64> { using T = uint64_t; };
+__device__ inline int popcnt(uint32_t x) { return __popc(x); }
+__device__ inline int popcnt(uint64_t x) { return __popcll(x); }
+
+// The BITS-bit field of a wave ballot that starts at lane `first`.
+template <int BITS> __device__ inline typename SkWord<BITS>::T ballot_field(uint64_t m, int first) {
+  if constexpr (BITS == 64) return m;
+  else return (typename SkWord<BITS>::T)((m >> first) & ((1ull << BITS) - 1ull));
+}
 
 template <int DT> __device__ inline float load_elem(const char* row, int i);
 template <> __device__ inline float load_elem<F32>(const char* row, int i) {
@@ -80,63 +94,66 @@ __device__ inline int sketch_bit(const float* xs, const uint16_t* Ws, const char
   return exact_sign<DT, D>(row, W, bits, b);
 }
 
-// Copies the [D][32] bf16 projection into LDS (all threads of the workgroup).
-template <int D>
+// Copies the [D][BITS] bf16 projection into LDS (all threads of the workgroup).
+template <int D, int BITS>
 __device__ inline void stage_proj(uint16_t* Ws, const uint16_t* W) {
-  for (int i = threadIdx.x; i < D * kMaxBits / 8; i += kNT)
+  for (int i = threadIdx.x; i < D * BITS / 8; i += kNT)
     reinterpret_cast<uint4*>(Ws)[i] = reinterpret_cast<const uint4*>(W)[i];
 }
 
 constexpr int kSketchRows = 64;   // rows per workgroup in sketch_rows_kernel
 
 // Sketches of rows [row0, row0 + nrows) of each listed unit: a workgroup
-// stages the projection once and then covers kSketchRows rows, eight at a
-// time (one 32-lane half-wave per row; the lane index is the bit).
-template <int DT, int D>
+// stages the projection once and then covers kSketchRows rows, kNT / BITS at
+// a time (BITS lanes per row; the lane index within the row is the bit).
+template <int DT, int D, int BITS>
 __global__ __launch_bounds__(kNT) void sketch_rows_kernel(Shape sh, UnitList ul, const void* x, int P, int row0,
-                                                          int nrows, const uint16_t* proj, uint32_t* out) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[D * kMaxBits];
-  __shared__ float xs[kNT / 32][D];
+                                                          int nrows, const uint16_t* proj,
+                                                          typename SkWord<BITS>::T* out) {
+  constexpr int RPP = kNT / BITS;                            // rows per pass
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[D * BITS];
+  __shared__ float xs[RPP][D];
   constexpr int ES = elem_bytes<DT>();
   const int u = ul.ids ? ul.ids[blockIdx.y] : blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
-  const int half = lane >> 5;
-  const int b = lane & 31;
-  const int slot = threadIdx.x / 32;                       // row slot within a pass of 8 rows
-  stage_proj<D>(Ws, proj);
-  for (int pass = 0; pass < kSketchRows / (kNT / 32); ++pass) {
-    const int r = blockIdx.x * kSketchRows + pass * (kNT / 32) + slot;   // row index within [0, nrows)
+  const int b = lane % BITS;
+  const int slot = threadIdx.x / BITS;                       // row slot within a pass
+  stage_proj<D, BITS>(Ws, proj);
+  for (int pass = 0; pass < kSketchRows / RPP; ++pass) {
+    const int r = blockIdx.x * kSketchRows + pass * RPP + slot;   // row index within [0, nrows)
     const bool ok = r < nrows;
     const char* row = (const char*)x + ((size_t)u * P + row0 + (ok ? r : 0)) * D * ES;
     __syncthreads();                                        // previous pass done with xs; Ws staged
-    for (int i = b; i < D; i += 32) xs[slot][i] = ok ? load_elem<DT>(row, i) : 0.f;
+    for (int i = b; i < D; i += BITS) xs[slot][i] = ok ? load_elem<DT>(row, i) : 0.f;
     __syncthreads();
-    const int bit = ok ? sketch_bit<DT, D>(xs[slot], Ws, row, proj, kMaxBits, b) : 0;
+    const int bit = ok ? sketch_bit<DT, D>(xs[slot], Ws, row, proj, BITS, b) : 0;
     const uint64_t m = __ballot(bit != 0);
-    if (ok && b == 0) out[(size_t)u * P + row0 + r] = (uint32_t)(m >> (32 * half));
+    if (ok && b == 0) out[(size_t)u * P + row0 + r] = ballot_field<BITS>(m, lane);
   }
 }
 
 // Prompt replay for one HASH unit per workgroup; slot state in LDS.
-template <int DT, int D>
+template <int DT, int D, int BITS>
 __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c, UnitList ul, int P,
-                                                          const uint32_t* qsk, const uint32_t* ksk,
+                                                          const typename SkWord<BITS>::T* qsk,
+                                                          const typename SkWord<BITS>::T* ksk,
                                                           const void* k, const void* v) {
+  using SW = typename SkWord<BITS>::T;
   constexpr int EPL = St<DT>::EPL;
   constexpr int ES = elem_bytes<DT>();
   constexpr int LPR = D / EPL;
   constexpr int RPI = kNT / LPR;
-  extern __shared__ uint32_t lds[];          // sk[B] then pos[B]
+  extern __shared__ __attribute__((aligned(16))) char lds[];   // sk[B] then pos[B]
   __shared__ uint64_t kscr[kNT / kWave];
   const int u = ul.ids[blockIdx.x];
   const int tid = threadIdx.x;
   const HeadMeta m = c.meta[u];
   const int B = m.heavy;
   const int n0 = min(P, B);
-  uint32_t* ssk = lds;
-  int32_t* spos = reinterpret_cast<int32_t*>(lds + B);
-  const uint32_t* kq = ksk + (size_t)u * P;
-  const uint32_t* qq = qsk + (size_t)u * P;
+  SW* ssk = reinterpret_cast<SW*>(lds);
+  int32_t* spos = reinterpret_cast<int32_t*>(lds + (size_t)B * sizeof(SW));
+  const SW* kq = ksk + (size_t)u * P;
+  const SW* qq = qsk + (size_t)u * P;
   for (int s = tid; s < n0; s += kNT) {
     ssk[s] = kq[s];
     spos[s] = s;
@@ -145,10 +162,10 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
   // key = distance << 48 | (2^24 - 1 - position) << 24 | slot: the maximum is
   // the farthest key, then the oldest position
   for (int i = B; i < P; ++i) {
-    const uint32_t qs = qq[i];
+    const SW qs = qq[i];
     uint64_t best = 0;
     for (int s = tid; s < B; s += kNT) {
-      const uint64_t key = ((uint64_t)__popc(qs ^ ssk[s]) << 48) |
+      const uint64_t key = ((uint64_t)popcnt(qs ^ ssk[s]) << 48) |
                            ((uint64_t)(0xFFFFFF - spos[s]) << 24) | (uint64_t)s;
       best = key > best ? key : best;
     }
@@ -172,13 +189,13 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
   const size_t slot0 = (size_t)u * c.cap;
   for (int s = tid; s < c.cap; s += kNT) {
     int32_t p = -1;
-    uint32_t sk = 0u;
+    SW sk = 0;
     if (s < n0) {
       p = spos[s];
       sk = ssk[s];
     }
     c.pos[slot0 + s] = p;
-    c.sk[slot0 + s] = sk;
+    reinterpret_cast<SW*>(c.sk)[slot0 + s] = sk;
     c.S[slot0 + s] = 0.0;
   }
   if (tid == 0) c.count[u] = n0;
@@ -196,64 +213,70 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
 }
 
 // Decode-time replacement for one HASH unit per workgroup.
-template <int DT, int D>
+template <int DT, int D, int BITS>
 __global__ __launch_bounds__(kNT) void hash_evict_kernel(Shape sh, LayerCache c, UnitList ul, int t,
                                                          const void* q, const void* k, const void* v,
                                                          int32_t* evicted) {
+  using SW = typename SkWord<BITS>::T;
   constexpr int EPL = St<DT>::EPL;
   constexpr int ES = elem_bytes<DT>();
   constexpr int LPR = D / EPL;
-  __shared__ uint32_t sk2[2];
+  __shared__ SW sk2[2];
   __shared__ uint64_t kscr[kNT / kWave];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[D * kMaxBits];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[D * BITS];
   __shared__ float xs[2][D];
   const int u = ul.ids[blockIdx.x];
   const int tid = threadIdx.x;
   const HeadMeta m = c.meta[u];
   const int B = m.heavy;
-  stage_proj<D>(Ws, c.proj);
+  stage_proj<D, BITS>(Ws, c.proj);
   for (int i = tid; i < 2 * D; i += kNT)
     xs[i / D][i % D] = load_elem<DT>((const char*)(i < D ? q : k) + (size_t)u * D * ES, i % D);
   __syncthreads();
-  // wave 0: lanes 0-31 sketch q, lanes 32-63 sketch k
-  if (tid < kWave) {
-    const int half = tid >> 5;
-    const char* row = (const char*)(half ? k : q) + (size_t)u * D * ES;
-    const int bit = sketch_bit<DT, D>(xs[half], Ws, row, c.proj, kMaxBits, tid & 31);
+  // threads [0, BITS) sketch q, [BITS, 2 BITS) sketch k; one bit per lane
+  if (tid < 2 * BITS) {
+    const int r = tid / BITS, b = tid % BITS;
+    const char* row = (const char*)(r ? k : q) + (size_t)u * D * ES;
+    const int bit = sketch_bit<DT, D>(xs[r], Ws, row, c.proj, BITS, b);
     const uint64_t msk = __ballot(bit != 0);
-    if (tid == 0) {
-      sk2[0] = (uint32_t)msk;
-      sk2[1] = (uint32_t)(msk >> 32);
-    }
+    if (b == 0) sk2[r] = ballot_field<BITS>(msk, tid & (kWave - 1));
   }
   __syncthreads();
   const size_t slot0 = (size_t)u * c.cap;
   const int n = c.count[u];
   int slot, ev;
   if (n >= B) {
-    const uint32_t qs = sk2[0];
+    const SW qs = sk2[0];
     uint64_t best = 0;
-    // four slots per 16-byte load of sketches and of positions when the unit's
-    // first slot is 16-byte aligned (slot0 % 4 == 0); the remainder, or every
-    // slot otherwise, one at a time
-    const uint32_t* skp = c.sk + slot0;
+    // PER slots per 16-byte load of sketches (4 of 32 bits, 2 of 64) and the
+    // matching load of positions when the unit's first slot is aligned
+    // (slot0 % PER == 0); the remainder, or every slot otherwise, one at a time
+    constexpr int PER = 16 / (int)sizeof(SW);
+    const SW* skp = reinterpret_cast<const SW*>(c.sk) + slot0;
     const int32_t* psp = c.pos + slot0;
-    const bool vec = ((slot0 & 3) == 0);
-    const int n4 = vec ? (n & ~3) : 0;
-    for (int s4 = tid * 4; s4 < n4; s4 += kNT * 4) {
-      const uint4 a = *reinterpret_cast<const uint4*>(skp + s4);
-      const int4 p = *reinterpret_cast<const int4*>(psp + s4);
-      const uint32_t av[4] = {a.x, a.y, a.z, a.w};
-      const int32_t pv[4] = {p.x, p.y, p.z, p.w};
+    const bool vec = (slot0 % PER) == 0;
+    const int nv = vec ? (n / PER) * PER : 0;
+    for (int sv = tid * PER; sv < nv; sv += kNT * PER) {
+      const uint4 a = *reinterpret_cast<const uint4*>(skp + sv);
+      SW av[PER];
+      int32_t pv[PER];
+      __builtin_memcpy(av, &a, 16);
+      if constexpr (PER == 4) {
+        const int4 p = *reinterpret_cast<const int4*>(psp + sv);
+        pv[0] = p.x; pv[1] = p.y; pv[2] = p.z; pv[3] = p.w;
+      } else {
+        const int2 p = *reinterpret_cast<const int2*>(psp + sv);
+        pv[0] = p.x; pv[1] = p.y;
+      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint64_t key = ((uint64_t)__popc(qs ^ av[j]) << 48) | ((uint64_t)(0xFFFFFF - pv[j]) << 24) |
-                             (uint64_t)(s4 + j);
+      for (int j = 0; j < PER; ++j) {
+        const uint64_t key = ((uint64_t)popcnt(qs ^ av[j]) << 48) | ((uint64_t)(0xFFFFFF - pv[j]) << 24) |
+                             (uint64_t)(sv + j);
         best = key > best ? key : best;
       }
     }
-    for (int s = n4 + tid; s < n; s += kNT) {
-      const uint64_t key = ((uint64_t)__popc(qs ^ skp[s]) << 48) | ((uint64_t)(0xFFFFFF - psp[s]) << 24) |
+    for (int s = nv + tid; s < n; s += kNT) {
+      const uint64_t key = ((uint64_t)popcnt(qs ^ skp[s]) << 48) | ((uint64_t)(0xFFFFFF - psp[s]) << 24) |
                            (uint64_t)s;
       best = key > best ? key : best;
     }
@@ -282,71 +305,82 @@ __global__ __launch_bounds__(kNT) void hash_evict_kernel(Shape sh, LayerCache c,
   }
   if (tid == 0) {
     c.pos[slot0 + slot] = t;
-    c.sk[slot0 + slot] = sk2[1];
+    reinterpret_cast<SW*>(c.sk)[slot0 + slot] = sk2[1];
     c.S[slot0 + slot] = 0.0;
     if (slot == n) c.count[u] = n + 1;
     if (evicted) evicted[u] = ev;
   }
 }
 
-#define KVE_DISPATCH(FN, ...)                                                   \
+#define KVE_DISPATCH_D(FN, BITS, ...)                                           \
   switch (sh.dtype * 1000 + sh.d) {                                              \
-    case F32 * 1000 + 64: return FN<F32, 64>(__VA_ARGS__);                       \
-    case F32 * 1000 + 128: return FN<F32, 128>(__VA_ARGS__);                     \
-    case F16 * 1000 + 64: return FN<F16, 64>(__VA_ARGS__);                       \
-    case F16 * 1000 + 128: return FN<F16, 128>(__VA_ARGS__);                     \
-    case BF16 * 1000 + 64: return FN<BF16, 64>(__VA_ARGS__);                     \
-    case BF16 * 1000 + 128: return FN<BF16, 128>(__VA_ARGS__);                   \
+    case F32 * 1000 + 64: return FN<F32, 64, BITS>(__VA_ARGS__);                 \
+    case F32 * 1000 + 128: return FN<F32, 128, BITS>(__VA_ARGS__);               \
+    case F16 * 1000 + 64: return FN<F16, 64, BITS>(__VA_ARGS__);                 \
+    case F16 * 1000 + 128: return FN<F16, 128, BITS>(__VA_ARGS__);               \
+    case BF16 * 1000 + 64: return FN<BF16, 64, BITS>(__VA_ARGS__);               \
+    case BF16 * 1000 + 128: return FN<BF16, 128, BITS>(__VA_ARGS__);             \
   }                                                                              \
   return hipErrorInvalidValue;
 
-template <int DT, int D>
+#define KVE_DISPATCH(FN, BITS_RT, ...)                                          \
+  switch (BITS_RT) {                                                             \
+    case 16: { KVE_DISPATCH_D(FN, 16, __VA_ARGS__) }                             \
+    case 32: { KVE_DISPATCH_D(FN, 32, __VA_ARGS__) }                             \
+    case 64: { KVE_DISPATCH_D(FN, 64, __VA_ARGS__) }                             \
+  }                                                                              \
+  return hipErrorInvalidValue;
+
+template <int DT, int D, int BITS>
 hipError_t sketch_t(const Shape& sh, UnitList ul, const void* x, int P, int row0, int nrows,
-                    const uint16_t* proj, uint32_t* out, hipStream_t st) {
+                    const uint16_t* proj, void* out, hipStream_t st) {
   if (nrows <= 0 || ul.n <= 0) return hipSuccess;
   dim3 grid((nrows + kSketchRows - 1) / kSketchRows, ul.n);
-  hipLaunchKernelGGL((sketch_rows_kernel<DT, D>), grid, dim3(kNT), 0, st, sh, ul, x, P, row0, nrows, proj, out);
+  hipLaunchKernelGGL((sketch_rows_kernel<DT, D, BITS>), grid, dim3(kNT), 0, st, sh, ul, x, P, row0, nrows, proj,
+                     reinterpret_cast<typename SkWord<BITS>::T*>(out));
   return hipGetLastError();
 }
 
-template <int DT, int D>
-hipError_t replay_t(const Shape& sh, const LayerCache& c, UnitList ul, int P, const uint32_t* qsk,
-                    const uint32_t* ksk, const void* k, const void* v, int B, hipStream_t st) {
+template <int DT, int D, int BITS>
+hipError_t replay_t(const Shape& sh, const LayerCache& c, UnitList ul, int P, const void* qsk, const void* ksk,
+                    const void* k, const void* v, int B, hipStream_t st) {
+  using SW = typename SkWord<BITS>::T;
   if (ul.n <= 0) return hipSuccess;
-  const size_t lds = (size_t)B * 8;
+  const size_t lds = (size_t)B * (sizeof(SW) + 4);
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)hash_replay_kernel<DT, D>,
+    hipError_t e = hipFuncSetAttribute((const void*)hash_replay_kernel<DT, D, BITS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((hash_replay_kernel<DT, D>), dim3(ul.n), dim3(kNT), lds, st, sh, c, ul, P, qsk, ksk, k, v);
+  hipLaunchKernelGGL((hash_replay_kernel<DT, D, BITS>), dim3(ul.n), dim3(kNT), lds, st, sh, c, ul, P,
+                     reinterpret_cast<const SW*>(qsk), reinterpret_cast<const SW*>(ksk), k, v);
   return hipGetLastError();
 }
 
-template <int DT, int D>
+template <int DT, int D, int BITS>
 hipError_t evict_t(const Shape& sh, const LayerCache& c, UnitList ul, int t, const void* q, const void* k,
                    const void* v, int32_t* evicted, hipStream_t st) {
   if (ul.n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((hash_evict_kernel<DT, D>), dim3(ul.n), dim3(kNT), 0, st, sh, c, ul, t, q, k, v, evicted);
+  hipLaunchKernelGGL((hash_evict_kernel<DT, D, BITS>), dim3(ul.n), dim3(kNT), 0, st, sh, c, ul, t, q, k, v,
+                     evicted);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_sketch_rows(const Shape& sh, UnitList units, const void* x, int P, int row0, int nrows,
-                              const uint16_t* proj, uint32_t* out, hipStream_t st) {
-  KVE_DISPATCH(sketch_t, sh, units, x, P, row0, nrows, proj, out, st)
+                              const uint16_t* proj, int bits, void* out, hipStream_t st) {
+  KVE_DISPATCH(sketch_t, bits, sh, units, x, P, row0, nrows, proj, out, st)
 }
 
 hipError_t launch_hash_prefill(const Shape& sh, const LayerCache& c, UnitList units, int P, int max_budget,
-                               const uint32_t* qsk, const uint32_t* ksk, const void* k, const void* v,
-                               hipStream_t st) {
-  KVE_DISPATCH(replay_t, sh, c, units, P, qsk, ksk, k, v, max_budget, st)
+                               const void* qsk, const void* ksk, const void* k, const void* v, hipStream_t st) {
+  KVE_DISPATCH(replay_t, c.sk_bits, sh, c, units, P, qsk, ksk, k, v, max_budget, st)
 }
 
 hipError_t launch_hash_evict(const Shape& sh, const LayerCache& c, UnitList units, int t, const void* q,
                              const void* k, const void* v, int32_t* evicted, hipStream_t st) {
-  KVE_DISPATCH(evict_t, sh, c, units, t, q, k, v, evicted, st)
+  KVE_DISPATCH(evict_t, c.sk_bits, sh, c, units, t, q, k, v, evicted, st)
 }
 
 }  // namespace kve

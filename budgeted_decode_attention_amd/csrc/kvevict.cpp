@@ -46,7 +46,12 @@ constexpr int kMaxContext = 32768;     // LDS-resident per-unit slot lists
 constexpr int kSplitAbove = 1024;
 constexpr int kSplitChunkMixed = 256;
 constexpr size_t kMaxSplitLds = 150 * 1024;
-constexpr int kMaxHashBudget = 16384;  // replay keeps sketches and positions in LDS
+// The replay keeps every slot's sketch and position in LDS: 8 bytes per slot
+// with 16- and 32-bit sketches, 12 with 64-bit ones.
+constexpr int kMaxHashBudget = 16384;
+constexpr int kMaxHashBudget64 = 12288;
+
+int sketch_word_bytes(int bits) { return bits == 64 ? 8 : 4; }
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -152,9 +157,10 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
             return fail(KVE_EINVAL, "layer %d head %d: LOCAL needs heavy = 0 and 1 <= recent <= max_context", l, h);
           break;
         case KVE_HASH:
-          if (rc != 0 || hv < 1 || hv > std::min(c->max_context, kMaxHashBudget))
+          if (rc != 0 || hv < 1 ||
+              hv > std::min(c->max_context, c->sketch_bits == 64 ? kMaxHashBudget64 : kMaxHashBudget))
             return fail(KVE_EINVAL, "layer %d head %d: HASH needs recent = 0 and 1 <= budget <= %d", l, h,
-                        std::min(c->max_context, kMaxHashBudget));
+                        std::min(c->max_context, c->sketch_bits == 64 ? kMaxHashBudget64 : kMaxHashBudget));
           li.any_hash = true;
           li.max_hash_budget = std::max(li.max_hash_budget, hv);
           need_proj = true;
@@ -211,8 +217,8 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
   }
   if (need_bitmap && (!c->keep_token_bitmap || c->vocab < 1))
     return fail(KVE_EINVAL, "SPECIAL heads need keep_token_bitmap and vocab >= 1");
-  if (need_proj && (!c->lsh_proj_bf16 || c->sketch_bits != 32))
-    return fail(KVE_EUNSUPPORTED, "HASH heads need lsh_proj_bf16 and sketch_bits = 32");
+  if (need_proj && (!c->lsh_proj_bf16 || (c->sketch_bits != 16 && c->sketch_bits != 32 && c->sketch_bits != 64)))
+    return fail(KVE_EUNSUPPORTED, "HASH heads need lsh_proj_bf16 and sketch_bits of 16, 32 or 64");
   if (need_ids_tables) {
     if (!c->special_token_bitmap || !c->punct_token_bitmap || c->vocab < 1)
       return fail(KVE_EINVAL, "ADAPTIVE heads need special_token_bitmap, punct_token_bitmap and vocab >= 1");
@@ -256,8 +262,8 @@ struct kve_ctx {
   uint16_t* proj = nullptr;            // device [layers][d][32]
   float* lse = nullptr;                // device [U][max_context][2]
   double* colsum = nullptr;            // device [U][max_context]
-  uint32_t* qsk = nullptr;             // device [U][max_context]
-  uint32_t* ksk = nullptr;             // device [U][max_context]
+  void* qsk = nullptr;                 // device [U][max_context] sketch words
+  void* ksk = nullptr;
   bool sync_check = false;
 
   kve::IdSets sets() const { return {bitmap, special, punct, cfg.vocab}; }
@@ -283,11 +289,12 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
   auto* special = any_adaptive ? pl.take<uint32_t>(words) : nullptr;
   auto* punct = any_adaptive ? pl.take<uint32_t>(words) : nullptr;
   auto* mass = any_adaptive ? pl.take<double>(U * N) : nullptr;
-  auto* proj = any_hash ? pl.take<uint16_t>((size_t)c->layers * d * 32) : nullptr;
+  const size_t bits = c->sketch_bits, swb = sketch_word_bytes(c->sketch_bits);
+  auto* proj = any_hash ? pl.take<uint16_t>((size_t)c->layers * d * bits) : nullptr;
   auto* lse = pl.take<float>(U * N * 2);
   auto* colsum = pl.take<double>(U * N);
-  auto* qsk = any_hash ? pl.take<uint32_t>(U * N) : nullptr;
-  auto* ksk = any_hash ? pl.take<uint32_t>(U * N) : nullptr;
+  void* qsk = any_hash ? (void*)pl.take<char>(U * N * swb) : nullptr;
+  void* ksk = any_hash ? (void*)pl.take<char>(U * N * swb) : nullptr;
   // split-decode scratch, sized for the largest split layer
   size_t split_cap = 0, split_nch = 0;
   for (const auto& li : info)
@@ -317,11 +324,12 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
     lc.V = pl.take<char>(U * cap * d * es);
     lc.S = pl.take<double>(U * cap);
     lc.pos = pl.take<int32_t>(U * cap);
-    lc.sk = li.any_hash ? pl.take<uint32_t>(U * cap) : nullptr;
+    lc.sk = li.any_hash ? (void*)pl.take<char>(U * cap * swb) : nullptr;
+    lc.sk_bits = c->sketch_bits;
     lc.count = pl.take<int32_t>(U);
     lc.npcount = pl.take<int32_t>(U);
     lc.meta = meta ? meta + (size_t)l * U : nullptr;
-    lc.proj = proj ? proj + (size_t)l * d * 32 : nullptr;
+    lc.proj = proj ? proj + (size_t)l * d * bits : nullptr;
     lc.cap = (int32_t)cap;
     int32_t* h2o_ids = li.h2o_units.empty() ? nullptr : pl.take<int32_t>(li.h2o_units.size());
     int32_t* hash_ids = li.hash_units.empty() ? nullptr : pl.take<int32_t>(li.hash_units.size());
@@ -427,7 +435,7 @@ kve_status kvevict_create(const kve_config* cfg, void* d_workspace, size_t bytes
     s = dev(hipMemcpy(ctx->punct, cfg->punct_token_bitmap, ((size_t)cfg->vocab + 31) / 32 * 4,
                       hipMemcpyHostToDevice), "copy punctuation bitmap");
   if (s == KVE_OK && ctx->proj)
-    s = dev(hipMemcpy(ctx->proj, cfg->lsh_proj_bf16, (size_t)cfg->layers * cfg->head_dim * 32 * 2,
+    s = dev(hipMemcpy(ctx->proj, cfg->lsh_proj_bf16, (size_t)cfg->layers * cfg->head_dim * cfg->sketch_bits * 2,
                       hipMemcpyHostToDevice), "copy projection");
   for (int l = 0; l < cfg->layers && s == KVE_OK; ++l) {
     Layer& L = ctx->layers[l];
@@ -512,8 +520,9 @@ kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t P, const void* q
   if (e == hipSuccess)
     e = kve::launch_prefill_select(sh, L.cache, P, h->colsum, k, v, token_ids, h->sets(), st);
   if (e == hipSuccess && L.hash.n) {
-    e = kve::launch_sketch_rows(sh, L.hash, q, P, 0, P, L.cache.proj, h->qsk, st);
-    if (e == hipSuccess) e = kve::launch_sketch_rows(sh, L.hash, k, P, 0, P, L.cache.proj, h->ksk, st);
+    const int bits = h->cfg.sketch_bits;
+    e = kve::launch_sketch_rows(sh, L.hash, q, P, 0, P, L.cache.proj, bits, h->qsk, st);
+    if (e == hipSuccess) e = kve::launch_sketch_rows(sh, L.hash, k, P, 0, P, L.cache.proj, bits, h->ksk, st);
     if (e == hipSuccess)
       e = kve::launch_hash_prefill(sh, L.cache, L.hash, P, L.info.max_hash_budget, h->qsk, h->ksk, k, v, st);
   }

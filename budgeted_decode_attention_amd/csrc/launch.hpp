@@ -42,12 +42,14 @@ struct LayerCache {
   double* S;            // [U][cap] accumulated scores (H2O heads); the 64-bit
                         // pivotal histories in the same bytes (PERSIST heads)
   int32_t* pos;         // [U][cap] position per slot, -1 = empty
-  uint32_t* sk;         // [U][cap] key sketches (HASH heads), or null
+  void* sk;             // [U][cap] key sketches (HASH heads; 32-bit words for 16 and 32
+                        // sketch bits, 64-bit words for 64), or null
   int32_t* count;       // [U] occupied slots
   int32_t* npcount;     // [U] occupied slots holding unprotected tokens (H2O units with protected ids)
   HeadMeta* meta;       // [U] (written by the prefill for profiled units)
   const uint16_t* proj; // [d][bits] bf16 projection (HASH), or null
   int32_t cap;          // slot stride per unit
+  int32_t sk_bits;      // sketch width (HASH layers): 16, 32 or 64
 };
 
 struct Shape {
@@ -124,11 +126,11 @@ hipError_t launch_prefill_adaptive(const Shape& sh, const LayerCache& c, UnitLis
 // Packed sign sketches of `n` rows of x (row stride d) under proj, per unit
 // list, for rows [row0, row0 + nrows) of each unit's [P][d] block.
 hipError_t launch_sketch_rows(const Shape& sh, UnitList units, const void* x, int P, int row0,
-                              int nrows, const uint16_t* proj, uint32_t* out, hipStream_t st);
+                              int nrows, const uint16_t* proj, int bits, void* out, hipStream_t st);
 // Prompt replay for the listed HASH units; writes pos/sk/count, then gathers K/V.
 // `max_budget` is the largest HASH budget among the listed units (LDS size).
 hipError_t launch_hash_prefill(const Shape& sh, const LayerCache& c, UnitList units, int P,
-                               int max_budget, const uint32_t* qsk, const uint32_t* ksk,
+                               int max_budget, const void* qsk, const void* ksk,
                                const void* k, const void* v, hipStream_t st);
 // Decode: replacement before attention for the listed HASH units.
 hipError_t launch_hash_evict(const Shape& sh, const LayerCache& c, UnitList units, int t,

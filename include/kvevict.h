@@ -133,8 +133,9 @@ typedef struct {
   /* HASH heads only (else may be NULL/0): sketch width and the Gaussian
    * projection, host, one [head_dim][sketch_bits] row-major matrix per layer
    * of bfloat16 bit patterns.  Bit b of a sketch (b-th least significant) is
-   * set iff the exact value of sum_i W[i][b] x[i] is > 0. */
-  int32_t sketch_bits;                 /* 32 */
+   * set iff the exact value of sum_i W[i][b] x[i] is > 0.  The HASH budget is
+   * at most 16384 slots (12288 with 64-bit sketches). */
+  int32_t sketch_bits;                 /* 16, 32 or 64 */
   const uint16_t* lsh_proj_bf16;       /* [layers][head_dim][sketch_bits] */
   /* PERSIST heads only (else may be NULL): host [layers * heads] history
    * window in steps, 1..64; entries of other heads are ignored. */

@@ -34,7 +34,7 @@ from .attention import attend, causal_attention
 
 
 def sketches(X: np.ndarray, W: np.ndarray) -> np.ndarray:
-    """Packed sign sketches of the rows of X [n, d] under W [d, bits] (bits <= 63).
+    """Packed sign sketches of the rows of X [n, d] under W [d, bits] (bits <= 64).
 
     The sign is that of the exact dot product.  Entries are exact float64
     values (bf16 inputs: every product is exact).  A float64 dot of n terms

@@ -140,3 +140,19 @@ def test_adaptive_configs(over, status):
 def test_adaptive_needs_its_id_sets():
     c, keep = cfg(policy=[6, 1, 1], vocab=100, keep_ids=[0])
     assert status_of(c)[0] == binding.KVE_EINVAL
+
+
+@pytest.mark.parametrize("bits,budget,status", [(16, 50, binding.KVE_OK), (64, 50, binding.KVE_OK),
+                                                (48, 50, binding.KVE_EUNSUPPORTED)])
+def test_sketch_widths(bits, budget, status):
+    proj = torch.zeros((128, bits), dtype=torch.bfloat16)
+    c, keep = cfg(policy=[4, 1, 1], heavy=[budget, 10, 10], recent=[0, 5, 5], proj=proj)
+    assert status_of(c)[0] == status
+
+
+def test_64_bit_sketches_cap_the_budget():
+    proj = torch.zeros((128, 64), dtype=torch.bfloat16)
+    c, keep = cfg(policy=[4, 1, 1], heavy=[13000, 10, 10], recent=[0, 5, 5], proj=proj, max_context=20000)
+    assert status_of(c)[0] == binding.KVE_EINVAL
+    c, keep = cfg(policy=[4, 1, 1], heavy=[12288, 10, 10], recent=[0, 5, 5], proj=proj, max_context=20000)
+    assert status_of(c)[0] == binding.KVE_OK

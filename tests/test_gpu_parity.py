@@ -251,3 +251,15 @@ def test_adaptive_threshold_extremes(thr, decode_path):
                             profile_threshold=thr)
     rep, r = run_and_check(w)
     assert (r.choice == (1 if thr == 0.0 else 5)).all()
+
+
+@pytest.mark.parametrize("bits", [16, 64])
+def test_hash_sketch_widths(bits, decode_path):
+    """16- and 64-bit sketches (32 is the workload's width): bit-exact
+    decisions against the oracle, including a budget above a 64-bit word's
+    vector-load multiple and a unit stride that is not."""
+    w = dataclasses.replace(configs.scaled("hashevict_lsh", batch=2, heads=3, prompt=500, steps=70),
+                            sketch_bits=bits)
+    assert w.hash_budget == 250
+    rep, _ = run_and_check(w)
+    assert rep.decisions == 6 * 70

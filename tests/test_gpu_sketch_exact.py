@@ -8,6 +8,8 @@ CPU that naive signs would change the replay's decisions.  The logits of such
 keys are huge, so outputs are not compared; kept sets and evictions are.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -22,8 +24,8 @@ pytestmark = pytest.mark.gpu
 P, T, BUDGET = 160, 48, 64
 
 
-def crafted_inputs(seed=0):
-    w = configs.scaled("hashevict_lsh", batch=1, heads=2, prompt=P, steps=T)
+def crafted_inputs(seed=0, bits=32):
+    w = dataclasses.replace(configs.scaled("hashevict_lsh", batch=1, heads=2, prompt=P, steps=T), sketch_bits=bits)
     inp = generate_layer(w, 0, "cpu", seed)
     rng = np.random.default_rng(seed)
     proj = inp.proj.clone()
@@ -62,8 +64,9 @@ def naive_sketches(X, W):
     return out
 
 
-def test_cancelling_projections_take_the_exact_sign():
-    w, inp = crafted_inputs()
+@pytest.mark.parametrize("bits", [16, 32, 64])
+def test_cancelling_projections_take_the_exact_sign(bits):
+    w, inp = crafted_inputs(bits=bits)
     Wp = inp.proj.float().double().numpy()
     # the crafted rows really need the exact path, and it changes decisions
     Q, K, V = unit_sequence(inp, 0, 0)

@@ -60,15 +60,18 @@ def test_freq_local_keeps_window_and_budget():
 
 # ---------------------------------------------------------------- HashEvict
 
-def test_sketch_identity_projection_is_sign_bits():
-    """W = I (d = 32): bit b of the sketch is [x_b > 0]; bit 0 is the least significant."""
-    rng = np.random.default_rng(0)
-    X = rng.standard_normal((50, 32))
+@pytest.mark.parametrize("bits", [16, 32, 64])
+def test_sketch_identity_projection_is_sign_bits(bits):
+    """W = I (d = bits): bit b of the sketch is [x_b > 0]; bit 0 is the least significant."""
+    rng = np.random.default_rng(bits)
+    X = rng.standard_normal((50, bits))
     X[3, 5] = 0.0                        # sign(0) -> 0
-    sk = hashevict.sketches(X, np.eye(32))
+    X[4, bits - 1] = 1.0                 # the top bit set
+    sk = hashevict.sketches(X, np.eye(bits))
     for i in range(50):
-        exp = sum(1 << b for b in range(32) if X[i, b] > 0)
+        exp = sum(1 << b for b in range(bits) if X[i, b] > 0)
         assert int(sk[i]) == exp
+    assert int(sk[4]) >> (bits - 1) == 1
 
 
 def test_sketch_sign_is_exact_for_cancelling_sums():
