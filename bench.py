@@ -36,8 +36,30 @@ DEFAULT_WORKLOAD = "opt30b_decode_h2o"
 
 # ---------------------------------------------------------------- CPU baseline (oracle)
 
+def _hash_recovered_share(tr, Q, K, P: int, scale: float) -> float:
+    """Mean over decode steps of the share of the full causal softmax (keys
+    0..t) that lands on the HashEvict cache attended at step t -- the quality
+    side of the sketch-width trade-off.  Rebuilt from the oracle's eviction
+    log; not part of the timed oracle run."""
+    import numpy as np
+    cache = list(int(j) for j in tr.prefill_kept)
+    shares = []
+    for s_, t in enumerate(range(P, P + len(tr.evicted))):
+        e = int(tr.evicted[s_])
+        if e >= 0:
+            cache[cache.index(e)] = t
+        else:
+            cache.append(t)
+        lg = (K[: t + 1] @ Q[t]) * scale
+        p = np.exp(lg - lg.max())
+        p /= p.sum()
+        shares.append(float(p[np.array(cache)].sum()))
+    return float(np.mean(shares))
+
+
 def _oracle_unit(args):
-    """One unit through the float64 oracle (prefill + every decode step)."""
+    """One unit through the float64 oracle (prefill + every decode step).
+    Returns (seconds, extra) -- extra: the HashEvict cache's recovered share."""
     import numpy as np
     from oracle import adaptive, fastgen, h2o, hashevict, persistence
     kind, Q, K, V, P, a, b, scale, extra = args
@@ -51,11 +73,13 @@ def _oracle_unit(args):
         ids, special, punct, rows, thr = extra
         adaptive.run_unit(Q, K, V, ids, P, special, punct, a, b, scale, rows, thr)
     elif kind == "hash":
-        hashevict.run_unit(Q, K, V, np.asarray(extra, dtype=np.float64), P, a, scale)
+        tr = hashevict.run_unit(Q, K, V, np.asarray(extra, dtype=np.float64), P, a, scale)
+        dt = time.perf_counter() - t0
+        return dt, _hash_recovered_share(tr, Q, K, P, scale)
     else:
         pol, ids, keep = extra
         fastgen.run_unit(pol, Q, K, V, P, scale, heavy=a, recent=b, ids=ids, keep_ids=keep)
-    return time.perf_counter() - t0
+    return time.perf_counter() - t0, None
 
 
 def cpu_baseline(w, n_units: int, workers: int):
@@ -65,7 +89,8 @@ def cpu_baseline(w, n_units: int, workers: int):
     import numpy as np
     from workloads import configs
     from workloads.generate import generate_layer, unit_ids, unit_sequence
-    sample_w = configs.scaled(w.name, batch=1, heads=w.heads, prompt=w.prompt, steps=w.steps)
+    import dataclasses
+    sample_w = dataclasses.replace(w, batch=1)            # the workload's own shapes, one sequence
     pol, hv, rc = w.policy_table(0)
     tasks = []
     layer = 0
@@ -96,8 +121,10 @@ def cpu_baseline(w, n_units: int, workers: int):
     ctx = mp.get_context("spawn")
     t0 = time.perf_counter()
     with ctx.Pool(workers) as pool:
-        per = pool.map(_oracle_unit, tasks, chunksize=1)
+        res = pool.map(_oracle_unit, tasks, chunksize=1)
     wall = time.perf_counter() - t0
+    per = [r[0] for r in res]
+    extra = [r[1] for r in res if r[1] is not None]
     job_s = wall * w.units / len(tasks)
     tokens = w.batch * w.steps
     return {
@@ -106,6 +133,7 @@ def cpu_baseline(w, n_units: int, workers: int):
                   f"{workers} processes x 1 BLAS thread, wall {wall:.2f} s "
                   f"(mean {sum(per) / len(per):.3f} s per unit); job time scaled by units "
                   f"({job_s:.0f} s for the whole job)",
+        "hash_recovered_share": float(np.mean(extra)) if extra else None,
     }
 
 
@@ -167,7 +195,8 @@ def decode_bytes_per_layer_step(w, ids=None) -> float:
         return w.units_per_layer * (B * d * s * 2 + B * 20 + io)
     if w.family == "hash":
         B = w.hash_budget
-        return w.units_per_layer * (B * d * s * 2 + B * 8 + io + 4)
+        word = 8 if w.sketch_bits == 64 else 4                        # sketch word per slot
+        return w.units_per_layer * (B * d * s * 2 + B * (word + 4) + io + word)
     import numpy as np
     P, T = w.prompt, w.steps
     keep = np.isin(np.asarray(ids), np.array(w.keep_ids()))           # [batch, N]
@@ -381,6 +410,8 @@ def main():
                          "shape is unchanged); the printed line then describes that reduced job")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--sketch-bits", type=int, default=0,
+                    help="HashEvict workloads: sketch width 16, 32 or 64 (0: the workload's own, 32)")
     ap.add_argument("--prompt-out", action="store_true",
                     help="also produce the prompt attention output in every prefill")
     ap.add_argument("--sample-every", type=int, default=4,
@@ -395,6 +426,8 @@ def main():
     w = configs.get(a.workload)
     if a.layers:
         w = dataclasses.replace(w, layers=min(a.layers, w.layers))
+    if a.sketch_bits:
+        w = dataclasses.replace(w, sketch_bits=a.sketch_bits)
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -438,6 +471,8 @@ def main():
         "detail": {"prefill_ms_per_step": r["prefill_ms"], "decode_ms_per_step": r["decode_ms"],
                    "decode_only_tokens_per_s": tokens / (r["decode_ms"] * 1e-3),
                    "prompt_out": a.prompt_out,
+                   "sketch_bits": w.sketch_bits if w.family == "hash" else None,
+                   "hash_recovered_share": cpu.get("hash_recovered_share") if cpu else None,
                    "composites_chosen": ({str(k): int((r["choice0"] == k).sum()) for k in range(1, 6)}
                                          if r["choice0"] is not None else None),
                    "prefill_algorithmic_tflops": pf_flops / (r["prefill_ms"] * 1e-3) / 1e12,
