@@ -22,6 +22,11 @@ method:
 * ``persistence`` - the persistence-of-importance reading of [SH]: pivotal
                   bits (weight >= 1/|A|) over a history window, eviction of
                   the lowest count outside the recent window.
+* ``adaptive``  - FastGen's profiling step: the per-head composite chosen by
+                  recovered attention over the last prompt rows.
+* ``quant``     - the 4-bit cache format (groups of 32, float32 scale and
+                  rounding) that [SH] combines with eviction; the H2O and
+                  persistence loops take what a cache slot reads back.
 * ``lockstep``  - replays a unit against a GPU run's logs with the near-tie
                   acceptance band, and measures the score and output errors.
 
@@ -45,5 +50,7 @@ Parity unpinned: the H2O score trajectory for generic inputs beyond those
 invariants and brute-force checks -- the pages print no worked example; the
 persistence rule itself is a reading of a one-sentence hypothesis, so its
 pins (closed forms on constructed inputs, invariants, a replay of recorded
-weights) check the oracle against that reading, not against the page.
+weights) check the oracle against that reading, not against the page; the
+4-bit format is likewise a reading (the page names no format), pinned by
+exact grids, brute-force nearest grid points and the rounding bound.
 """

@@ -77,15 +77,21 @@ def prefill(Q: np.ndarray, K: np.ndarray, heavy: int, recent: int, scale: float)
 
 
 def attend_step(cache: Cache, t: int, q: np.ndarray, K_all: np.ndarray, V_all: np.ndarray,
-                scale: float):
+                scale: float, Kc: Optional[np.ndarray] = None, Vc: Optional[np.ndarray] = None):
     """Attention of the step-t query over the kept tokens plus token t itself.
 
     Returns (out [d], A, S_A): A = kept positions followed by t, and S_A the
     scores after this step's weights are added (S_t = its own weight).
-    The cache reads keys/values by position from the full sequences.
+    Kept tokens read what a cache slot holds (Kc / Vc, by position: the full
+    sequences unless the cache stores a lossy format); token t is the step's
+    own input, at full precision.
     """
     A = np.append(cache.pos, t).astype(np.int64)
-    p, out = attend(q, K_all[A], V_all[A], scale)
+    Kc = K_all if Kc is None else Kc
+    Vc = V_all if Vc is None else Vc
+    Ks = np.vstack([Kc[cache.pos], K_all[t:t + 1]])
+    Vs = np.vstack([Vc[cache.pos], V_all[t:t + 1]])
+    p, out = attend(q, Ks, Vs, scale)
     S_A = np.append(cache.S, 0.0) + p
     return out, A, S_A
 
@@ -123,8 +129,10 @@ class Trajectory:
 
 def run_unit(Q_all: np.ndarray, K_all: np.ndarray, V_all: np.ndarray, P: int,
              heavy: int, recent: int, scale: float, steps: Optional[int] = None,
-             want_prompt_out: bool = False) -> Trajectory:
-    """Prefill on the first P positions, then decode positions P..P+steps-1."""
+             want_prompt_out: bool = False, Kc: Optional[np.ndarray] = None,
+             Vc: Optional[np.ndarray] = None) -> Trajectory:
+    """Prefill on the first P positions, then decode positions P..P+steps-1.
+    Kc / Vc: what cache slots read back per position (lossy cache formats)."""
     N = Q_all.shape[0]
     T = N - P if steps is None else steps
     budget = heavy + recent
@@ -135,7 +143,7 @@ def run_unit(Q_all: np.ndarray, K_all: np.ndarray, V_all: np.ndarray, P: int,
         _, prompt_out = causal_attention(Q_all[:P], K_all[:P], V_all[:P], scale)
     outs, ev, evs = [], [], []
     for t in range(P, P + T):
-        o, A, S_A = attend_step(cache, t, Q_all[t], K_all, V_all, scale)
+        o, A, S_A = attend_step(cache, t, Q_all[t], K_all, V_all, scale, Kc, Vc)
         outs.append(o)
         if len(A) > budget:
             i = h2o_victim(A, S_A, t, recent)

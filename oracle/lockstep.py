@@ -168,8 +168,9 @@ def accept_h2o_victim(A: np.ndarray, S_A: np.ndarray, cand: np.ndarray, i_ref: i
 
 
 def check_h2o(Q, K, V, P: int, heavy: int, recent: int, scale: float, gpu: GpuUnit,
-              steps: Optional[int] = None) -> UnitReport:
-    """H2O family (also FastGen frequency+local heads)."""
+              steps: Optional[int] = None, Kc=None, Vc=None) -> UnitReport:
+    """H2O family (also FastGen frequency+local heads).  Kc / Vc: cache slot
+    contents per position for lossy cache formats."""
     rep = UnitReport()
     T = len(gpu.evicted) if steps is None else steps
     budget = heavy + recent
@@ -180,7 +181,7 @@ def check_h2o(Q, K, V, P: int, heavy: int, recent: int, scale: float, gpu: GpuUn
     cache = h2o.Cache(kept.copy(), c[kept].copy())
     for s in range(T):
         t = P + s
-        o, A, S_A = h2o.attend_step(cache, t, Q[t], K, V, scale)
+        o, A, S_A = h2o.attend_step(cache, t, Q[t], K, V, scale, Kc, Vc)
         _check_out(rep, s, gpu.out[s], o)
         g = int(gpu.evicted[s])
         if len(A) <= budget:
@@ -309,7 +310,7 @@ def _check_history_bits(rep: UnitReport, where: str, pos, gpu_bits, ref_pos, ref
 
 
 def check_persist(Q, K, V, P: int, heavy: int, recent: int, window: int, scale: float, gpu: GpuUnit,
-                  steps: Optional[int] = None) -> UnitReport:
+                  steps: Optional[int] = None, Kc=None, Vc=None) -> UnitReport:
     """Persistence-count eviction (Scissorhands reading)."""
     rep = UnitReport()
     T = len(gpu.evicted) if steps is None else steps
@@ -344,7 +345,7 @@ def check_persist(Q, K, V, P: int, heavy: int, recent: int, window: int, scale: 
     cache = persistence.Cache(kept, k_hist, k_amb)
     for s in range(T):
         t = P + s
-        o, A, hA, aA, _ = persistence.attend_step(cache, t, Q[t], K, V, scale, window)
+        o, A, hA, aA, _ = persistence.attend_step(cache, t, Q[t], K, V, scale, window, Kc, Vc)
         _check_out(rep, s, gpu.out[s], o)
         g = int(gpu.evicted[s])
         if len(A) <= budget:

@@ -99,11 +99,14 @@ def prefill(Q: np.ndarray, K: np.ndarray, heavy: int, recent: int, window: int, 
 
 
 def attend_step(cache: Cache, t: int, q: np.ndarray, K_all: np.ndarray, V_all: np.ndarray,
-                scale: float, window: int):
+                scale: float, window: int, Kc: Optional[np.ndarray] = None, Vc: Optional[np.ndarray] = None):
     """Attention of the step-t query over the kept tokens plus t; every history
-    shifts and takes this step's bit.  Returns (out, A, hist_A, amb_A, p)."""
+    shifts and takes this step's bit.  Returns (out, A, hist_A, amb_A, p).
+    Kept tokens read Kc / Vc (cache slot contents), token t its own input."""
     A = np.append(cache.pos, t).astype(np.int64)
-    p, out = attend(q, K_all[A], V_all[A], scale)
+    Kc = K_all if Kc is None else Kc
+    Vc = V_all if Vc is None else Vc
+    p, out = attend(q, np.vstack([Kc[cache.pos], K_all[t:t + 1]]), np.vstack([Vc[cache.pos], V_all[t:t + 1]]), scale)
     bits, near = pivotal(p, len(A))
     wm = np.uint64(window_mask(window))
     one = np.uint64(1)
@@ -146,7 +149,7 @@ class Trajectory:
 
 def run_unit(Q_all: np.ndarray, K_all: np.ndarray, V_all: np.ndarray, P: int, heavy: int, recent: int,
              window: int, scale: float, steps: Optional[int] = None, want_prompt_out: bool = False,
-             record: bool = False) -> Trajectory:
+             record: bool = False, Kc: Optional[np.ndarray] = None, Vc: Optional[np.ndarray] = None) -> Trajectory:
     """Prefill on the first P positions, then decode positions P..P+steps-1."""
     N = Q_all.shape[0]
     T = N - P if steps is None else steps
@@ -156,7 +159,7 @@ def run_unit(Q_all: np.ndarray, K_all: np.ndarray, V_all: np.ndarray, P: int, he
     prompt_out = causal_attention(Q_all[:P], K_all[:P], V_all[:P], scale)[1] if want_prompt_out else None
     outs, ev, rec = [], [], []
     for t in range(P, P + T):
-        o, A, h, a, p = attend_step(cache, t, Q_all[t], K_all, V_all, scale, window)
+        o, A, h, a, p = attend_step(cache, t, Q_all[t], K_all, V_all, scale, window, Kc, Vc)
         outs.append(o)
         if record:
             rec.append((A.copy(), p.copy()))

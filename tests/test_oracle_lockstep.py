@@ -235,3 +235,24 @@ def test_adaptive_checker_accepts_oracle_and_rejects_mistakes():
     # and C4 is then accepted (adopted) as within the recovery band
     rep = lockstep.check_adaptive(Q, K, V, ids, P, [0], [1, 2], hh, rc, 0.5, R, T4 + 1e-7, adaptive_gpu_unit(trl), 4)
     assert rep.adopted == 1 and not any("profile" in f for f in rep.failures)
+
+
+def test_checkers_follow_the_cache_copy():
+    """With a lossy cache copy (4-bit rows) the checkers accept the run made from
+    that copy and reject the full-precision run, whose outputs differ."""
+    from oracle import persistence, quant
+    rng = np.random.default_rng(21)
+    P, T, d, hh, r, w = 40, 20, 32, 6, 6, 16
+    Q, K, V = (rng.standard_normal((P + T, d)) for _ in range(3))
+    Kc, Vc = quant.roundtrip(K), quant.roundtrip(V)
+    tq = h2o.run_unit(Q, K, V, P, hh, r, 0.3, Kc=Kc, Vc=Vc)
+    tf = h2o.run_unit(Q, K, V, P, hh, r, 0.3)
+    for tr, ok in ((tq, True), (tf, False)):
+        g = lockstep.GpuUnit(prefill_pos=tr.prefill_kept.copy(), evicted=tr.evicted.copy(),
+                             out=tr.out.copy(), final_pos=tr.final.pos.copy(),
+                             prefill_S=tr.prefill_scores.copy(), final_S=tr.final.S.copy())
+        assert lockstep.check_h2o(Q, K, V, P, hh, r, 0.3, g, Kc=Kc, Vc=Vc).ok == ok
+    pq = persistence.run_unit(Q, K, V, P, hh, r, w, 0.3, Kc=Kc, Vc=Vc)
+    pf = persistence.run_unit(Q, K, V, P, hh, r, w, 0.3)
+    assert lockstep.check_persist(Q, K, V, P, hh, r, w, 0.3, persist_gpu_unit(pq, P), Kc=Kc, Vc=Vc).ok
+    assert not lockstep.check_persist(Q, K, V, P, hh, r, w, 0.3, persist_gpu_unit(pf, P), Kc=Kc, Vc=Vc).ok
