@@ -57,14 +57,29 @@ def _hash_recovered_share(tr, Q, K, P: int, scale: float) -> float:
     return float(np.mean(shares))
 
 
+def _q4_output_error(tr_q4, Q, K, V, P: int, a: int, b: int, scale: float) -> float:
+    """Mean over decode steps of ||o_4bit - o|| / ||o||: the same unit with
+    cache rows in the storage dtype gives o.  Not part of the timed oracle run."""
+    import numpy as np
+    from oracle import h2o
+    ref = h2o.run_unit(Q, K, V, P, a, b, scale).out
+    return float(np.mean(np.linalg.norm(tr_q4.out - ref, axis=1) / np.linalg.norm(ref, axis=1)))
+
+
 def _oracle_unit(args):
     """One unit through the float64 oracle (prefill + every decode step).
-    Returns (seconds, extra) -- extra: the HashEvict cache's recovered share."""
+    Returns (seconds, extra) -- extra: the HashEvict cache's recovered share,
+    or for 4-bit slots (on the units asked for) the output error against the
+    storage-dtype cache."""
     import numpy as np
-    from oracle import adaptive, fastgen, h2o, hashevict, persistence
+    from oracle import adaptive, fastgen, h2o, hashevict, persistence, quant
     kind, Q, K, V, P, a, b, scale, extra = args
     Q, K, V = (np.asarray(x, dtype=np.float64) for x in (Q, K, V))
     t0 = time.perf_counter()
+    if kind == "h2o_q4":
+        tr = h2o.run_unit(Q, K, V, P, a, b, scale, Kc=quant.roundtrip(K), Vc=quant.roundtrip(V))
+        dt = time.perf_counter() - t0
+        return dt, (_q4_output_error(tr, Q, K, V, P, a, b, scale) if extra else None)
     if kind == "h2o":
         h2o.run_unit(Q, K, V, P, a, b, scale)
     elif kind == "persist":
@@ -101,7 +116,9 @@ def cpu_baseline(w, n_units: int, workers: int):
             if len(tasks) >= n_units:
                 break
             Q, K, V = (x.astype(np.float32) for x in unit_sequence(inp, 0, h))
-            if w.family == "h2o":
+            if w.family == "h2o" and w.cache_bits == 4:
+                tasks.append(("h2o_q4", Q, K, V, w.prompt, hv[h], rc[h], scale, len(tasks) < 16))
+            elif w.family == "h2o":
                 tasks.append(("h2o", Q, K, V, w.prompt, hv[h], rc[h], scale, None))
             elif w.family == "persist":
                 tasks.append(("persist", Q, K, V, w.prompt, hv[h], rc[h], scale, w.window_table(0)[h]))
@@ -133,7 +150,9 @@ def cpu_baseline(w, n_units: int, workers: int):
                   f"{workers} processes x 1 BLAS thread, wall {wall:.2f} s "
                   f"(mean {sum(per) / len(per):.3f} s per unit); job time scaled by units "
                   f"({job_s:.0f} s for the whole job)",
-        "hash_recovered_share": float(np.mean(extra)) if extra else None,
+        "hash_recovered_share": float(np.mean(extra)) if extra and w.family == "hash" else None,
+        "q4_output_rel_err": float(np.mean(extra)) if extra and w.cache_bits == 4 else None,
+        "q4_units": len(extra) if w.cache_bits == 4 else 0,
     }
 
 
@@ -175,7 +194,8 @@ def adaptive_bytes_per_layer_step(w, ids, choice) -> float:
 
 def decode_bytes_per_layer_step(w, ids=None) -> float:
     """Algorithmic bytes of one layer's decode step, averaged over the T steps:
-    per unit, the kept K and V rows read (n slots x d x s x 2), the per-slot
+    per unit, the kept K and V rows read (n slots x d x s x 2; 4-bit slots:
+    d / 2 code bytes and d / 32 float32 scales per row), the per-slot
     metadata the policy needs (H2O: score read and write at the 4-byte float32
     minimum plus the position, 12 B; persistence counts: the 64-bit history
     read and written plus the position, 20 B; HashEvict: sketch and position, 8 B), the
@@ -185,14 +205,15 @@ def decode_bytes_per_layer_step(w, ids=None) -> float:
     earlier positions whose id is kept (counted from the ids)."""
     s = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
     d = w.head_dim
-    io = 3 * d * s + 2 * d * s + 4 * d
+    row = d // 2 + 4 * (d // 32) if w.cache_bits == 4 else d * s    # bytes of one cached row
+    io = 3 * d * s + 2 * row + 4 * d
     pol, hv, rc = w.policy_table(0)
     if w.family == "h2o":
         B = w.heavy + w.recent
-        return w.units_per_layer * (B * d * s * 2 + B * 12 + io)
+        return w.units_per_layer * (B * row * 2 + B * 12 + io)
     if w.family == "persist":
         B = w.heavy + w.recent
-        return w.units_per_layer * (B * d * s * 2 + B * 20 + io)
+        return w.units_per_layer * (B * row * 2 + B * 20 + io)
     if w.family == "hash":
         B = w.hash_budget
         word = 8 if w.sketch_bits == 64 else 4                        # sketch word per slot
@@ -299,7 +320,7 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
         kw.update(special_ids=list(w.special_ids), punct_ids=list(w.punct_ids), vocab=w.vocab,
                   profile_rows=w.profile_rows, profile_threshold=w.profile_threshold)
     kv = KVCache(w.layers, w.batch, w.heads, w.head_dim, w.context, inputs[0].prompt_q.dtype,
-                 *tabs, device=dev, **kw)
+                 *tabs, cache_bits=w.cache_bits, device=dev, **kw)
     ids = [x.ids for x in inputs]
     pids = [x[:, :w.prompt].contiguous() if x is not None else None for x in ids]
     dids = [[x[:, w.prompt + s].contiguous() for s in range(w.steps)] if x is not None else None for x in ids]
@@ -454,6 +475,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "batch": w.batch, "heads": w.heads,
                    "head_dim": w.head_dim, "prompt": w.prompt, "decode_steps": w.steps,
+                   "cached_kv": "4-bit slots (groups of 32, float32 scale)" if w.cache_bits == 4 else w.dtype,
                    "budget": {"h2o": f"{w.heavy} heavy + {w.recent} recent",
                               "fastgen": f"per head: full / local {w.local_window} / special+punct / "
                                          f"{w.freq_heavy} frequency + {w.local_window} local",
@@ -473,6 +495,8 @@ def main():
                    "prompt_out": a.prompt_out,
                    "sketch_bits": w.sketch_bits if w.family == "hash" else None,
                    "hash_recovered_share": cpu.get("hash_recovered_share") if cpu else None,
+                   "q4_output_rel_err_vs_storage_dtype_cache": cpu.get("q4_output_rel_err") if cpu else None,
+                   "q4_error_units": cpu.get("q4_units") if cpu else None,
                    "composites_chosen": ({str(k): int((r["choice0"] == k).sum()) for k in range(1, 6)}
                                          if r["choice0"] is not None else None),
                    "prefill_algorithmic_tflops": pf_flops / (r["prefill_ms"] * 1e-3) / 1e12,

@@ -26,8 +26,8 @@ DTYPE_CODES = {torch.float32: KVE_F32, torch.float16: KVE_F16, torch.bfloat16: K
 CODE_DTYPES = {v: k for k, v in DTYPE_CODES.items()}
 
 EXPORTED = ("kvevict_workspace_size", "kvevict_create", "kvevict_destroy", "kvevict_prefill",
-            "kvevict_decode_step", "kvevict_kept_indices", "kvevict_unit_policies", "kvevict_capacity",
-            "kvevict_position", "kvevict_status_string", "kvevict_last_error")
+            "kvevict_decode_step", "kvevict_kept_indices", "kvevict_unit_policies", "kvevict_cache_rows",
+            "kvevict_capacity", "kvevict_position", "kvevict_status_string", "kvevict_last_error")
 
 
 class KVEvictError(RuntimeError):
@@ -49,6 +49,7 @@ class kve_config(ctypes.Structure):
         ("special_token_bitmap", ctypes.POINTER(ctypes.c_uint32)),
         ("punct_token_bitmap", ctypes.POINTER(ctypes.c_uint32)),
         ("profile_rows", ctypes.c_int32), ("profile_threshold", ctypes.c_float),
+        ("cache_bits", ctypes.c_int32),
     ]
 
 
@@ -73,6 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvevict_decode_step": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
         "kvevict_kept_indices": (i32, [vp, i32, vp, vp, vp, vp]),
         "kvevict_unit_policies": (i32, [vp, i32, vp, vp]),
+        "kvevict_cache_rows": (i32, [vp, i32, vp, vp, vp, vp, vp]),
         "kvevict_capacity": (i32, [vp, i32]),
         "kvevict_position": (i32, [vp, i32]),
         "kvevict_status_string": (ctypes.c_char_p, [i32]),
@@ -116,11 +118,12 @@ def make_config(layers: int, batch: int, heads: int, head_dim: int, max_context:
                 policy, heavy, recent, softmax_scale: float = 0.0, keep_ids: Sequence[int] = (),
                 vocab: int = 0, proj: Optional[torch.Tensor] = None, history=None,
                 special_ids: Optional[Sequence[int]] = None, punct_ids: Optional[Sequence[int]] = None,
-                profile_rows: int = 0, profile_threshold: float = 0.0):
+                profile_rows: int = 0, profile_threshold: float = 0.0, cache_bits: int = 0):
     """Returns (kve_config, keepalive) -- keepalive holds the host tables.
 
     history: per-head history windows [layers * heads] (PERSIST heads), or None.
     special_ids, punct_ids, profile_rows, profile_threshold: ADAPTIVE heads.
+    cache_bits: 0 (rows in the storage dtype) or 4 (4-bit slots).
     """
     pol = np.ascontiguousarray(np.asarray(policy, dtype=np.int32).reshape(-1))
     hv = np.ascontiguousarray(np.asarray(heavy, dtype=np.int32).reshape(-1))
@@ -132,6 +135,7 @@ def make_config(layers: int, batch: int, heads: int, head_dim: int, max_context:
     cfg.policy = pol.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     cfg.heavy = hv.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     cfg.recent = rc.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    cfg.cache_bits = cache_bits
     if vocab:
         bm = keep_bitmap(keep_ids, vocab)
         keep.append(bm)
@@ -202,6 +206,11 @@ def kvevict_unit_policies(h, layer: int, choice_out, stream=None) -> None:
            "kvevict_unit_policies")
 
 
+def kvevict_cache_rows(h, layer: int, k_out, v_out, k_scale_out=None, v_scale_out=None, stream=None) -> None:
+    _check(load_library().kvevict_cache_rows(h, layer, _ptr(k_out), _ptr(v_out), _ptr(k_scale_out),
+                                             _ptr(v_scale_out), _stream(stream)), "kvevict_cache_rows")
+
+
 def kvevict_capacity(h, layer: int) -> int:
     return int(load_library().kvevict_capacity(h, layer))
 
@@ -223,7 +232,7 @@ class KVCache:
                  dtype: torch.dtype, policy, heavy, recent, softmax_scale: float = 0.0,
                  keep_ids: Sequence[int] = (), vocab: int = 0, proj: Optional[torch.Tensor] = None,
                  history=None, special_ids=None, punct_ids=None, profile_rows: int = 0,
-                 profile_threshold: float = 0.0, device="cuda"):
+                 profile_threshold: float = 0.0, cache_bits: int = 0, device="cuda"):
         self.layers, self.batch, self.heads, self.head_dim = layers, batch, heads, head_dim
         dev = torch.device(device)
         if dev.type == "cuda" and dev.index is None:
@@ -231,7 +240,8 @@ class KVCache:
         self.max_context, self.dtype, self.device = max_context, dtype, dev
         self.cfg, self._keep = make_config(layers, batch, heads, head_dim, max_context, dtype, policy, heavy,
                                            recent, softmax_scale, keep_ids, vocab, proj, history, special_ids,
-                                           punct_ids, profile_rows, profile_threshold)
+                                           punct_ids, profile_rows, profile_threshold, cache_bits)
+        self.cache_bits = cache_bits
         self.workspace_bytes = kvevict_workspace_size(self.cfg)
         self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
         self.handle = kvevict_create(self.cfg, self.workspace)
@@ -285,6 +295,25 @@ class KVCache:
         out = torch.empty((self.batch, self.heads), dtype=torch.int32, device=self.device)
         kvevict_unit_policies(self.handle, layer, out, stream)
         return out
+
+    def cache_rows(self, layer: int, stream=None):
+        """Slot contents of one layer: (k, v, k_scale, v_scale).  Rows in the
+        storage dtype [batch, heads, cap, d] with null scales, or for 4-bit
+        slots uint8 codes [batch, heads, cap, d / 2] (element 2b in the low
+        nibble of byte b, stored as code + 8) and float32 scales
+        [batch, heads, cap, d / 32]."""
+        cap, d = self.capacity(layer), self.head_dim
+        if self.cache_bits == 4:
+            k = torch.empty((self.batch, self.heads, cap, d // 2), dtype=torch.uint8, device=self.device)
+            v = torch.empty_like(k)
+            ks = torch.empty((self.batch, self.heads, cap, d // 32), dtype=torch.float32, device=self.device)
+            vs = torch.empty_like(ks)
+        else:
+            k = torch.empty((self.batch, self.heads, cap, d), dtype=self.dtype, device=self.device)
+            v = torch.empty_like(k)
+            ks = vs = None
+        kvevict_cache_rows(self.handle, layer, k, v, ks, vs, stream)
+        return k, v, ks, vs
 
     def kept_indices(self, layer: int, with_scores: bool = True, stream=None):
         cap = self.capacity(layer)

@@ -54,7 +54,7 @@ __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uin
 __device__ inline void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // ---------------------------------------------------------------- lane-group sums
-// Sum over aligned groups of G lanes (G in {4, 8, 16, 32}); every lane of the
+// Sum over aligned groups of G lanes (G in {2, 4, 8, 16, 32}); every lane of the
 // group receives the group's sum.  Within a 16-lane row the partners come from
 // DPP permutations (quad swaps, then the half-row and row mirrors), which pair
 // each lane with one holding the other half of the partial sums at each step.
@@ -63,9 +63,9 @@ template <int CTRL> __device__ inline float dpp_add(float v) {
 }
 
 template <int G> __device__ inline float group_sum(float v) {
-  static_assert(G == 4 || G == 8 || G == 16 || G == 32, "group size");
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16 || G == 32, "group size");
   v = dpp_add<0xB1>(v);        // quad_perm [1,0,3,2]
-  v = dpp_add<0x4E>(v);        // quad_perm [2,3,0,1]
+  if constexpr (G >= 4) v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
   if constexpr (G >= 8) v = dpp_add<0x141>(v);   // row_half_mirror
   if constexpr (G >= 16) v = dpp_add<0x140>(v);  // row_mirror
   if constexpr (G >= 32) v += __shfl_xor(v, 16);

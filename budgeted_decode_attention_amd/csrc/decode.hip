@@ -21,7 +21,16 @@
 //             `combine`, one workgroup per unit, merges the chunks under the
 //             global maximum and runs the same policy step, recomputing the
 //             exact weights from the logits for the float64 score update.
+//
+// 4-bit slots (Q4 instantiations): one lane owns half a group, 16 elements of
+// a row (d / 16 lanes per row, one 8-byte code load and its group's scale per
+// lane, the register budget of the 16-bit kernels, so every workgroup of a
+// layer stays resident); the dot uses the stored nibbles c + 8 and subtracts
+// 8 * (sum of the lane's query elements) once per row, the value pass
+// accumulates w * scale * (c + 8) and subtracts 8 * sum(w * scale) at the end.  Token t's own key and
+// value are read from the inputs at full precision and quantised into its slot.
 #include "common.hpp"
+#include "q4.hpp"
 
 namespace kve {
 namespace {
@@ -42,8 +51,13 @@ namespace {
 constexpr int kNT = 256;
 constexpr int kUnroll = KVE_DECODE_UNROLL;
 
+#ifndef KVE_DECODE_WAVES_PER_EU_Q4
+#define KVE_DECODE_WAVES_PER_EU_Q4 8
+#endif
 #if KVE_DECODE_WAVES_PER_EU > 0
-#define KVE_DECODE_ATTR __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(KVE_DECODE_WAVES_PER_EU)))
+#define KVE_DECODE_ATTR                  \
+  __launch_bounds__(kNT) __attribute__( \
+      (amdgpu_waves_per_eu(Q4 ? KVE_DECODE_WAVES_PER_EU_Q4 : KVE_DECODE_WAVES_PER_EU)))
 #else
 #define KVE_DECODE_ATTR __launch_bounds__(kNT)
 #endif
@@ -65,6 +79,25 @@ template <int DT, int D> struct Rows {
   static constexpr int LPR = D / EPL;
   static constexpr int RPI = kNT / LPR;
   static_assert(LPR >= 4 && LPR <= 32 && kNT % LPR == 0, "row layout");
+};
+
+// 4-bit rows: half a group (16 elements, 8 code bytes) per lane; lanes 2g
+// and 2g + 1 of a row share group g's scale.
+template <int D> struct Q4Rows {
+  static constexpr int EPL = kQGroup / 2;
+  static constexpr int LPR = D / EPL;         // 4 (d 64) or 8 (d 128)
+  static constexpr int RPI = kNT / LPR;
+  static constexpr int CB = D / 2;            // code bytes per row
+  static constexpr int G = D / kQGroup;       // scales per row
+  static constexpr int RED = kNT / 16;        // row groups left after the in-row fold
+  static_assert(LPR == 4 || LPR == 8, "row layout");
+};
+
+// Lane layout of the query and of the output columns for one slot format.
+template <int DT, int D, bool Q4> struct Lay {
+  static constexpr int EPL = Q4 ? Q4Rows<D>::EPL : Rows<DT, D>::EPL;
+  static constexpr int LPR = D / EPL;
+  static constexpr int NRED = Q4 ? Q4Rows<D>::RED : Rows<DT, D>::RPI;   // partial-output rows in LDS
 };
 
 // Logits scale * q.k_r for rows [r0, r1) into lg[r - r0] (LDS) and, when
@@ -123,17 +156,130 @@ __device__ inline void row_values(const char* Vb, const float* w, int r0, int r1
 }
 
 // Dot of q with one input row of unit u, held by row group 0 (threads
-// [0, LPR)); every lane of the group receives the value.
-template <int DT, int D>
+// [0, D / EPL)), each lane holding EPL elements; every lane of the group
+// receives the value.
+template <int DT, int D, int EPL = St<DT>::EPL>
 __device__ inline float group0_dot(const float* qf, const void* rows, int u) {
-  using R = Rows<DT, D>;
-  const int col = threadIdx.x % R::LPR;
-  float f[R::EPL];
-  St<DT>::unpack(ld16((const char*)rows + ((size_t)u * D + col * R::EPL) * R::ES), f);
+  constexpr int LPR = D / EPL;
+  const int col = threadIdx.x % LPR;
+  float f[EPL];
+  load_elems<DT, EPL>((const char*)rows + ((size_t)u * D + col * EPL) * elem_bytes<DT>(), f);
   float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < R::EPL; ++j) s = fmaf(qf[j], f[j], s);
-  return group_sum<R::LPR>(s);
+  for (int j = 0; j < EPL; ++j) s = fmaf(qf[j], f[j], s);
+  return group_sum<LPR>(s);
+}
+
+// ---------------------------------------------------------------- 4-bit rows
+#ifndef KVE_DECODE_UNROLL_Q4
+#define KVE_DECODE_UNROLL_Q4 2
+#endif
+constexpr int kUnrollQ4 = KVE_DECODE_UNROLL_Q4;
+
+__device__ inline float ld_scale(const float* p) {
+#if KVE_DECODE_NT_LOADS
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+__device__ inline uint2 ld_codes(const void* p) {
+#if KVE_DECODE_NT_LOADS
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+#else
+  return *reinterpret_cast<const uint2*>(p);
+#endif
+}
+
+// Logits of 4-bit rows [r0, r1): Kq = the unit's code bytes, Ks its scales;
+// qf = this lane's 16 query elements, qsum their sum.
+template <int D>
+__device__ inline void row_logits_q4(const char* Kq, const float* Ks, const float* qf, float qsum, float scale,
+                                     int r0, int r1, float* lg, float* lgg) {
+  using Q = Q4Rows<D>;
+  const int col = threadIdx.x % Q::LPR, rg = threadIdx.x / Q::LPR;
+  for (int b = r0; b < r1; b += Q::RPI * kUnrollQ4) {
+    uint2 raw[kUnrollQ4];
+    float sc[kUnrollQ4];
+#pragma unroll
+    for (int i = 0; i < kUnrollQ4; ++i) {
+      const int r = b + i * Q::RPI + rg;
+      raw[i] = r < r1 ? ld_codes(Kq + (size_t)r * Q::CB + col * 8) : make_uint2(0, 0);
+      sc[i] = r < r1 ? ld_scale(Ks + (size_t)r * Q::G + col / 2) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kUnrollQ4; ++i) {
+      const int r = b + i * Q::RPI + rg;
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        float f[8];
+        q4_nibbles(w == 0 ? raw[i].x : raw[i].y, f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s = fmaf(qf[w * 8 + j], f[j], s);
+      }
+      s = group_sum<Q::LPR>(sc[i] * fmaf(-8.f, qsum, s)) * scale;
+      if (col == 0 && r < r1) {
+        lg[r - r0] = s;
+        if (lgg) lgg[r] = s;
+      }
+    }
+  }
+}
+
+// acc (this lane's 16 columns) += sum over rows [r0, r1) of w[r - r0] * scale_r
+// * (c + 8); off += sum of w[r - r0] * scale_r (the caller subtracts 8 * off).
+template <int D>
+__device__ inline void row_values_q4(const char* Vq, const float* Vs, const float* w, int r0, int r1, float* acc,
+                                     float& off) {
+  using Q = Q4Rows<D>;
+  const int col = threadIdx.x % Q::LPR, rg = threadIdx.x / Q::LPR;
+  for (int b = r0; b < r1; b += Q::RPI * kUnrollQ4) {
+    uint2 raw[kUnrollQ4];
+    float sc[kUnrollQ4];
+#pragma unroll
+    for (int i = 0; i < kUnrollQ4; ++i) {
+      const int r = b + i * Q::RPI + rg;
+      raw[i] = r < r1 ? ld_codes(Vq + (size_t)r * Q::CB + col * 8) : make_uint2(0, 0);
+      sc[i] = r < r1 ? ld_scale(Vs + (size_t)r * Q::G + col / 2) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kUnrollQ4; ++i) {
+      const int r = b + i * Q::RPI + rg;
+      const float ws = r < r1 ? w[r - r0] * sc[i] : 0.f;
+      off += ws;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        float f[8];
+        q4_nibbles(k == 0 ? raw[i].x : raw[i].y, f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[k * 8 + j] = fmaf(ws, f[j], acc[k * 8 + j]);
+      }
+    }
+  }
+}
+
+// Folds the row groups of each 16-lane row (lanes with equal column, LPR
+// apart) by DPP rotations, then lanes [0, LPR) of each 16-lane row store
+// their 16 columns: red[tid / 16][d].
+template <int D>
+__device__ inline void stash_q4(float* acc, float* red) {
+  using Q = Q4Rows<D>;
+#pragma unroll
+  for (int j = 0; j < Q::EPL; ++j) {
+    float v = acc[j];
+    if constexpr (Q::LPR <= 4) v = dpp_add<0x124>(v);   // row_ror:4
+    v = dpp_add<0x128>(v);                               // row_ror:8
+    acc[j] = v;
+  }
+  const int l16 = threadIdx.x % 16;
+  if (l16 < Q::LPR) {
+#pragma unroll
+    for (int j = 0; j < Q::EPL; ++j) red[(threadIdx.x / 16) * D + l16 * Q::EPL + j] = acc[j];
+  }
 }
 
 // Per-lane partial outputs -> red[rg][d]; after a barrier column i's total is
@@ -152,7 +298,7 @@ __device__ inline void stash_groups(const float* acc, float* red) {
 // n kept slots (read for H2O and PERSIST heads only), e_new = exp(l_t - M),
 // L = the sum of every weight, invL = 1 / L.  Control flow is uniform over
 // the workgroup; contains barriers.
-template <int DT, int D>
+template <int DT, int D, bool Q4>
 __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const DecodeIO& io, const HeadMeta& m,
                                    int u, int n, const float* wts, float e_new, double L, double invL,
                                    MinKey* kscr) {
@@ -277,13 +423,23 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
   }
   if (wslot >= 0) {
     __syncthreads();                           // every read of the slot is done
-    char* Kb = (char*)c.K + slot0 * D * R::ES;
-    char* Vb = (char*)c.V + slot0 * D * R::ES;
-    if (tid < R::LPR) {
-      const size_t src = ((size_t)u * D + tid * R::EPL) * R::ES;
-      const size_t dst = ((size_t)wslot * D + tid * R::EPL) * R::ES;
-      st16(Kb + dst, ld16((const char*)io.k + src));
-      st16(Vb + dst, ld16((const char*)io.v + src));
+    if constexpr (Q4) {
+      constexpr int G = D / kQGroup;
+      if (tid < G) {
+        const size_t src = (size_t)u * D * R::ES;
+        const size_t row = slot0 + wslot;
+        q4_store_group<DT, D>((const char*)io.k + src, (char*)c.K + row * (D / 2), c.Ksc + row * G, tid);
+        q4_store_group<DT, D>((const char*)io.v + src, (char*)c.V + row * (D / 2), c.Vsc + row * G, tid);
+      }
+    } else {
+      char* Kb = (char*)c.K + slot0 * D * R::ES;
+      char* Vb = (char*)c.V + slot0 * D * R::ES;
+      if (tid < R::LPR) {
+        const size_t src = ((size_t)u * D + tid * R::EPL) * R::ES;
+        const size_t dst = ((size_t)wslot * D + tid * R::EPL) * R::ES;
+        st16(Kb + dst, ld16((const char*)io.k + src));
+        st16(Vb + dst, ld16((const char*)io.v + src));
+      }
     }
     if (tid == 0) {
       c.S[slot0 + wslot] = s_new;
@@ -296,32 +452,40 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
 }
 
 // ------------------------------------------------------------------ fused
-template <int DT, int D>
+template <int DT, int D, bool Q4>
 __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, DecodeIO io) {
   using R = Rows<DT, D>;
+  using Y = Lay<DT, D, Q4>;
   extern __shared__ float wts[];                 // [cap + 1]
-  __shared__ float red[R::RPI * D];
+  __shared__ float red[Y::NRED * D];
   __shared__ float fscr[kNT / kWave];
   __shared__ double dscr[kNT / kWave];
   __shared__ MinKey kscr[kNT / kWave];
 
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
-  const int col = tid % R::LPR;
-  const int rg = tid / R::LPR;
+  const int col = tid % Y::LPR;
+  const int rg = tid / Y::LPR;
   const HeadMeta m = c.meta[u];
   const int n = c.count[u];
   const int with_new = m.policy == HASH ? 0 : 1;  // HASH: token t is already in a slot
   const size_t slot0 = (size_t)u * c.cap;
-  const char* Kb = (const char*)c.K + slot0 * D * R::ES;
-  const char* Vb = (const char*)c.V + slot0 * D * R::ES;
+  const char* Kb = (const char*)c.K + slot0 * (Q4 ? D / 2 : D * R::ES);
+  const char* Vb = (const char*)c.V + slot0 * (Q4 ? D / 2 : D * R::ES);
 
-  float qf[R::EPL];
-  St<DT>::unpack(ld16((const char*)io.q + ((size_t)u * D + col * R::EPL) * R::ES), qf);
+  float qf[Y::EPL];
+  load_elems<DT, Y::EPL>((const char*)io.q + ((size_t)u * D + col * Y::EPL) * R::ES, qf);
 
-  row_logits<DT, D>(Kb, qf, sh.scale, 0, n, wts, nullptr);
+  if constexpr (Q4) {
+    float qsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < Y::EPL; ++j) qsum += qf[j];
+    row_logits_q4<D>(Kb, c.Ksc + slot0 * Q4Rows<D>::G, qf, qsum, sh.scale, 0, n, wts, nullptr);
+  } else {
+    row_logits<DT, D>(Kb, qf, sh.scale, 0, n, wts, nullptr);
+  }
   if (with_new && rg == 0) {
-    const float s = group0_dot<DT, D>(qf, io.k, u) * sh.scale;
+    const float s = group0_dot<DT, D, Y::EPL>(qf, io.k, u) * sh.scale;
     if (col == 0) wts[n] = s;
   }
   __syncthreads();
@@ -341,36 +505,45 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
   const double invL = 1.0 / L;
 
   // output o = sum_j w_j v_j / L
-  float acc[R::EPL];
+  float acc[Y::EPL];
 #pragma unroll
-  for (int j = 0; j < R::EPL; ++j) acc[j] = 0.f;
-  row_values<DT, D>(Vb, wts, 0, n, acc);
+  for (int j = 0; j < Y::EPL; ++j) acc[j] = 0.f;
+  if constexpr (Q4) {
+    float off = 0.f;
+    row_values_q4<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, wts, 0, n, acc, off);
+#pragma unroll
+    for (int j = 0; j < Y::EPL; ++j) acc[j] = fmaf(-8.f, off, acc[j]);
+  } else {
+    row_values<DT, D>(Vb, wts, 0, n, acc);
+  }
   if (with_new && rg == 0) {
     const float w = wts[n];
-    float f[R::EPL];
-    St<DT>::unpack(ld16((const char*)io.v + ((size_t)u * D + col * R::EPL) * R::ES), f);
+    float f[Y::EPL];
+    load_elems<DT, Y::EPL>((const char*)io.v + ((size_t)u * D + col * Y::EPL) * R::ES, f);
 #pragma unroll
-    for (int j = 0; j < R::EPL; ++j) acc[j] = fmaf(w, f[j], acc[j]);
+    for (int j = 0; j < Y::EPL; ++j) acc[j] = fmaf(w, f[j], acc[j]);
   }
-  stash_groups<DT, D>(acc, red);
+  if constexpr (Q4) stash_q4<D>(acc, red);
+  else stash_groups<DT, D>(acc, red);
   __syncthreads();
   for (int i = tid; i < D; i += kNT) {
     float s = 0.f;
 #pragma unroll 4
-    for (int g = 0; g < R::RPI; ++g) s += red[g * D + i];
+    for (int g = 0; g < Y::NRED; ++g) s += red[g * D + i];
     io.out[(size_t)u * D + i] = (float)((double)s * invL);
   }
-  policy_step<DT, D>(sh, c, io, m, u, n, wts, with_new ? wts[n] : 0.f, L, invL, kscr);
+  policy_step<DT, D, Q4>(sh, c, io, m, u, n, wts, with_new ? wts[n] : 0.f, L, invL, kscr);
 }
 
 // ------------------------------------------------------------------ split
 // One chunk [c0, c0 + chunk) of one unit's kept slots:
 // part = (unnormalised output[d], chunk maximum, chunk sum of exp(l - max)).
-template <int DT, int D>
+template <int DT, int D, bool Q4>
 __global__ KVE_DECODE_ATTR void decode_partial_kernel(Shape sh, LayerCache c, DecodeIO io, SplitScratch sp) {
   using R = Rows<DT, D>;
+  using Y = Lay<DT, D, Q4>;
   extern __shared__ float lg[];                  // [chunk]
-  __shared__ float red[R::RPI * D];
+  __shared__ float red[Y::NRED * D];
   __shared__ float fscr[kNT / kWave];
   __shared__ double dscr[kNT / kWave];
   const int u = blockIdx.y;
@@ -380,16 +553,24 @@ __global__ KVE_DECODE_ATTR void decode_partial_kernel(Shape sh, LayerCache c, De
   if (c0 >= n) return;                           // uniform: the whole workgroup leaves
   const int c1 = min(n, c0 + sp.chunk);
   const int tid = threadIdx.x;
-  const int col = tid % R::LPR;
+  const int col = tid % Y::LPR;
   const HeadMeta m = c.meta[u];
   const size_t slot0 = (size_t)u * c.cap;
-  const char* Kb = (const char*)c.K + slot0 * D * R::ES;
-  const char* Vb = (const char*)c.V + slot0 * D * R::ES;
-  float qf[R::EPL];
-  St<DT>::unpack(ld16((const char*)io.q + ((size_t)u * D + col * R::EPL) * R::ES), qf);
+  const char* Kb = (const char*)c.K + slot0 * (Q4 ? D / 2 : D * R::ES);
+  const char* Vb = (const char*)c.V + slot0 * (Q4 ? D / 2 : D * R::ES);
+  float qf[Y::EPL];
+  load_elems<DT, Y::EPL>((const char*)io.q + ((size_t)u * D + col * Y::EPL) * R::ES, qf);
 
   const bool keep_logits = m.policy == H2O || m.policy == PERSIST;   // the combine needs every weight
-  row_logits<DT, D>(Kb, qf, sh.scale, c0, c1, lg, keep_logits ? sp.logits + slot0 : nullptr);
+  if constexpr (Q4) {
+    float qsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < Y::EPL; ++j) qsum += qf[j];
+    row_logits_q4<D>(Kb, c.Ksc + slot0 * Q4Rows<D>::G, qf, qsum, sh.scale, c0, c1, lg,
+                     keep_logits ? sp.logits + slot0 : nullptr);
+  } else {
+    row_logits<DT, D>(Kb, qf, sh.scale, c0, c1, lg, keep_logits ? sp.logits + slot0 : nullptr);
+  }
   __syncthreads();
   const int len = c1 - c0;
   float mx = -INFINITY;
@@ -402,17 +583,25 @@ __global__ KVE_DECODE_ATTR void decode_partial_kernel(Shape sh, LayerCache c, De
     ls += (double)w;
   }
   const double L = block_sum<kNT>(ls, dscr);     // barriers inside: lg[] complete
-  float acc[R::EPL];
+  float acc[Y::EPL];
 #pragma unroll
-  for (int j = 0; j < R::EPL; ++j) acc[j] = 0.f;
-  row_values<DT, D>(Vb, lg, c0, c1, acc);
-  stash_groups<DT, D>(acc, red);
+  for (int j = 0; j < Y::EPL; ++j) acc[j] = 0.f;
+  if constexpr (Q4) {
+    float off = 0.f;
+    row_values_q4<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, lg, c0, c1, acc, off);
+#pragma unroll
+    for (int j = 0; j < Y::EPL; ++j) acc[j] = fmaf(-8.f, off, acc[j]);
+    stash_q4<D>(acc, red);
+  } else {
+    row_values<DT, D>(Vb, lg, c0, c1, acc);
+    stash_groups<DT, D>(acc, red);
+  }
   __syncthreads();
   float* part = sp.part + ((size_t)u * sp.max_chunks + ch) * (D + 2);
   for (int i = tid; i < D; i += kNT) {
     float s = 0.f;
 #pragma unroll 4
-    for (int g = 0; g < R::RPI; ++g) s += red[g * D + i];
+    for (int g = 0; g < Y::NRED; ++g) s += red[g * D + i];
     part[i] = s;
   }
   if (tid == 0) {
@@ -423,7 +612,7 @@ __global__ KVE_DECODE_ATTR void decode_partial_kernel(Shape sh, LayerCache c, De
 
 // Merges a unit's chunks, normalises the output and runs the policy step.
 // The unit's chunk partials are staged in LDS with coalesced loads first.
-template <int DT, int D>
+template <int DT, int D, bool Q4>
 __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, DecodeIO io, SplitScratch sp) {
   using R = Rows<DT, D>;
   extern __shared__ float lds[];                 // [max_chunks * (D + 2)] partials, then [cap] weights
@@ -499,7 +688,7 @@ __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, De
     }
     io.out[(size_t)u * D + i] = (float)((double)s * invL);
   }
-  policy_step<DT, D>(sh, c, io, m, u, n, wts, e_new, L, invL, kscr);
+  policy_step<DT, D, Q4>(sh, c, io, m, u, n, wts, e_new, L, invL, kscr);
 }
 
 hipError_t set_lds(const void* fn, size_t lds) {
@@ -507,27 +696,33 @@ hipError_t set_lds(const void* fn, size_t lds) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-template <int DT, int D>
-hipError_t launch_t(const Shape& sh, const LayerCache& c, const DecodeIO& io, const SplitScratch* sp,
+template <int DT, int D, bool Q4>
+hipError_t launch_f(const Shape& sh, const LayerCache& c, const DecodeIO& io, const SplitScratch* sp,
                     hipStream_t st) {
   if (!sp) {
     const size_t lds = (size_t)(c.cap + 1) * sizeof(float);
-    hipError_t e = set_lds((const void*)decode_fused_kernel<DT, D>, lds);
+    hipError_t e = set_lds((const void*)decode_fused_kernel<DT, D, Q4>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_fused_kernel<DT, D>), dim3(sh.units()), dim3(kNT), lds, st, sh, c, io);
+    hipLaunchKernelGGL((decode_fused_kernel<DT, D, Q4>), dim3(sh.units()), dim3(kNT), lds, st, sh, c, io);
     return hipGetLastError();
   }
   const size_t lds_p = (size_t)sp->chunk * sizeof(float);
   const size_t lds_c = ((size_t)sp->max_chunks * (D + 2) + c.cap) * sizeof(float);
-  hipError_t e = set_lds((const void*)decode_partial_kernel<DT, D>, lds_p);
-  if (e == hipSuccess) e = set_lds((const void*)decode_combine_kernel<DT, D>, lds_c);
+  hipError_t e = set_lds((const void*)decode_partial_kernel<DT, D, Q4>, lds_p);
+  if (e == hipSuccess) e = set_lds((const void*)decode_combine_kernel<DT, D, Q4>, lds_c);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_partial_kernel<DT, D>), dim3(sp->max_chunks, sh.units()), dim3(kNT), lds_p, st, sh, c,
-                     io, *sp);
+  hipLaunchKernelGGL((decode_partial_kernel<DT, D, Q4>), dim3(sp->max_chunks, sh.units()), dim3(kNT), lds_p, st, sh,
+                     c, io, *sp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<DT, D>), dim3(sh.units()), dim3(kNT), lds_c, st, sh, c, io, *sp);
+  hipLaunchKernelGGL((decode_combine_kernel<DT, D, Q4>), dim3(sh.units()), dim3(kNT), lds_c, st, sh, c, io, *sp);
   return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_t(const Shape& sh, const LayerCache& c, const DecodeIO& io, const SplitScratch* sp,
+                    hipStream_t st) {
+  return c.q4 ? launch_f<DT, D, true>(sh, c, io, sp, st) : launch_f<DT, D, false>(sh, c, io, sp, st);
 }
 
 }  // namespace

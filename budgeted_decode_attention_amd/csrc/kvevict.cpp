@@ -219,6 +219,13 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
     return fail(KVE_EINVAL, "SPECIAL heads need keep_token_bitmap and vocab >= 1");
   if (need_proj && (!c->lsh_proj_bf16 || (c->sketch_bits != 16 && c->sketch_bits != 32 && c->sketch_bits != 64)))
     return fail(KVE_EUNSUPPORTED, "HASH heads need lsh_proj_bf16 and sketch_bits of 16, 32 or 64");
+  if (c->cache_bits != 0 && c->cache_bits != 4)
+    return fail(KVE_EUNSUPPORTED, "cache_bits %d not built (0 or 4)", c->cache_bits);
+  if (c->cache_bits == 4)
+    for (int i = 0; i < c->layers * c->heads; ++i)
+      if (c->policy[i] != KVE_H2O && c->policy[i] != KVE_PERSIST)
+        return fail(KVE_EUNSUPPORTED, "layer %d head %d: 4-bit slots are built for H2O and PERSIST heads only",
+                    i / c->heads, i % c->heads);
   if (need_ids_tables) {
     if (!c->special_token_bitmap || !c->punct_token_bitmap || c->vocab < 1)
       return fail(KVE_EINVAL, "ADAPTIVE heads need special_token_bitmap, punct_token_bitmap and vocab >= 1");
@@ -320,8 +327,13 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
     const LayerInfo& li = info[l];
     const size_t cap = li.cap;
     kve::LayerCache lc{};
-    lc.K = pl.take<char>(U * cap * d * es);
-    lc.V = pl.take<char>(U * cap * d * es);
+    const bool q4 = c->cache_bits == 4;
+    const size_t row_bytes = q4 ? d / 2 : d * es;   // 4-bit slots: two codes per byte
+    lc.K = pl.take<char>(U * cap * row_bytes);
+    lc.V = pl.take<char>(U * cap * row_bytes);
+    lc.Ksc = q4 ? pl.take<float>(U * cap * (d / 32)) : nullptr;
+    lc.Vsc = q4 ? pl.take<float>(U * cap * (d / 32)) : nullptr;
+    lc.q4 = q4 ? 1 : 0;
     lc.S = pl.take<double>(U * cap);
     lc.pos = pl.take<int32_t>(U * cap);
     lc.sk = li.any_hash ? (void*)pl.take<char>(U * cap * swb) : nullptr;
@@ -572,6 +584,28 @@ kve_status kvevict_kept_indices(kve_handle h, int32_t layer, int32_t* pos_out, i
     e = hipMemcpyAsync(scores_out, L.cache.S, U * cap * 8, hipMemcpyDeviceToDevice, st);
   if (e != hipSuccess) return dev(e, "kept_indices copy");
   return finish(h, st, "kept_indices");
+}
+
+kve_status kvevict_cache_rows(kve_handle h, int32_t layer, void* k_out, void* v_out, float* k_scale_out,
+                              float* v_scale_out, void* stream) {
+  kve_status s = check_layer(h, layer);
+  if (s != KVE_OK) return s;
+  const Layer& L = h->layers[layer];
+  const bool q4 = L.cache.q4 != 0;
+  if (!k_out || !v_out || (q4 && (!k_scale_out || !v_scale_out)))
+    return fail(KVE_EINVAL, "k_out and v_out (and, for 4-bit slots, the scale outputs) are required");
+  if (L.position < 0) return fail(KVE_ESTATE, "layer %d has no cache yet", layer);
+  hipStream_t st = (hipStream_t)stream;
+  const size_t U = h->shape.units(), cap = L.cache.cap, d = h->shape.d;
+  const size_t rows = U * cap * (q4 ? d / 2 : d * elem_size(h->cfg.dtype));
+  hipError_t e = hipMemcpyAsync(k_out, L.cache.K, rows, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(v_out, L.cache.V, rows, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && q4)
+    e = hipMemcpyAsync(k_scale_out, L.cache.Ksc, U * cap * (d / 32) * 4, hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && q4)
+    e = hipMemcpyAsync(v_scale_out, L.cache.Vsc, U * cap * (d / 32) * 4, hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return dev(e, "cache_rows copy");
+  return finish(h, st, "cache_rows");
 }
 
 kve_status kvevict_unit_policies(kve_handle h, int32_t layer, int32_t* choice_out, void* stream) {

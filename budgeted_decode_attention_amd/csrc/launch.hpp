@@ -37,8 +37,8 @@ struct IdSets {
 
 // One layer's cache, carved from the workspace.
 struct LayerCache {
-  void* K;              // [U][cap][d] storage dtype
-  void* V;              // [U][cap][d]
+  void* K;              // [U][cap][d] storage dtype, or [U][cap][d / 2] 4-bit code bytes (q4)
+  void* V;              // [U][cap][d], likewise
   double* S;            // [U][cap] accumulated scores (H2O heads); the 64-bit
                         // pivotal histories in the same bytes (PERSIST heads)
   int32_t* pos;         // [U][cap] position per slot, -1 = empty
@@ -50,6 +50,9 @@ struct LayerCache {
   const uint16_t* proj; // [d][bits] bf16 projection (HASH), or null
   int32_t cap;          // slot stride per unit
   int32_t sk_bits;      // sketch width (HASH layers): 16, 32 or 64
+  float* Ksc;           // [U][cap][d / 32] group scales of the 4-bit K rows (q4), else null
+  float* Vsc;           // [U][cap][d / 32] group scales of the 4-bit V rows (q4), else null
+  int32_t q4;           // 1: slots hold 4-bit rows (H2O and PERSIST heads only)
 };
 
 struct Shape {

@@ -1,0 +1,78 @@
+// 4-bit cache slots (gfx950 device helpers).
+//
+// Scissorhands summary page, Abstract: the budgeted cache combines with 4-bit
+// quantisation.  The page fixes no format; the one used here: a row of d
+// elements is d / 32 groups of 32 consecutive elements, each with a float32
+// scale = (largest magnitude) * fl32(1/7) and codes c = rint(x / scale) in
+// [-7, 7] (float32 quotient, correctly rounded, then rounded half to even; a
+// zero scale gives codes 0).  A slot row reads back as c * scale.
+//
+// Storage: the d / 2 code bytes of a row hold element 2b of byte b in the low
+// nibble and element 2b + 1 in the high nibble, each as c + 8 (1..15); the
+// scales of a row are d / 32 consecutive floats.  A group's codes are 16
+// bytes: the quantiser writes one group per lane with one 16-byte store.
+#pragma once
+
+#include "common.hpp"
+
+namespace kve {
+
+constexpr int kQGroup = 32;
+constexpr float kInvQMax = (float)(1.0 / 7.0);
+
+// n consecutive elements of the storage dtype at p (16-byte aligned) as floats.
+template <int DT, int N>
+__device__ inline void load_elems(const void* p, float* f) {
+  constexpr int EPL = St<DT>::EPL;
+  static_assert(N % EPL == 0, "whole 16-byte loads");
+#pragma unroll
+  for (int i = 0; i < N / EPL; ++i) St<DT>::unpack(ld16((const char*)p + i * 16), f + i * EPL);
+}
+
+// One group x[0, 32) -> its 16 code bytes and its scale.  Every decision is a
+// float32 operation with one rounding: the product for the scale, the
+// quotient (__fdiv_rn), the round to nearest even (rintf).
+__device__ inline void q4_quantize(const float* x, uint4& packed, float& scale) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < kQGroup; ++j) amax = fmaxf(amax, fabsf(x[j]));
+  scale = __fmul_rn(amax, kInvQMax);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < kQGroup; ++j) {
+    float c = scale > 0.f ? rintf(__fdiv_rn(x[j], scale)) : 0.f;
+    c = fminf(fmaxf(c, -7.f), 7.f);
+    w[j >> 3] |= (uint32_t)((int)c + 8) << ((j & 7) * 4);
+  }
+  packed = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The eight stored nibbles (c + 8) of one little-endian code word, in element
+// order, as floats.  Masking every other nibble into byte lanes lets
+// each element convert with one unsigned-byte-to-float conversion.
+__device__ inline void q4_nibbles(uint32_t w, float* f) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  f[0] = (float)(lo & 0xffu);
+  f[1] = (float)(hi & 0xffu);
+  f[2] = (float)((lo >> 8) & 0xffu);
+  f[3] = (float)((hi >> 8) & 0xffu);
+  f[4] = (float)((lo >> 16) & 0xffu);
+  f[5] = (float)((hi >> 16) & 0xffu);
+  f[6] = (float)(lo >> 24);
+  f[7] = (float)(hi >> 24);
+}
+
+// Quantises the row of D elements at src (storage dtype) into code bytes dst
+// and scales dsc, group g = the calling lane's `g`.
+template <int DT, int D>
+__device__ inline void q4_store_group(const void* src, char* dst, float* dsc, int g) {
+  float x[kQGroup];
+  load_elems<DT, kQGroup>((const char*)src + (size_t)g * kQGroup * (16 / St<DT>::EPL), x);
+  uint4 pk;
+  float sc;
+  q4_quantize(x, pk, sc);
+  st16(dst + g * 16, pk);
+  dsc[g] = sc;
+}
+
+}  // namespace kve

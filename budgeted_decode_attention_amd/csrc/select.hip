@@ -21,6 +21,7 @@
 // first.  Occupied slots are [0, count) in increasing position order (LOCAL:
 // ring order); the rest of the stride holds position -1 and score 0.
 #include "common.hpp"
+#include "q4.hpp"
 
 namespace kve {
 namespace {
@@ -114,7 +115,8 @@ __device__ inline void radix_top(int nc, int want, int first_pass, Key key, Cand
   cut = r.cut;
 }
 
-// Gathers the K/V rows of kept_pos[0, count) into the unit's slots.
+// Gathers the K/V rows of kept_pos[0, count) into the unit's slots; a layer
+// of 4-bit slots quantises them on the way (one lane per group of 32).
 template <int DT, int D>
 __device__ inline void gather_rows(const LayerCache& c, int u, int P, const int32_t* kept_pos, int count,
                                    const void* k, const void* v) {
@@ -125,6 +127,18 @@ __device__ inline void gather_rows(const LayerCache& c, int u, int P, const int3
   const int tid = threadIdx.x;
   const size_t slot0 = (size_t)u * c.cap;
   const size_t src0 = (size_t)u * P * D * ES;
+  if (c.q4) {
+    constexpr int G = D / kQGroup;
+    char* Kd = (char*)c.K + slot0 * (D / 2);
+    char* Vd = (char*)c.V + slot0 * (D / 2);
+    const int g = tid % G;
+    for (int s = tid / G; s < count; s += kNT / G) {
+      const size_t so = src0 + (size_t)kept_pos[s] * D * ES;
+      q4_store_group<DT, D>((const char*)k + so, Kd + (size_t)s * (D / 2), c.Ksc + (slot0 + s) * G, g);
+      q4_store_group<DT, D>((const char*)v + so, Vd + (size_t)s * (D / 2), c.Vsc + (slot0 + s) * G, g);
+    }
+    return;
+  }
   char* Kd = (char*)c.K + slot0 * D * ES;
   char* Vd = (char*)c.V + slot0 * D * ES;
   const int col = tid % LPR;

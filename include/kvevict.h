@@ -148,6 +148,20 @@ typedef struct {
   const uint32_t* punct_token_bitmap;
   int32_t profile_rows;
   float profile_threshold;
+  /* Cached K/V format (Scissorhands page, Abstract: the budgeted cache
+   * combines with 4-bit quantisation; the format is a reading).
+   *   0  rows in the storage dtype.
+   *   4  4-bit slots: each row of head_dim elements is head_dim / 32 groups
+   *      of 32; a group stores a float32 scale = (its largest magnitude) *
+   *      fl32(1/7) and codes c = rint(x / scale) clamped to [-7, 7], the
+   *      quotient a correctly rounded float32 division and rint half to even
+   *      (a zero scale gives codes 0); the row reads back as c * scale.
+   *      Every head of every layer must be KVE_H2O or KVE_PERSIST
+   *      (KVE_EUNSUPPORTED otherwise).  Prompt scores and the prompt output
+   *      use the inputs at full precision; rows are quantised when they enter
+   *      the cache, and the step-t query uses token t's own key and value
+   *      unquantised at that step. */
+  int32_t cache_bits;
 } kve_config;
 
 /* Bytes of device workspace the configuration needs (including 256-byte
@@ -201,6 +215,18 @@ kve_status kvevict_decode_step(kve_handle h, int32_t layer,
  * protected ones; other heads export 0), or NULL.  `capacity` is kvevict_capacity(h, layer). */
 kve_status kvevict_kept_indices(kve_handle h, int32_t layer, int32_t* pos_out,
                                 int32_t* count_out, double* scores_out, void* stream);
+
+/* Copies one layer's slot contents in slot order (device pointers,
+ * stream-ordered; ESTATE before the layer's prefill).  `capacity` is
+ * kvevict_capacity(h, layer), U = batch * heads, d = head_dim.
+ * cache_bits 0: k_out, v_out [U][capacity][d] storage dtype; the scale
+ *   arguments are ignored (may be NULL).
+ * cache_bits 4: k_out, v_out [U][capacity][d / 2] bytes, byte b of a row
+ *   holding element 2b in its low nibble and 2b + 1 in its high nibble, each
+ *   as c + 8; k_scale_out, v_scale_out [U][capacity][d / 32] float32.
+ * Slots beyond a unit's count hold stale bytes. */
+kve_status kvevict_cache_rows(kve_handle h, int32_t layer, void* k_out, void* v_out, float* k_scale_out,
+                              float* v_scale_out, void* stream);
 
 /* The composite each unit of the layer chose at its last prefill (FastGen
  * profiling, KVE_ADAPTIVE heads): choice_out [batch][heads] int32 receives

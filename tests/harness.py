@@ -10,7 +10,7 @@ import numpy as np
 import torch
 
 from budgeted_decode_attention_amd import KVCache
-from oracle import lockstep
+from oracle import lockstep, quant
 from workloads import configs
 from workloads.configs import ADAPTIVE, FULL, H2O, HASH, LOCAL, PERSIST, SPECIAL, Workload
 from workloads.generate import LayerInputs, generate_layer, unit_ids, unit_sequence
@@ -36,7 +36,7 @@ def make_cache(w: Workload, inp: LayerInputs, policy=None, heavy=None, recent=No
         hw = [w.history_window if p == PERSIST else 0 for p in pol] if history is None else history
         kw.update(history=np.tile(np.array(hw, dtype=np.int32), layers))
     return KVCache(layers, w.batch, w.heads, w.head_dim, max_context or w.context,
-                   inp.prompt_q.dtype, tables[0], tables[1], tables[2], **kw)
+                   inp.prompt_q.dtype, tables[0], tables[1], tables[2], cache_bits=w.cache_bits, **kw)
 
 
 @dataclass
@@ -98,14 +98,16 @@ def check_unit(w: Workload, inp_cpu: LayerInputs, r: GpuRun, b: int, h: int, pol
     P = inp_cpu.prompt_q.shape[2]
     T = r.out.shape[0]
     g = gpu_unit(r, b, h)
+    # 4-bit slots: cached rows read back what the format holds
+    Kc, Vc = (quant.roundtrip(K), quant.roundtrip(V)) if w.cache_bits == 4 else (None, None)
     if p == H2O:
-        rep = lockstep.check_h2o(Q, K, V, P, hh, rr, sc, g, steps=T)
+        rep = lockstep.check_h2o(Q, K, V, P, hh, rr, sc, g, steps=T, Kc=Kc, Vc=Vc)
     elif p == HASH:
         Wp = inp_cpu.proj.float().double().cpu().numpy()
         rep = lockstep.check_hash(Q, K, V, Wp, P, hh, sc, g, steps=T)
     elif p == PERSIST:
         win = w.history_window if history is None else history[h]
-        rep = lockstep.check_persist(Q, K, V, P, hh, rr, win, sc, g, steps=T)
+        rep = lockstep.check_persist(Q, K, V, P, hh, rr, win, sc, g, steps=T, Kc=Kc, Vc=Vc)
     elif p == ADAPTIVE:
         rep = lockstep.check_adaptive(Q, K, V, unit_ids(inp_cpu, b), P, list(w.special_ids), list(w.punct_ids),
                                       hh, rr, sc, w.profile_rows, w.profile_threshold, g, int(r.choice[b, h]),

@@ -22,7 +22,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     lib = binding.load_library()
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -156,3 +156,33 @@ def test_64_bit_sketches_cap_the_budget():
     assert status_of(c)[0] == binding.KVE_EINVAL
     c, keep = cfg(policy=[4, 1, 1], heavy=[12288, 10, 10], recent=[0, 5, 5], proj=proj, max_context=20000)
     assert status_of(c)[0] == binding.KVE_OK
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(cache_bits=4), binding.KVE_OK),
+    (dict(cache_bits=4, policy=[5, 1, 5], history=[8, 8, 8]), binding.KVE_OK),
+    (dict(cache_bits=4, head_dim=64), binding.KVE_OK),
+    (dict(cache_bits=4, dtype=torch.float32), binding.KVE_OK),
+    (dict(cache_bits=8), binding.KVE_EUNSUPPORTED),
+    (dict(cache_bits=4, policy=[2, 1, 1], heavy=[0, 10, 10], recent=[5, 5, 5]), binding.KVE_EUNSUPPORTED),
+    (dict(cache_bits=4, policy=[0, 1, 1], heavy=[0, 10, 10], recent=[0, 5, 5]), binding.KVE_EUNSUPPORTED),
+])
+def test_four_bit_slots_configs(over, status):
+    c, keep = cfg(**over)
+    assert status_of(c)[0] == status
+
+
+def test_four_bit_slots_shrink_the_workspace():
+    # per slot: d / 2 code bytes and d / 32 float scales for K and for V
+    # (160 bytes at d 128) in place of 2 * d * 2 bytes of bf16 rows (512)
+    big = dict(max_context=4096, heavy=[1000, 1000, 1000], recent=[1000, 1000, 1000])
+    s16, n16 = status_of(cfg(**big)[0])
+    s4, n4 = status_of(cfg(cache_bits=4, **big)[0])
+    assert s16 == s4 == binding.KVE_OK
+    units, cap = 2 * 3, 2000
+    assert abs((n16 - n4) - units * cap * (512 - 160)) < 16 * 256
+
+
+def test_cache_rows_rejects_a_null_handle():
+    lib = binding.load_library()
+    assert lib.kvevict_cache_rows(None, 0, None, None, None, None, None) == binding.KVE_EINVAL

@@ -107,3 +107,10 @@ def test_prompt_output_full_size(name):
             worst = max(worst, e)
             assert e <= lockstep.OUT_RTOL, (b, h, i, e)
     print(f"[fullsize] prompt output max rel err {worst:.2e}", flush=True)
+
+
+def test_opt30b_q4_layer_full_size():
+    """4-bit slots at the OPT-30B shape: lockstep on sampled units against the
+    oracle with quantised cache rows."""
+    rep = run_full("opt30b_decode_h2o_q4", 6)
+    assert rep.decisions == 6 * 256

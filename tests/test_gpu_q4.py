@@ -1,0 +1,130 @@
+"""GPU parity of the 4-bit cache slots (Scissorhands page, Abstract: the
+budgeted cache combined with 4-bit quantisation) against the float64 oracle
+whose cached rows read back what the format holds.
+
+Trajectories are checked in lockstep like the 16-bit caches (kept sets exact up
+to the near-tie band, scores within 1e-5, outputs within 2e-3 of the largest
+output element); the stored codes and scales are compared bit for bit with the
+oracle's quantiser, both sides taking every rounding decision in float32."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quant
+from tests import harness
+from tests.test_gpu_parity import decode_path, run_and_check  # noqa: F401  (fixture)
+from workloads import configs
+from workloads.configs import H2O, PERSIST
+from workloads.generate import generate_layer, unit_sequence
+
+pytestmark = pytest.mark.gpu
+
+
+def test_q4_h2o_bf16_scaled(decode_path):
+    w = configs.scaled("opt30b_decode_h2o_q4", batch=2, heads=3, prompt=700, steps=60)
+    assert (w.heavy, w.recent, w.cache_bits) == (70, 70, 4)
+    rep, _ = run_and_check(w)
+    assert rep.decisions == 6 * 60
+
+
+def test_q4_h2o_fp16_d64(decode_path):
+    """d = 64: two lanes per row, the 8-lane fold of the value pass."""
+    w = dataclasses.replace(configs.scaled("opt6.7b_layer_h2o", batch=2, heads=4, prompt=300, steps=60),
+                            head_dim=64, cache_bits=4)
+    run_and_check(w)
+
+
+def test_q4_h2o_fp32(decode_path):
+    w = dataclasses.replace(configs.scaled("opt6.7b_layer_h2o", batch=1, heads=3, prompt=150, steps=40),
+                            dtype="f32", cache_bits=4)
+    run_and_check(w)
+
+
+def test_q4_persist_and_h2o_heads(decode_path):
+    w = dataclasses.replace(configs.scaled("opt30b_decode_persist", batch=2, heads=3, prompt=400, steps=60),
+                            cache_bits=4)
+    run_and_check(w, policy=[PERSIST, H2O, PERSIST], heavy=[40, 40, 20], recent=[40, 40, 10],
+                  history=[64, 0, 9])
+
+
+@pytest.mark.parametrize("P,T,hh,rc", [(1, 30, 4, 4), (5, 40, 8, 8), (90, 30, 12, 0), (257, 20, 100, 27)])
+def test_q4_edge_shapes(P, T, hh, rc, decode_path):
+    """One-token prompt, prompt shorter than the budget, no recent window,
+    a ragged prompt."""
+    w = configs.scaled("opt30b_decode_h2o_q4", batch=1, heads=2, prompt=P, steps=T)
+    run_and_check(w, policy=[H2O] * 2, heavy=[hh] * 2, recent=[rc] * 2)
+
+
+def expected_rows(X: np.ndarray):
+    """Oracle codes of the rows of X as stored nibbles (c + 8, element 2b in the
+    low nibble of byte b) and their scales."""
+    codes, scale = quant.quantize_rows(X)
+    nib = (codes.astype(np.int16) + 8).astype(np.uint8)
+    return nib[:, 0::2] | (nib[:, 1::2] << 4), scale
+
+
+def check_slot_bytes(w, inp, kv, units):
+    pos, cnt, _ = kv.kept_indices(0, with_scores=False)
+    k, v, ks, vs = kv.cache_rows(0)
+    pos, cnt = pos.cpu().numpy(), cnt.cpu().numpy()
+    k, v, ks, vs = (x.cpu().numpy() for x in (k, v, ks, vs))
+    for b, h in units:
+        n = int(cnt[b, h])
+        p = pos[b, h, :n].astype(np.int64)
+        _, K, V = unit_sequence(inp, b, h)
+        for got, gsc, X, name in ((k, ks, K, "K"), (v, vs, V, "V")):
+            codes, scale = expected_rows(X[p])
+            assert np.array_equal(got[b, h, :n], codes), f"{name} codes differ at b={b} h={h}"
+            assert np.array_equal(gsc[b, h, :n].view(np.uint32), scale.view(np.uint32)), \
+                f"{name} scales differ at b={b} h={h}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_q4_slot_codes_and_scales_are_bit_exact(dtype):
+    """After the prefill and after decode steps, every occupied slot holds the
+    oracle's codes and scales of its position's row.  Some key and value
+    groups are zero (scale 0, codes 0) and some rows are tiny or huge."""
+    w = dataclasses.replace(configs.scaled("opt30b_decode_h2o_q4", batch=2, heads=2, prompt=200, steps=40),
+                            dtype=dtype)
+    print(f"\n[q4 bytes] {dtype}", flush=True)
+    inp = generate_layer(w, 0, "cpu", 3)
+    for t in (inp.prompt_k, inp.prompt_v):
+        t[:, :, 5:20, :32] = 0
+        t[:, :, 30:40, 64:] = 0
+        t[:, :, 50:60] *= 1e-3
+        t[:, :, 60:70] *= 1e3 if dtype != "f16" else 30
+    for t in (inp.dec_k, inp.dec_v):
+        t[::3, :, :, 32:64] = 0
+    kv = harness.make_cache(w, inp)
+    gi = inp.to("cuda")
+    units = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    kv.prefill(0, gi.prompt_q, gi.prompt_k, gi.prompt_v)
+    check_slot_bytes(w, inp, kv, units)
+    for s in range(w.steps):
+        kv.decode_step(0, gi.dec_q[s], gi.dec_k[s], gi.dec_v[s])
+    torch.cuda.synchronize()
+    check_slot_bytes(w, inp, kv, units)
+    kv.close()
+
+
+def test_storage_dtype_slots_hold_the_input_rows():
+    """Without quantisation a slot holds its position's row unchanged."""
+    w = configs.scaled("opt30b_decode_h2o", batch=2, heads=2, prompt=300, steps=30)
+    inp = generate_layer(w, 0, "cpu", 1)
+    kv = harness.make_cache(w, inp)
+    harness.run_layer(kv, inp.to("cuda"))
+    pos, cnt, _ = kv.kept_indices(0, with_scores=False)
+    k, v, ks, vs = kv.cache_rows(0)
+    assert ks is None and vs is None
+    for b in range(w.batch):
+        for h in range(w.heads):
+            n = int(cnt[b, h])
+            p = pos[b, h, :n].cpu().numpy().astype(np.int64)
+            Kall = torch.cat([inp.prompt_k[b, h], inp.dec_k[:, b, h]], 0)
+            Vall = torch.cat([inp.prompt_v[b, h], inp.dec_v[:, b, h]], 0)
+            assert torch.equal(k[b, h, :n].cpu(), Kall[p])
+            assert torch.equal(v[b, h, :n].cpu(), Vall[p])
+    kv.close()

@@ -11,7 +11,10 @@ PERSIST=5.
 
 Beside the five workloads, ``opt30b_decode_persist`` runs the OPT-30B-shaped
 decode under the persistence-count rule (the Scissorhands reading) with the
-same 20% budget, so the two scoring rules are measured on one shape.
+same 20% budget, so the two scoring rules are measured on one shape;
+``llama65b_fastgen_profiled`` lets FastGen's profile choose each unit's
+composite; ``opt30b_decode_h2o_q4`` is the OPT-30B-shaped H2O decode with
+4-bit cache slots (eviction combined with quantisation).
 """
 
 from __future__ import annotations
@@ -47,6 +50,7 @@ class Workload:
     profile_rows: int = 0      # profiled heads: prompt rows the profile reads
     profile_threshold: float = 0.0   # profiled heads: attention share a composite must recover
     sketch_bits: int = 32
+    cache_bits: int = 0        # cached K/V: 0 = the storage dtype, 4 = 4-bit slots
     vocab: int = 32000
     special_ids: Tuple[int, ...] = (0, 1, 2, 3)
     punct_ids: Tuple[int, ...] = tuple(range(4, 14))
@@ -165,8 +169,15 @@ _add(Workload(
                 "bf16, P=4096, T=512; composites special / +punctuation / +409 frequent / +1024 local / full, "
                 "chosen per (sequence, head) at 95% recovered attention over the last 64 prompt rows"))
 
+_add(Workload(
+    name="opt30b_decode_h2o_q4", index=8, layers=48, batch=32, heads=56, head_dim=128, dtype="bf16",
+    prompt=2048, steps=256, family="h2o", structure="zipf_dir", cache_bits=4, **_h2o20(2048),
+    description="OPT-30B-shaped H2O decode with 4-bit cache slots: 48 layers, batch 32, 56 heads, d=128, "
+                "bf16 inputs, P=2048, T=256, 20% budget (204 + 204); K/V rows in groups of 32 with a "
+                "float32 scale and 4-bit codes"))
+
 ORDER = ["tiny_h2o", "opt6.7b_layer_h2o", "opt30b_decode_h2o", "llama65b_fastgen", "hashevict_lsh"]
-NEXT = ["opt30b_decode_persist", "llama65b_fastgen_profiled"]
+NEXT = ["opt30b_decode_persist", "llama65b_fastgen_profiled", "opt30b_decode_h2o_q4"]
 
 
 def get(name: str) -> Workload:
