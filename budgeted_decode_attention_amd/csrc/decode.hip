@@ -172,7 +172,7 @@ __device__ inline float group0_dot(const float* qf, const void* rows, int u) {
 
 // ---------------------------------------------------------------- 4-bit rows
 #ifndef KVE_DECODE_UNROLL_Q4
-#define KVE_DECODE_UNROLL_Q4 2
+#define KVE_DECODE_UNROLL_Q4 1
 #endif
 constexpr int kUnrollQ4 = KVE_DECODE_UNROLL_Q4;
 
@@ -194,22 +194,40 @@ __device__ inline uint2 ld_codes(const void* p) {
 #endif
 }
 
+// One load tile of 4-bit rows: kUnrollQ4 rows per thread (rows b + i RPI + rg
+// of [b, r1)), their 8 code bytes and group scale; rows past r1 read as zero.
+struct Q4Tile {
+  uint2 raw[kUnrollQ4];
+  float sc[kUnrollQ4];
+};
+
+template <int D>
+__device__ inline void q4_load(const char* Xq, const float* Xs, int b, int r1, Q4Tile& t) {
+  using Q = Q4Rows<D>;
+  const int col = threadIdx.x % Q::LPR, rg = threadIdx.x / Q::LPR;
+#pragma unroll
+  for (int i = 0; i < kUnrollQ4; ++i) {
+    const int r = b + i * Q::RPI + rg;
+    t.raw[i] = r < r1 ? ld_codes(Xq + (size_t)r * Q::CB + col * 8) : make_uint2(0, 0);
+    t.sc[i] = r < r1 ? ld_scale(Xs + (size_t)r * Q::G + col / 2) : 0.f;
+  }
+}
+
 // Logits of 4-bit rows [r0, r1): Kq = the unit's code bytes, Ks its scales;
-// qf = this lane's 16 query elements, qsum their sum.
+// qf = this lane's 16 query elements, qsum their sum.  Double-buffered: the
+// next tile's loads are in flight while the current one is reduced.
 template <int D>
 __device__ inline void row_logits_q4(const char* Kq, const float* Ks, const float* qf, float qsum, float scale,
                                      int r0, int r1, float* lg, float* lgg) {
   using Q = Q4Rows<D>;
+  constexpr int STEP = Q::RPI * kUnrollQ4;
   const int col = threadIdx.x % Q::LPR, rg = threadIdx.x / Q::LPR;
-  for (int b = r0; b < r1; b += Q::RPI * kUnrollQ4) {
-    uint2 raw[kUnrollQ4];
-    float sc[kUnrollQ4];
-#pragma unroll
-    for (int i = 0; i < kUnrollQ4; ++i) {
-      const int r = b + i * Q::RPI + rg;
-      raw[i] = r < r1 ? ld_codes(Kq + (size_t)r * Q::CB + col * 8) : make_uint2(0, 0);
-      sc[i] = r < r1 ? ld_scale(Ks + (size_t)r * Q::G + col / 2) : 0.f;
-    }
+  Q4Tile cur;
+  if (r0 < r1) q4_load<D>(Kq, Ks, r0, r1, cur);
+  for (int b = r0; b < r1; b += STEP) {
+    Q4Tile nxt;
+    const bool more = b + STEP < r1;           // uniform
+    if (more) q4_load<D>(Kq, Ks, b + STEP, r1, nxt);
 #pragma unroll
     for (int i = 0; i < kUnrollQ4; ++i) {
       const int r = b + i * Q::RPI + rg;
@@ -217,48 +235,48 @@ __device__ inline void row_logits_q4(const char* Kq, const float* Ks, const floa
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
         float f[8];
-        q4_nibbles(w == 0 ? raw[i].x : raw[i].y, f);
+        q4_nibbles(w == 0 ? cur.raw[i].x : cur.raw[i].y, f);
 #pragma unroll
         for (int j = 0; j < 8; ++j) s = fmaf(qf[w * 8 + j], f[j], s);
       }
-      s = group_sum<Q::LPR>(sc[i] * fmaf(-8.f, qsum, s)) * scale;
+      s = group_sum<Q::LPR>(cur.sc[i] * fmaf(-8.f, qsum, s)) * scale;
       if (col == 0 && r < r1) {
         lg[r - r0] = s;
         if (lgg) lgg[r] = s;
       }
     }
+    if (more) cur = nxt;
   }
 }
 
 // acc (this lane's 16 columns) += sum over rows [r0, r1) of w[r - r0] * scale_r
 // * (c + 8); off += sum of w[r - r0] * scale_r (the caller subtracts 8 * off).
+// `first` is the tile of rows from r0, already loaded by the caller.
 template <int D>
 __device__ inline void row_values_q4(const char* Vq, const float* Vs, const float* w, int r0, int r1, float* acc,
-                                     float& off) {
+                                     float& off, const Q4Tile& first) {
   using Q = Q4Rows<D>;
-  const int col = threadIdx.x % Q::LPR, rg = threadIdx.x / Q::LPR;
-  for (int b = r0; b < r1; b += Q::RPI * kUnrollQ4) {
-    uint2 raw[kUnrollQ4];
-    float sc[kUnrollQ4];
+  constexpr int STEP = Q::RPI * kUnrollQ4;
+  const int rg = threadIdx.x / Q::LPR;
+  Q4Tile cur = first;
+  for (int b = r0; b < r1; b += STEP) {
+    Q4Tile nxt;
+    const bool more = b + STEP < r1;           // uniform
+    if (more) q4_load<D>(Vq, Vs, b + STEP, r1, nxt);
 #pragma unroll
     for (int i = 0; i < kUnrollQ4; ++i) {
       const int r = b + i * Q::RPI + rg;
-      raw[i] = r < r1 ? ld_codes(Vq + (size_t)r * Q::CB + col * 8) : make_uint2(0, 0);
-      sc[i] = r < r1 ? ld_scale(Vs + (size_t)r * Q::G + col / 2) : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < kUnrollQ4; ++i) {
-      const int r = b + i * Q::RPI + rg;
-      const float ws = r < r1 ? w[r - r0] * sc[i] : 0.f;
+      const float ws = r < r1 ? w[r - r0] * cur.sc[i] : 0.f;
       off += ws;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         float f[8];
-        q4_nibbles(k == 0 ? raw[i].x : raw[i].y, f);
+        q4_nibbles(k == 0 ? cur.raw[i].x : cur.raw[i].y, f);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[k * 8 + j] = fmaf(ws, f[j], acc[k * 8 + j]);
       }
     }
+    if (more) cur = nxt;
   }
 }
 
@@ -424,12 +442,15 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
   if (wslot >= 0) {
     __syncthreads();                           // every read of the slot is done
     if constexpr (Q4) {
+      // one element per thread: threads [0, D) the key row, [D, 2D) the value
+      // row (whole waves; with D = 64 the upper two waves have no element)
       constexpr int G = D / kQGroup;
-      if (tid < G) {
-        const size_t src = (size_t)u * D * R::ES;
+      if (tid < 2 * D) {
+        const bool val = tid >= D;
+        const int e = tid - (val ? D : 0);
         const size_t row = slot0 + wslot;
-        q4_store_group<DT, D>((const char*)io.k + src, (char*)c.K + row * (D / 2), c.Ksc + row * G, tid);
-        q4_store_group<DT, D>((const char*)io.v + src, (char*)c.V + row * (D / 2), c.Vsc + row * G, tid);
+        const float x = load_one<DT>((const char*)(val ? io.v : io.k) + (size_t)u * D * R::ES, e);
+        q4_quantize_lane(x, e, (char*)(val ? c.V : c.K) + row * (D / 2), (val ? c.Vsc : c.Ksc) + row * G);
       }
     } else {
       char* Kb = (char*)c.K + slot0 * D * R::ES;
@@ -488,6 +509,11 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
     const float s = group0_dot<DT, D, Y::EPL>(qf, io.k, u) * sh.scale;
     if (col == 0) wts[n] = s;
   }
+  // 4-bit rows: the value pass's first tile loads while the softmax runs
+  Q4Tile vfirst;
+  if constexpr (Q4) {
+    if (n > 0) q4_load<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, 0, n, vfirst);
+  }
   __syncthreads();
 
   // softmax over the n kept slots (+ the new token)
@@ -510,7 +536,7 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
   for (int j = 0; j < Y::EPL; ++j) acc[j] = 0.f;
   if constexpr (Q4) {
     float off = 0.f;
-    row_values_q4<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, wts, 0, n, acc, off);
+    row_values_q4<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, wts, 0, n, acc, off, vfirst);
 #pragma unroll
     for (int j = 0; j < Y::EPL; ++j) acc[j] = fmaf(-8.f, off, acc[j]);
   } else {
@@ -571,6 +597,8 @@ __global__ KVE_DECODE_ATTR void decode_partial_kernel(Shape sh, LayerCache c, De
   } else {
     row_logits<DT, D>(Kb, qf, sh.scale, c0, c1, lg, keep_logits ? sp.logits + slot0 : nullptr);
   }
+  Q4Tile vfirst;
+  if constexpr (Q4) q4_load<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, c0, c1, vfirst);
   __syncthreads();
   const int len = c1 - c0;
   float mx = -INFINITY;
@@ -588,7 +616,7 @@ __global__ KVE_DECODE_ATTR void decode_partial_kernel(Shape sh, LayerCache c, De
   for (int j = 0; j < Y::EPL; ++j) acc[j] = 0.f;
   if constexpr (Q4) {
     float off = 0.f;
-    row_values_q4<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, lg, c0, c1, acc, off);
+    row_values_q4<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, lg, c0, c1, acc, off, vfirst);
 #pragma unroll
     for (int j = 0; j < Y::EPL; ++j) acc[j] = fmaf(-8.f, off, acc[j]);
     stash_q4<D>(acc, red);

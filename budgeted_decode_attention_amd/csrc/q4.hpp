@@ -62,6 +62,37 @@ __device__ inline void q4_nibbles(uint32_t w, float* f) {
   f[7] = (float)(hi >> 24);
 }
 
+// Element e of a storage-dtype row as a float.
+template <int DT>
+__device__ inline float load_one(const void* row, int e) {
+  if constexpr (DT == F32) {
+    return reinterpret_cast<const float*>(row)[e];
+  } else if constexpr (DT == BF16) {
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[e] << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(row)[e]);
+  }
+}
+
+// The same quantisation with one element per lane: lanes e of a row (e in
+// [0, D), 32 consecutive lanes per group, whole waves) each hold x = element
+// e; the group's largest magnitude comes from a butterfly over its 32 lanes,
+// the code from the lane's own quotient, and eight lanes' nibbles are merged
+// into one 32-bit word, stored by the group's lanes with e % 8 == 0.
+__device__ inline void q4_quantize_lane(float x, int e, char* dst, float* dsc) {
+  float amax = fabsf(x);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const float scale = __fmul_rn(amax, kInvQMax);
+  float c = scale > 0.f ? rintf(__fdiv_rn(x, scale)) : 0.f;
+  c = fminf(fmaxf(c, -7.f), 7.f);
+  uint32_t w = (uint32_t)((int)c + 8) << ((e & 7) * 4);
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) w |= (uint32_t)__shfl_xor((int)w, o);
+  if ((e & 7) == 0) reinterpret_cast<uint32_t*>(dst)[e >> 3] = w;
+  if ((e & (kQGroup - 1)) == 0) dsc[e / kQGroup] = scale;
+}
+
 // Quantises the row of D elements at src (storage dtype) into code bytes dst
 // and scales dsc, group g = the calling lane's `g`.
 template <int DT, int D>
