@@ -39,8 +39,9 @@ constexpr int kMaxContext = 32768;     // LDS-resident per-unit slot lists
 // Layers whose slot stride exceeds kSplitAbove use the split decode.  Chunk
 // size: a layer whose heads all share one capacity splits each unit in about
 // two (half the capacity rounded up to 256, at least 512: fewer partials to
-// merge); a layer with mixed capacities uses 256-slot chunks so units of very
-// different sizes balance across the GPU.  Both can be overridden at create
+// merge); a layer with mixed capacities, or whose units fill the stride to
+// different counts (profiled and special-id heads), uses 256-slot chunks so
+// units of very different sizes balance across the GPU.  Both can be overridden at create
 // time through the environment (KVEVICT_SPLIT_ABOVE, KVEVICT_SPLIT_CHUNK) to
 // exercise either path at any size.
 constexpr int kSplitAbove = 1024;
@@ -190,6 +191,10 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
       }
       const int hc = head_capacity(p, hv, rc, c->max_context);
       if (h > 0 && hc != li.cap) li.uniform = false;
+      // profiled and special-id units fill their common stride to very
+      // different counts (chosen composite, token ids): balance them as a
+      // layer of mixed capacities
+      if (p == KVE_ADAPTIVE || p == KVE_SPECIAL) li.uniform = false;
       li.cap = std::max(li.cap, hc);
     }
     for (int b = 0; b < c->batch; ++b)
