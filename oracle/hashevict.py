@@ -95,8 +95,16 @@ class Trajectory:
 
 
 def run_unit(Q_all, K_all, V_all, W, P, B, scale, steps=None, want_prompt_out=False,
-             qsk=None, ksk=None) -> Trajectory:
-    """Prompt replay, then decode positions P..P+steps-1 with pre-attention replacement."""
+             qsk=None, ksk=None, Kc=None, Vc=None) -> Trajectory:
+    """Prompt replay, then decode positions P..P+steps-1 with pre-attention replacement.
+
+    Kc / Vc: what a cache slot holding each position reads back (lossy cache
+    formats; the full sequences otherwise).  Sketches are taken from the
+    inputs when a token enters; the step attends the cache after the
+    replacement, so token t is read from its slot like every kept token.
+    """
+    Kc = K_all if Kc is None else Kc
+    Vc = V_all if Vc is None else Vc
     N = Q_all.shape[0]
     T = N - P if steps is None else steps
     if qsk is None:
@@ -116,7 +124,7 @@ def run_unit(Q_all, K_all, V_all, W, P, B, scale, steps=None, want_prompt_out=Fa
             ev.append(-1)
             cache.append(t)
         A = np.array(cache, dtype=np.int64)
-        outs.append(attend(Q_all[t], K_all[A], V_all[A], scale)[1])
+        outs.append(attend(Q_all[t], Kc[A], Vc[A], scale)[1])
     po = causal_attention(Q_all[:P], K_all[:P], V_all[:P], scale)[1] if want_prompt_out else None
     return Trajectory(kept0, np.array(outs).reshape(T, -1), np.array(ev, dtype=np.int64),
                       np.sort(np.array(cache, dtype=np.int64)), qsk, ksk, po)

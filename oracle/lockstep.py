@@ -242,10 +242,13 @@ def check_fastgen(policy: int, Q, K, V, P, scale, gpu: GpuUnit, *, heavy=0, rece
 
 
 def check_hash(Q, K, V, Wp, P: int, B: int, scale: float, gpu: GpuUnit, steps: Optional[int] = None,
-               qsk=None, ksk=None) -> UnitReport:
+               qsk=None, ksk=None, Kc=None, Vc=None) -> UnitReport:
     """HashEvict: integer distances, so choices must match; at equal maximal distance any
     maximiser is accepted (and counted) -- the GPU uses the same oldest-first order,
-    so none is expected."""
+    so none is expected.  Kc / Vc: cache slot contents per position (lossy formats);
+    HashEvict attends the cache after the insertion, token t included."""
+    Kc = K if Kc is None else Kc
+    Vc = V if Vc is None else Vc
     rep = UnitReport()
     T = len(gpu.evicted) if steps is None else steps
     if qsk is None:
@@ -281,7 +284,7 @@ def check_hash(Q, K, V, Wp, P: int, B: int, scale: float, gpu: GpuUnit, steps: O
                 rep.failures.append(f"step {s}: evicted {g} under budget")
             cache.append(t)
         A = np.array(cache, dtype=np.int64)
-        _check_out(rep, s, gpu.out[s], attend(Q[t], K[A], V[A], scale)[1])
+        _check_out(rep, s, gpu.out[s], attend(Q[t], Kc[A], Vc[A], scale)[1])
     if not np.array_equal(np.sort(np.asarray(gpu.final_pos, dtype=np.int64)), np.sort(np.array(cache))):
         rep.failures.append("final kept set differs")
     return rep

@@ -128,3 +128,25 @@ def test_storage_dtype_slots_hold_the_input_rows():
             assert torch.equal(k[b, h, :n].cpu(), Kall[p])
             assert torch.equal(v[b, h, :n].cpu(), Vall[p])
     kv.close()
+
+
+def test_cache_rows_error_paths():
+    """ESTATE before the layer's prefill; a 4-bit cache needs the scale outputs."""
+    from budgeted_decode_attention_amd import binding
+    w = configs.scaled("opt30b_decode_h2o_q4", batch=1, heads=2, prompt=64, steps=4)
+    inp = generate_layer(w, 0, "cpu", 0)
+    kv = harness.make_cache(w, inp)
+    with pytest.raises(binding.KVEvictError) as e:
+        kv.cache_rows(0)
+    assert e.value.status == binding.KVE_ESTATE
+    gi = inp.to("cuda")
+    kv.prefill(0, gi.prompt_q, gi.prompt_k, gi.prompt_v)
+    k, v, ks, vs = kv.cache_rows(0)
+    with pytest.raises(binding.KVEvictError) as e:
+        binding.kvevict_cache_rows(kv.handle, 0, k, v, None, None)
+    assert e.value.status == binding.KVE_EINVAL
+    with pytest.raises(binding.KVEvictError) as e:
+        binding.kvevict_cache_rows(kv.handle, 1, k, v, ks, vs)
+    assert e.value.status == binding.KVE_EINVAL
+    torch.cuda.synchronize()
+    kv.close()

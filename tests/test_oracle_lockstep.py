@@ -256,3 +256,17 @@ def test_checkers_follow_the_cache_copy():
     pf = persistence.run_unit(Q, K, V, P, hh, r, w, 0.3)
     assert lockstep.check_persist(Q, K, V, P, hh, r, w, 0.3, persist_gpu_unit(pq, P), Kc=Kc, Vc=Vc).ok
     assert not lockstep.check_persist(Q, K, V, P, hh, r, w, 0.3, persist_gpu_unit(pf, P), Kc=Kc, Vc=Vc).ok
+
+
+def test_hash_checker_follows_the_cache_copy():
+    from oracle import quant
+    rng = np.random.default_rng(23)
+    N, P, d, B = 60, 40, 32, 16
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    W = rng.standard_normal((d, 32))
+    Kc, Vc = quant.roundtrip(K), quant.roundtrip(V)
+    for kc, vc, ok in ((Kc, Vc, True), (None, None, False)):
+        tr = hashevict.run_unit(Q, K, V, W, P, B, 0.3, Kc=kc, Vc=vc)
+        g = lockstep.GpuUnit(prefill_pos=tr.prefill_kept, evicted=tr.evicted.copy(), out=tr.out,
+                             final_pos=tr.final_kept, prefill_S=None, final_S=None)
+        assert lockstep.check_hash(Q, K, V, W, P, B, 0.3, g, Kc=Kc, Vc=Vc).ok == ok

@@ -132,3 +132,30 @@ def test_step_token_is_read_at_full_precision():
     np.testing.assert_allclose(tp.out[0], attend(Q[P], Ks, Vs, d ** -0.5)[1], rtol=0, atol=1e-12)
     # and the lossy copy does change what the cache attends to
     assert np.abs(tr.out - h2o.run_unit(Q, K, V, P, 5, 5, d ** -0.5).out).max() > 1e-4
+
+
+def test_hashevict_reads_every_attended_row_from_its_slot():
+    """HashEvict attends the cache after inserting token t: with 4-bit slots
+    every attended row, t included, is the slot copy; the sketches (from the
+    inputs) and hence every eviction are those of the full-precision run."""
+    from oracle import hashevict
+    rng = np.random.default_rng(13)
+    N, P, d, B = 50, 30, 64, 12
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    W = rng.standard_normal((d, 32))
+    Kc, Vc = quant.roundtrip(K), quant.roundtrip(V)
+    full = hashevict.run_unit(Q, K, V, W, P, B, d ** -0.5)
+    q4 = hashevict.run_unit(Q, K, V, W, P, B, d ** -0.5, Kc=Kc, Vc=Vc)
+    assert np.array_equal(full.evicted, q4.evicted) and np.array_equal(full.final_kept, q4.final_kept)
+    # first decode step: the cache after the replacement holds P in some slot
+    cache = list(hashevict.replay_prompt(q4.qsk, q4.ksk, P, B))
+    v = hashevict.farthest(int(q4.qsk[P]), np.array(cache, dtype=np.int64), q4.ksk)
+    cache[v] = P
+    A = np.array(cache, dtype=np.int64)
+    np.testing.assert_allclose(q4.out[0], attend(Q[P], Kc[A], Vc[A], d ** -0.5)[1], rtol=0, atol=1e-12)
+    assert np.abs(q4.out - full.out).max() > 1e-4
+    # rows the format holds exactly change nothing
+    Kg, Vg = _grid_rows(rng, N, d), _grid_rows(rng, N, d)
+    a = hashevict.run_unit(Q, Kg, Vg, W, P, B, d ** -0.5)
+    b = hashevict.run_unit(Q, Kg, Vg, W, P, B, d ** -0.5, Kc=quant.roundtrip(Kg), Vc=quant.roundtrip(Vg))
+    assert np.array_equal(a.out, b.out)
