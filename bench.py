@@ -87,8 +87,9 @@ def _oracle_unit(args):
     elif kind == "adaptive":
         ids, special, punct, rows, thr = extra
         adaptive.run_unit(Q, K, V, ids, P, special, punct, a, b, scale, rows, thr)
-    elif kind == "hash":
-        tr = hashevict.run_unit(Q, K, V, np.asarray(extra, dtype=np.float64), P, a, scale)
+    elif kind in ("hash", "hash_q4"):
+        cc = dict(Kc=quant.roundtrip(K), Vc=quant.roundtrip(V)) if kind == "hash_q4" else {}
+        tr = hashevict.run_unit(Q, K, V, np.asarray(extra, dtype=np.float64), P, a, scale, **cc)
         dt = time.perf_counter() - t0
         return dt, _hash_recovered_share(tr, Q, K, P, scale)
     else:
@@ -127,7 +128,8 @@ def cpu_baseline(w, n_units: int, workers: int):
                               (unit_ids(inp, 0), list(w.special_ids), list(w.punct_ids), w.profile_rows,
                                w.profile_threshold)))
             elif w.family == "hash":
-                tasks.append(("hash", Q, K, V, w.prompt, hv[h], 0, scale, inp.proj.float().numpy()))
+                tasks.append(("hash_q4" if w.cache_bits == 4 else "hash", Q, K, V, w.prompt, hv[h], 0, scale,
+                              inp.proj.float().numpy()))
             else:
                 tasks.append(("fastgen", Q, K, V, w.prompt, hv[h], rc[h], scale,
                               (pol[h], unit_ids(inp, 0), w.keep_ids())))
@@ -151,8 +153,8 @@ def cpu_baseline(w, n_units: int, workers: int):
                   f"(mean {sum(per) / len(per):.3f} s per unit); job time scaled by units "
                   f"({job_s:.0f} s for the whole job)",
         "hash_recovered_share": float(np.mean(extra)) if extra and w.family == "hash" else None,
-        "q4_output_rel_err": float(np.mean(extra)) if extra and w.cache_bits == 4 else None,
-        "q4_units": len(extra) if w.cache_bits == 4 else 0,
+        "q4_output_rel_err": float(np.mean(extra)) if extra and w.cache_bits == 4 and w.family != "hash" else None,
+        "q4_units": len(extra) if w.cache_bits == 4 and w.family != "hash" else 0,
     }
 
 
@@ -217,7 +219,7 @@ def decode_bytes_per_layer_step(w, ids=None) -> float:
     if w.family == "hash":
         B = w.hash_budget
         word = 8 if w.sketch_bits == 64 else 4                        # sketch word per slot
-        return w.units_per_layer * (B * d * s * 2 + B * (word + 4) + io + word)
+        return w.units_per_layer * (B * row * 2 + B * (word + 4) + io + word)
     import numpy as np
     P, T = w.prompt, w.steps
     keep = np.isin(np.asarray(ids), np.array(w.keep_ids()))           # [batch, N]

@@ -50,6 +50,18 @@ template <> struct St<F16> {
 
 template <int DT> constexpr int elem_bytes() { return 16 / St<DT>::EPL; }
 
+// Element i of a storage-dtype row as a float.
+template <int DT>
+__device__ inline float load_elem(const void* row, int i) {
+  if constexpr (DT == F32) {
+    return reinterpret_cast<const float*>(row)[i];
+  } else if constexpr (DT == BF16) {
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[i] << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(row)[i]);
+  }
+}
+
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ inline void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 

@@ -449,7 +449,7 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
         const bool val = tid >= D;
         const int e = tid - (val ? D : 0);
         const size_t row = slot0 + wslot;
-        const float x = load_one<DT>((const char*)(val ? io.v : io.k) + (size_t)u * D * R::ES, e);
+        const float x = load_elem<DT>((const char*)(val ? io.v : io.k) + (size_t)u * D * R::ES, e);
         q4_quantize_lane(x, e, (char*)(val ? c.V : c.K) + row * (D / 2), (val ? c.Vsc : c.Ksc) + row * G);
       }
     } else {

@@ -17,7 +17,12 @@
 // Sketch widths of 16, 32 and 64 bits (the page only asks for a projection
 // far narrower than the head dimension): one lane per bit, 32-bit words for
 // 16 and 32 bits, 64-bit words for 64.
+//
+// With 4-bit slots the rows entering the cache (the replay's gather, the
+// replacement at each step) are quantised; sketches always come from the
+// inputs.
 #include "common.hpp"
+#include "q4.hpp"
 
 namespace kve {
 namespace {
@@ -33,17 +38,6 @@ __device__ inline int popcnt(uint64_t x) { return __popcll(x); }
 template <int BITS> __device__ inline typename SkWord<BITS>::T ballot_field(uint64_t m, int first) {
   if constexpr (BITS == 64) return m;
   else return (typename SkWord<BITS>::T)((m >> first) & ((1ull << BITS) - 1ull));
-}
-
-template <int DT> __device__ inline float load_elem(const char* row, int i);
-template <> __device__ inline float load_elem<F32>(const char* row, int i) {
-  return reinterpret_cast<const float*>(row)[i];
-}
-template <> __device__ inline float load_elem<BF16>(const char* row, int i) {
-  return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[i] << 16);
-}
-template <> __device__ inline float load_elem<F16>(const char* row, int i) {
-  return (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(row)[i]);
 }
 
 __device__ inline double bf16_to_double(uint16_t w) { return (double)__uint_as_float((uint32_t)w << 16); }
@@ -201,6 +195,18 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
   if (tid == 0) c.count[u] = n0;
   // gather
   const size_t src0 = (size_t)u * P * D * ES;
+  if (c.q4) {
+    constexpr int G = D / kQGroup;
+    char* Kq = (char*)c.K + slot0 * (D / 2);
+    char* Vq = (char*)c.V + slot0 * (D / 2);
+    const int g = tid % G;
+    for (int s = tid / G; s < n0; s += kNT / G) {
+      const size_t so = src0 + (size_t)spos[s] * D * ES;
+      q4_store_group<DT, D>((const char*)k + so, Kq + (size_t)s * (D / 2), c.Ksc + (slot0 + s) * G, g);
+      q4_store_group<DT, D>((const char*)v + so, Vq + (size_t)s * (D / 2), c.Vsc + (slot0 + s) * G, g);
+    }
+    return;
+  }
   char* Kd = (char*)c.K + slot0 * D * ES;
   char* Vd = (char*)c.V + slot0 * D * ES;
   const int col = tid % LPR;
@@ -297,11 +303,23 @@ __global__ __launch_bounds__(kNT) void hash_evict_kernel(Shape sh, LayerCache c,
     ev = -1;
   }
   __syncthreads();
-  char* Kd = (char*)c.K + (slot0 + slot) * D * ES;
-  char* Vd = (char*)c.V + (slot0 + slot) * D * ES;
-  if (tid < LPR) {
-    st16(Kd + tid * EPL * ES, ld16((const char*)k + ((size_t)u * D + tid * EPL) * ES));
-    st16(Vd + tid * EPL * ES, ld16((const char*)v + ((size_t)u * D + tid * EPL) * ES));
+  if (c.q4) {
+    // one element per thread: threads [0, D) the key row, [D, 2D) the value row
+    constexpr int G = D / kQGroup;
+    if (tid < 2 * D) {
+      const bool val = tid >= D;
+      const int e = tid - (val ? D : 0);
+      const size_t row = slot0 + slot;
+      const float x = load_elem<DT>((const char*)(val ? v : k) + (size_t)u * D * ES, e);
+      q4_quantize_lane(x, e, (char*)(val ? c.V : c.K) + row * (D / 2), (val ? c.Vsc : c.Ksc) + row * G);
+    }
+  } else {
+    char* Kd = (char*)c.K + (slot0 + slot) * D * ES;
+    char* Vd = (char*)c.V + (slot0 + slot) * D * ES;
+    if (tid < LPR) {
+      st16(Kd + tid * EPL * ES, ld16((const char*)k + ((size_t)u * D + tid * EPL) * ES));
+      st16(Vd + tid * EPL * ES, ld16((const char*)v + ((size_t)u * D + tid * EPL) * ES));
+    }
   }
   if (tid == 0) {
     c.pos[slot0 + slot] = t;

@@ -39,9 +39,10 @@ constexpr int kMaxContext = 32768;     // LDS-resident per-unit slot lists
 // Layers whose slot stride exceeds kSplitAbove use the split decode.  Chunk
 // size: a layer whose heads all share one capacity splits each unit in about
 // two (half the capacity rounded up to 256, at least 512: fewer partials to
-// merge); a layer with mixed capacities, or whose units fill the stride to
-// different counts (profiled and special-id heads), uses 256-slot chunks so
-// units of very different sizes balance across the GPU.  Both can be overridden at create
+// merge), in about four with 4-bit slots; a layer with mixed capacities, or
+// whose units fill the stride to different counts (profiled and special-id
+// heads), uses 256-slot chunks so units of very different sizes balance
+// across the GPU.  Both can be overridden at create
 // time through the environment (KVEVICT_SPLIT_ABOVE, KVEVICT_SPLIT_CHUNK) to
 // exercise either path at any size.
 constexpr int kSplitAbove = 1024;
@@ -76,10 +77,11 @@ SplitPolicy split_policy() {
   return p;
 }
 
-int layer_chunk(const SplitPolicy& sp, int cap, bool uniform) {
+int layer_chunk(const SplitPolicy& sp, int cap, bool uniform, bool q4) {
   if (sp.chunk) return sp.chunk;
   if (!uniform) return kSplitChunkMixed;
-  return std::max(512, (cap / 2 + 255) / 256 * 256);
+  // 4-bit slots carry a third of the bytes: four chunks per unit fill the GPU
+  return std::max(512, (cap / (q4 ? 4 : 2) + 255) / 256 * 256);
 }
 
 
@@ -211,7 +213,7 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
     LayerInfo& li = (*info)[l];
     li.split = li.cap > sp.above;
     if (!li.split) continue;
-    li.chunk = layer_chunk(sp, li.cap, li.uniform);
+    li.chunk = layer_chunk(sp, li.cap, li.uniform, c->cache_bits == 4);
     li.nch = (li.cap + li.chunk - 1) / li.chunk;
     if (li.nch > kve::kMaxChunks)
       return fail(KVE_EUNSUPPORTED, "layer %d: %d slots need more than %d chunks of %d", l, li.cap,
@@ -228,8 +230,8 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
     return fail(KVE_EUNSUPPORTED, "cache_bits %d not built (0 or 4)", c->cache_bits);
   if (c->cache_bits == 4)
     for (int i = 0; i < c->layers * c->heads; ++i)
-      if (c->policy[i] != KVE_H2O && c->policy[i] != KVE_PERSIST)
-        return fail(KVE_EUNSUPPORTED, "layer %d head %d: 4-bit slots are built for H2O and PERSIST heads only",
+      if (c->policy[i] != KVE_H2O && c->policy[i] != KVE_PERSIST && c->policy[i] != KVE_HASH)
+        return fail(KVE_EUNSUPPORTED, "layer %d head %d: 4-bit slots are built for H2O, PERSIST and HASH heads only",
                     i / c->heads, i % c->heads);
   if (need_ids_tables) {
     if (!c->special_token_bitmap || !c->punct_token_bitmap || c->vocab < 1)

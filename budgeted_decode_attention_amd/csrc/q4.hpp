@@ -10,7 +10,9 @@
 // Storage: the d / 2 code bytes of a row hold element 2b of byte b in the low
 // nibble and element 2b + 1 in the high nibble, each as c + 8 (1..15); the
 // scales of a row are d / 32 consecutive floats.  A group's codes are 16
-// bytes: the quantiser writes one group per lane with one 16-byte store.
+// bytes.  The prefill gather quantises one group per lane (one 16-byte store,
+// many rows in parallel); the decode step's single new row is quantised with
+// one element per lane; the decode kernels read half a group per lane.
 #pragma once
 
 #include "common.hpp"
@@ -60,18 +62,6 @@ __device__ inline void q4_nibbles(uint32_t w, float* f) {
   f[5] = (float)((hi >> 16) & 0xffu);
   f[6] = (float)(lo >> 24);
   f[7] = (float)(hi >> 24);
-}
-
-// Element e of a storage-dtype row as a float.
-template <int DT>
-__device__ inline float load_one(const void* row, int e) {
-  if constexpr (DT == F32) {
-    return reinterpret_cast<const float*>(row)[e];
-  } else if constexpr (DT == BF16) {
-    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[e] << 16);
-  } else {
-    return (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(row)[e]);
-  }
 }
 
 // The same quantisation with one element per lane: lanes e of a row (e in

@@ -156,11 +156,13 @@ typedef struct {
    *      fl32(1/7) and codes c = rint(x / scale) clamped to [-7, 7], the
    *      quotient a correctly rounded float32 division and rint half to even
    *      (a zero scale gives codes 0); the row reads back as c * scale.
-   *      Every head of every layer must be KVE_H2O or KVE_PERSIST
-   *      (KVE_EUNSUPPORTED otherwise).  Prompt scores and the prompt output
-   *      use the inputs at full precision; rows are quantised when they enter
-   *      the cache, and the step-t query uses token t's own key and value
-   *      unquantised at that step. */
+   *      Every head of every layer must be KVE_H2O, KVE_PERSIST or KVE_HASH
+   *      (KVE_EUNSUPPORTED otherwise).  Prompt scores, sketches and the
+   *      prompt output use the inputs at full precision; rows are quantised
+   *      when they enter the cache.  H2O and PERSIST steps use token t's own
+   *      key and value unquantised at step t; a HASH step attends the cache
+   *      after the replacement, so token t is read from its 4-bit slot like
+   *      every kept token. */
   int32_t cache_bits;
 } kve_config;
 

@@ -104,7 +104,7 @@ def check_unit(w: Workload, inp_cpu: LayerInputs, r: GpuRun, b: int, h: int, pol
         rep = lockstep.check_h2o(Q, K, V, P, hh, rr, sc, g, steps=T, Kc=Kc, Vc=Vc)
     elif p == HASH:
         Wp = inp_cpu.proj.float().double().cpu().numpy()
-        rep = lockstep.check_hash(Q, K, V, Wp, P, hh, sc, g, steps=T)
+        rep = lockstep.check_hash(Q, K, V, Wp, P, hh, sc, g, steps=T, Kc=Kc, Vc=Vc)
     elif p == PERSIST:
         win = w.history_window if history is None else history[h]
         rep = lockstep.check_persist(Q, K, V, P, hh, rr, win, sc, g, steps=T, Kc=Kc, Vc=Vc)

@@ -166,6 +166,8 @@ def test_64_bit_sketches_cap_the_budget():
     (dict(cache_bits=8), binding.KVE_EUNSUPPORTED),
     (dict(cache_bits=4, policy=[2, 1, 1], heavy=[0, 10, 10], recent=[5, 5, 5]), binding.KVE_EUNSUPPORTED),
     (dict(cache_bits=4, policy=[0, 1, 1], heavy=[0, 10, 10], recent=[0, 5, 5]), binding.KVE_EUNSUPPORTED),
+    (dict(cache_bits=4, policy=[4, 1, 1], heavy=[50, 10, 10], recent=[0, 5, 5],
+          proj=torch.zeros((128, 32), dtype=torch.bfloat16)), binding.KVE_OK),
 ])
 def test_four_bit_slots_configs(over, status):
     c, keep = cfg(**over)
@@ -175,11 +177,12 @@ def test_four_bit_slots_configs(over, status):
 def test_four_bit_slots_shrink_the_workspace():
     # per slot: d / 2 code bytes and d / 32 float scales for K and for V
     # (160 bytes at d 128) in place of 2 * d * 2 bytes of bf16 rows (512)
-    big = dict(max_context=4096, heavy=[1000, 1000, 1000], recent=[1000, 1000, 1000])
+    # (a fused-decode size: no split scratch, whose chunking differs with the format)
+    big = dict(max_context=4096, heavy=[500, 500, 500], recent=[500, 500, 500])
     s16, n16 = status_of(cfg(**big)[0])
     s4, n4 = status_of(cfg(cache_bits=4, **big)[0])
     assert s16 == s4 == binding.KVE_OK
-    units, cap = 2 * 3, 2000
+    units, cap = 2 * 3, 1000
     assert abs((n16 - n4) - units * cap * (512 - 160)) < 16 * 256
 
 

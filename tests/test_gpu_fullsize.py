@@ -114,3 +114,8 @@ def test_opt30b_q4_layer_full_size():
     oracle with quantised cache rows."""
     rep = run_full("opt30b_decode_h2o_q4", 6)
     assert rep.decisions == 6 * 256
+
+
+def test_hashevict_q4_full_size():
+    rep = run_full("hashevict_lsh_q4", 4)
+    assert rep.decisions == 4 * 1024

@@ -150,3 +150,26 @@ def test_cache_rows_error_paths():
     assert e.value.status == binding.KVE_EINVAL
     torch.cuda.synchronize()
     kv.close()
+
+
+def test_q4_hash_scaled(decode_path):
+    """HashEvict with 4-bit slots: evictions bit-exact (sketches from the
+    inputs), outputs against the oracle attending the slot copies."""
+    w = dataclasses.replace(configs.scaled("hashevict_lsh", batch=2, heads=3, prompt=600, steps=70), cache_bits=4)
+    rep, _ = run_and_check(w)
+    assert rep.adopted == 0 and rep.decisions > 0
+
+
+def test_q4_hash_fp16_d64(decode_path):
+    w = dataclasses.replace(configs.scaled("hashevict_lsh", batch=1, heads=3, prompt=300, steps=50),
+                            dtype="f16", head_dim=64, cache_bits=4)
+    run_and_check(w)
+
+
+def test_q4_hash_slot_codes_are_bit_exact():
+    w = dataclasses.replace(configs.scaled("hashevict_lsh", batch=2, heads=2, prompt=300, steps=40), cache_bits=4)
+    inp = generate_layer(w, 0, "cpu", 4)
+    kv = harness.make_cache(w, inp)
+    harness.run_layer(kv, inp.to("cuda"))
+    check_slot_bytes(w, inp, kv, [(b, h) for b in range(w.batch) for h in range(w.heads)])
+    kv.close()

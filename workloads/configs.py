@@ -13,8 +13,9 @@ Beside the five workloads, ``opt30b_decode_persist`` runs the OPT-30B-shaped
 decode under the persistence-count rule (the Scissorhands reading) with the
 same 20% budget, so the two scoring rules are measured on one shape;
 ``llama65b_fastgen_profiled`` lets FastGen's profile choose each unit's
-composite; ``opt30b_decode_h2o_q4`` is the OPT-30B-shaped H2O decode with
-4-bit cache slots (eviction combined with quantisation).
+composite; ``opt30b_decode_h2o_q4`` and ``hashevict_lsh_q4`` are the
+OPT-30B-shaped H2O decode and the HashEvict workload with 4-bit cache slots
+(eviction combined with quantisation).
 """
 
 from __future__ import annotations
@@ -176,8 +177,14 @@ _add(Workload(
                 "bf16 inputs, P=2048, T=256, 20% budget (204 + 204); K/V rows in groups of 32 with a "
                 "float32 scale and 4-bit codes"))
 
+_add(Workload(
+    name="hashevict_lsh_q4", index=9, layers=1, batch=16, heads=32, head_dim=128, dtype="bf16",
+    prompt=8192, steps=1024, family="hash", structure="clusters", cache_bits=4, **_hash(8192),
+    description="HashEvict with 4-bit cache slots: batch 16, 32 heads, d=128, bf16 inputs, P=8192, T=1024, "
+                "budget 50%, 32-bit sketches from the full-precision inputs"))
+
 ORDER = ["tiny_h2o", "opt6.7b_layer_h2o", "opt30b_decode_h2o", "llama65b_fastgen", "hashevict_lsh"]
-NEXT = ["opt30b_decode_persist", "llama65b_fastgen_profiled", "opt30b_decode_h2o_q4"]
+NEXT = ["opt30b_decode_persist", "llama65b_fastgen_profiled", "opt30b_decode_h2o_q4", "hashevict_lsh_q4"]
 
 
 def get(name: str) -> Workload:
