@@ -77,11 +77,18 @@ SplitPolicy split_policy() {
   return p;
 }
 
-int layer_chunk(const SplitPolicy& sp, int cap, bool uniform, bool q4) {
+int layer_chunk(const SplitPolicy& sp, int cap, int head_dim, bool uniform, bool q4) {
   if (sp.chunk) return sp.chunk;
-  if (!uniform) return kSplitChunkMixed;
   // 4-bit slots carry a third of the bytes: four chunks per unit fill the GPU
-  return std::max(512, (cap / (q4 ? 4 : 2) + 255) / 256 * 256);
+  int chunk = uniform ? std::max(512, (cap / (q4 ? 4 : 2) + 255) / 256 * 256) : kSplitChunkMixed;
+  // grow it (256 slots at a time) until a unit's chunks fit the combine
+  // kernel: at most kMaxChunks partials, and the partials plus one weight per
+  // slot within kMaxSplitLds.  A single chunk always fits (cap <= kMaxContext).
+  for (;;) {
+    const size_t nch = (size_t)(cap + chunk - 1) / chunk;
+    if (nch <= (size_t)kve::kMaxChunks && (nch * (head_dim + 2) + cap) * 4 <= kMaxSplitLds) return chunk;
+    chunk += 256;
+  }
 }
 
 
@@ -213,7 +220,7 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
     LayerInfo& li = (*info)[l];
     li.split = li.cap > sp.above;
     if (!li.split) continue;
-    li.chunk = layer_chunk(sp, li.cap, li.uniform, c->cache_bits == 4);
+    li.chunk = layer_chunk(sp, li.cap, c->head_dim, li.uniform, c->cache_bits == 4);
     li.nch = (li.cap + li.chunk - 1) / li.chunk;
     if (li.nch > kve::kMaxChunks)
       return fail(KVE_EUNSUPPORTED, "layer %d: %d slots need more than %d chunks of %d", l, li.cap,

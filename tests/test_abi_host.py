@@ -189,3 +189,14 @@ def test_four_bit_slots_shrink_the_workspace():
 def test_cache_rows_rejects_a_null_handle():
     lib = binding.load_library()
     assert lib.kvevict_cache_rows(None, 0, None, None, None, None, None) == binding.KVE_EINVAL
+
+
+def test_mixed_layer_at_max_context_is_accepted():
+    """A layer mixing a FULL head (stride = the whole context) with other
+    policies at max_context 32768: the split decode's chunk grows until a
+    unit's chunks fit the combine kernel, so the layer is accepted."""
+    c, keep = cfg(batch=1, heads=4, max_context=32768, policy=[0, 2, 3, 1], heavy=[0, 0, 0, 3276],
+                  recent=[0, 8190, 0, 8190], keep_ids=list(range(14)), vocab=32000)
+    s, n = status_of(c)
+    assert s == binding.KVE_OK, binding.load_library().kvevict_last_error()
+    assert n > 0
