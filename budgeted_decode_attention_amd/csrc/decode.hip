@@ -194,90 +194,120 @@ __device__ inline uint2 ld_codes(const void* p) {
 #endif
 }
 
-// One load tile of 4-bit rows: kUnrollQ4 rows per thread (rows b + i RPI + rg
-// of [b, r1)), their 8 code bytes and group scale; rows past r1 read as zero.
+// One load tile of 4-bit rows: kUnrollQ4 rows per thread (rows b + i RPI +
+// rg), their 8 code bytes and group scale.  Rows past rlast re-read row rlast
+// (the last row of the range, or row 0 of an empty one), so every load is
+// issued unconditionally and the compiler waits only for the tile being
+// used, not for the one in flight behind it; callers mask those rows.
 struct Q4Tile {
   uint2 raw[kUnrollQ4];
   float sc[kUnrollQ4];
 };
 
 template <int D>
-__device__ inline void q4_load(const char* Xq, const float* Xs, int b, int r1, Q4Tile& t) {
+__device__ inline void q4_load(const char* Xq, const float* Xs, int b, int rlast, Q4Tile& t) {
+  using Q = Q4Rows<D>;
+  const int col = threadIdx.x % Q::LPR, rg = threadIdx.x / Q::LPR;
+#pragma unroll
+  for (int i = 0; i < kUnrollQ4; ++i) {
+    const int r = min(b + i * Q::RPI + rg, rlast);
+    t.raw[i] = ld_codes(Xq + (size_t)r * Q::CB + col * 8);
+    t.sc[i] = ld_scale(Xs + (size_t)r * Q::G + col / 2);
+  }
+}
+
+// Logits of one loaded tile (rows b + i RPI + rg) into lg[r - r0] and, when
+// lgg is non-null, lgg[r], for r < r1.
+template <int D>
+__device__ inline void q4_tile_logits(const Q4Tile& t, const float* qf, float qsum, float scale, int b, int r0,
+                                      int r1, float* lg, float* lgg) {
   using Q = Q4Rows<D>;
   const int col = threadIdx.x % Q::LPR, rg = threadIdx.x / Q::LPR;
 #pragma unroll
   for (int i = 0; i < kUnrollQ4; ++i) {
     const int r = b + i * Q::RPI + rg;
-    t.raw[i] = r < r1 ? ld_codes(Xq + (size_t)r * Q::CB + col * 8) : make_uint2(0, 0);
-    t.sc[i] = r < r1 ? ld_scale(Xs + (size_t)r * Q::G + col / 2) : 0.f;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      float f[8];
+      q4_nibbles(w == 0 ? t.raw[i].x : t.raw[i].y, f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s = fmaf(qf[w * 8 + j], f[j], s);
+    }
+    s = group_sum<Q::LPR>(t.sc[i] * fmaf(-8.f, qsum, s)) * scale;
+    if (col == 0 && r < r1) {
+      lg[r - r0] = s;
+      if (lgg) lgg[r] = s;
+    }
   }
 }
 
 // Logits of 4-bit rows [r0, r1): Kq = the unit's code bytes, Ks its scales;
-// qf = this lane's 16 query elements, qsum their sum.  Double-buffered: the
-// next tile's loads are in flight while the current one is reduced.
+// qf = this lane's 16 query elements, qsum their sum.  Two register tiles in
+// ping-pong: the next tile's loads are in flight while the current one is
+// reduced, and every pass of the loop issues both tiles' loads, so the state
+// at its back edge is the one at its entry.
 template <int D>
 __device__ inline void row_logits_q4(const char* Kq, const float* Ks, const float* qf, float qsum, float scale,
                                      int r0, int r1, float* lg, float* lgg) {
+  constexpr int STEP = Q4Rows<D>::RPI * kUnrollQ4;
+  const int rlast = max(r1 - 1, 0);
+  const int ntile = r1 > r0 ? (r1 - r0 + STEP - 1) / STEP : 0;
+  Q4Tile ta, tb;
+  q4_load<D>(Kq, Ks, r0, rlast, ta);
+  int k = 0;
+  for (; k + 1 < ntile; k += 2) {
+    const int b = r0 + k * STEP;
+    q4_load<D>(Kq, Ks, b + STEP, rlast, tb);
+    q4_tile_logits<D>(ta, qf, qsum, scale, b, r0, r1, lg, lgg);
+    q4_load<D>(Kq, Ks, b + 2 * STEP, rlast, ta);   // past the range: re-reads row rlast
+    q4_tile_logits<D>(tb, qf, qsum, scale, b + STEP, r0, r1, lg, lgg);
+  }
+  if (k < ntile) q4_tile_logits<D>(ta, qf, qsum, scale, r0 + k * STEP, r0, r1, lg, lgg);
+}
+
+// acc += w[r - r0] * scale_r * (c + 8) over one loaded tile's rows r < r1;
+// off += w[r - r0] * scale_r.
+template <int D>
+__device__ inline void q4_tile_values(const Q4Tile& t, const float* w, int b, int r0, int r1, float* acc,
+                                      float& off) {
   using Q = Q4Rows<D>;
-  constexpr int STEP = Q::RPI * kUnrollQ4;
-  const int col = threadIdx.x % Q::LPR, rg = threadIdx.x / Q::LPR;
-  Q4Tile cur;
-  if (r0 < r1) q4_load<D>(Kq, Ks, r0, r1, cur);
-  for (int b = r0; b < r1; b += STEP) {
-    Q4Tile nxt;
-    const bool more = b + STEP < r1;           // uniform
-    if (more) q4_load<D>(Kq, Ks, b + STEP, r1, nxt);
+  const int rg = threadIdx.x / Q::LPR;
 #pragma unroll
-    for (int i = 0; i < kUnrollQ4; ++i) {
-      const int r = b + i * Q::RPI + rg;
-      float s = 0.f;
+  for (int i = 0; i < kUnrollQ4; ++i) {
+    const int r = b + i * Q::RPI + rg;
+    const float ws = r < r1 ? w[r - r0] * t.sc[i] : 0.f;
+    off += ws;
 #pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        float f[8];
-        q4_nibbles(w == 0 ? cur.raw[i].x : cur.raw[i].y, f);
+    for (int k = 0; k < 2; ++k) {
+      float f[8];
+      q4_nibbles(k == 0 ? t.raw[i].x : t.raw[i].y, f);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s = fmaf(qf[w * 8 + j], f[j], s);
-      }
-      s = group_sum<Q::LPR>(cur.sc[i] * fmaf(-8.f, qsum, s)) * scale;
-      if (col == 0 && r < r1) {
-        lg[r - r0] = s;
-        if (lgg) lgg[r] = s;
-      }
+      for (int j = 0; j < 8; ++j) acc[k * 8 + j] = fmaf(ws, f[j], acc[k * 8 + j]);
     }
-    if (more) cur = nxt;
   }
 }
 
 // acc (this lane's 16 columns) += sum over rows [r0, r1) of w[r - r0] * scale_r
 // * (c + 8); off += sum of w[r - r0] * scale_r (the caller subtracts 8 * off).
-// `first` is the tile of rows from r0, already loaded by the caller.
+// `first` is the tile of rows from r0, already loaded by the caller with
+// q4_load(.., r0, max(r1 - 1, 0), ..); pipelined like row_logits_q4.
 template <int D>
 __device__ inline void row_values_q4(const char* Vq, const float* Vs, const float* w, int r0, int r1, float* acc,
                                      float& off, const Q4Tile& first) {
-  using Q = Q4Rows<D>;
-  constexpr int STEP = Q::RPI * kUnrollQ4;
-  const int rg = threadIdx.x / Q::LPR;
-  Q4Tile cur = first;
-  for (int b = r0; b < r1; b += STEP) {
-    Q4Tile nxt;
-    const bool more = b + STEP < r1;           // uniform
-    if (more) q4_load<D>(Vq, Vs, b + STEP, r1, nxt);
-#pragma unroll
-    for (int i = 0; i < kUnrollQ4; ++i) {
-      const int r = b + i * Q::RPI + rg;
-      const float ws = r < r1 ? w[r - r0] * cur.sc[i] : 0.f;
-      off += ws;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        float f[8];
-        q4_nibbles(k == 0 ? cur.raw[i].x : cur.raw[i].y, f);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[k * 8 + j] = fmaf(ws, f[j], acc[k * 8 + j]);
-      }
-    }
-    if (more) cur = nxt;
+  constexpr int STEP = Q4Rows<D>::RPI * kUnrollQ4;
+  const int rlast = max(r1 - 1, 0);
+  const int ntile = r1 > r0 ? (r1 - r0 + STEP - 1) / STEP : 0;
+  Q4Tile ta = first, tb;
+  int k = 0;
+  for (; k + 1 < ntile; k += 2) {
+    const int b = r0 + k * STEP;
+    q4_load<D>(Vq, Vs, b + STEP, rlast, tb);
+    q4_tile_values<D>(ta, w, b, r0, r1, acc, off);
+    q4_load<D>(Vq, Vs, b + 2 * STEP, rlast, ta);   // past the range: re-reads row rlast
+    q4_tile_values<D>(tb, w, b + STEP, r0, r1, acc, off);
   }
+  if (k < ntile) q4_tile_values<D>(ta, w, r0 + k * STEP, r0, r1, acc, off);
 }
 
 // Folds the row groups of each 16-lane row (lanes with equal column, LPR
@@ -512,7 +542,7 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
   // 4-bit rows: the value pass's first tile loads while the softmax runs
   Q4Tile vfirst;
   if constexpr (Q4) {
-    if (n > 0) q4_load<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, 0, n, vfirst);
+    q4_load<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, 0, max(n - 1, 0), vfirst);
   }
   __syncthreads();
 
@@ -598,7 +628,7 @@ __global__ KVE_DECODE_ATTR void decode_partial_kernel(Shape sh, LayerCache c, De
     row_logits<DT, D>(Kb, qf, sh.scale, c0, c1, lg, keep_logits ? sp.logits + slot0 : nullptr);
   }
   Q4Tile vfirst;
-  if constexpr (Q4) q4_load<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, c0, c1, vfirst);
+  if constexpr (Q4) q4_load<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, c0, max(c1 - 1, 0), vfirst);
   __syncthreads();
   const int len = c1 - c0;
   float mx = -INFINITY;
