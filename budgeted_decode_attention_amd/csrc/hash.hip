@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
   constexpr int LPR = D / EPL;
   constexpr int RPI = kNT / LPR;
   extern __shared__ __attribute__((aligned(16))) char lds[];   // sk[B] then pos[B]
-  __shared__ uint64_t kscr[kNT / kWave];
+  __shared__ uint64_t kscr[2][kNT / kWave];
   const int u = ul.ids[blockIdx.x];
   const int tid = threadIdx.x;
   const HeadMeta m = c.meta[u];
@@ -153,33 +153,59 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
     spos[s] = s;
   }
   __syncthreads();
-  // key = distance << 48 | (2^24 - 1 - position) << 24 | slot: the maximum is
-  // the farthest key, then the oldest position
+  // key = distance << 16 | (65535 - position): the maximum is the farthest
+  // key, then the oldest position.  Positions in the cache are distinct and
+  // below 65536, so the maximum is unique and its lane names the slot.
+  const int lane = tid & (kWave - 1);
   for (int i = B; i < P; ++i) {
     const SW qs = qq[i];
-    uint64_t best = 0;
-    for (int s = tid; s < B; s += kNT) {
-      const uint64_t key = ((uint64_t)popcnt(qs ^ ssk[s]) << 48) |
-                           ((uint64_t)(0xFFFFFF - spos[s]) << 24) | (uint64_t)s;
-      best = key > best ? key : best;
-    }
+    uint32_t best = 0;
+    int bslot = 0;
+    // four slots per thread per round: their LDS reads are issued together
+    for (int s0 = tid; s0 < B; s0 += 4 * kNT) {
+      SW sk[4];
+      int ps[4];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint64_t ot = __shfl_xor(best, o);
-      best = ot > best ? ot : best;
+      for (int j = 0; j < 4; ++j) {
+        const int s = min(s0 + j * kNT, B - 1);
+        sk[j] = ssk[s];
+        ps[j] = spos[s];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t key = ((uint32_t)popcnt(qs ^ sk[j]) << 16) | (uint32_t)(0xFFFF - ps[j]);
+        if (s0 + j * kNT < B && key > best) {
+          best = key;
+          bslot = s0 + j * kNT;
+        }
+      }
     }
-    if ((tid & (kWave - 1)) == 0) kscr[tid / kWave] = best;
+    // wave maximum: DPP within each 16-lane row, then the four rows' values
+    uint32_t wm = best;
+    wm = max(wm, (uint32_t)__builtin_amdgcn_mov_dpp((int)wm, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+    wm = max(wm, (uint32_t)__builtin_amdgcn_mov_dpp((int)wm, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+    wm = max(wm, (uint32_t)__builtin_amdgcn_mov_dpp((int)wm, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    wm = max(wm, (uint32_t)__builtin_amdgcn_mov_dpp((int)wm, 0x140, 0xF, 0xF, false));   // row_mirror
+    wm = max(max((uint32_t)__builtin_amdgcn_readlane((int)wm, 0), (uint32_t)__builtin_amdgcn_readlane((int)wm, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)wm, 32), (uint32_t)__builtin_amdgcn_readlane((int)wm, 48)));
+    const uint64_t won = __ballot(best == wm);  // exactly one lane
+    const int wl = __builtin_ctzll(won);
+    const int wslot = __builtin_amdgcn_readlane(bslot, wl);
+    // one barrier per step: the wave maxima alternate between two buffers,
+    // every thread reduces them, and the replaced slot is rewritten by the
+    // thread whose scan owns it (slot % NT), which alone reads it later
+    if (lane == 0) kscr[i & 1][tid / kWave] = ((uint64_t)wm << 32) | (uint32_t)wslot;
     __syncthreads();
-    if (tid == 0) {
-      uint64_t bb = kscr[0];
+    uint64_t bb = kscr[i & 1][0];
 #pragma unroll
-      for (int w = 1; w < kNT / kWave; ++w) bb = kscr[w] > bb ? kscr[w] : bb;
-      const int slot = (int)(bb & 0xFFFFFF);
+    for (int w = 1; w < kNT / kWave; ++w) bb = kscr[i & 1][w] > bb ? kscr[i & 1][w] : bb;
+    const int slot = (int)(bb & 0xFFFFFFFFu);
+    if (slot % kNT == tid) {
       ssk[slot] = kq[i];
       spos[slot] = i;
     }
-    __syncthreads();
   }
+  __syncthreads();                              // every slot's last write is visible
   const size_t slot0 = (size_t)u * c.cap;
   for (int s = tid; s < c.cap; s += kNT) {
     int32_t p = -1;
