@@ -126,6 +126,32 @@ __global__ __launch_bounds__(kNT) void sketch_rows_kernel(Shape sh, UnitList ul,
   }
 }
 
+// Eviction keys: distance << 16 | (65535 - position).  The maximum is the
+// farthest key, then the oldest position; positions in a cache are distinct
+// and below 65536, so a non-zero maximum is unique.  Lanes without a
+// candidate hold 0.
+__device__ inline uint32_t evict_key(uint32_t dist, int pos) { return (dist << 16) | (uint32_t)(0xFFFF - pos); }
+__device__ inline int key_position(uint32_t key) { return 0xFFFF - (int)(key & 0xFFFF); }
+
+// The wave's largest key (every lane receives it): DPP within each 16-lane
+// row, then the four rows' values.
+__device__ inline uint32_t wave_max_key(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+// (wave maximum << 32 | the slot of the lane that holds it); a wave with no
+// candidate reports key 0.
+__device__ inline uint64_t wave_best(uint32_t best, int bslot) {
+  const uint32_t wm = wave_max_key(best);
+  const int wl = __builtin_ctzll(__ballot(best == wm));
+  return ((uint64_t)wm << 32) | (uint32_t)__builtin_amdgcn_readlane(bslot, wl);
+}
+
 // Prompt replay for one HASH unit per workgroup; slot state in LDS.
 template <int DT, int D, int BITS>
 __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c, UnitList ul, int P,
@@ -153,9 +179,6 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
     spos[s] = s;
   }
   __syncthreads();
-  // key = distance << 16 | (65535 - position): the maximum is the farthest
-  // key, then the oldest position.  Positions in the cache are distinct and
-  // below 65536, so the maximum is unique and its lane names the slot.
   const int lane = tid & (kWave - 1);
   for (int i = B; i < P; ++i) {
     const SW qs = qq[i];
@@ -173,28 +196,18 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t key = ((uint32_t)popcnt(qs ^ sk[j]) << 16) | (uint32_t)(0xFFFF - ps[j]);
+        const uint32_t key = evict_key(popcnt(qs ^ sk[j]), ps[j]);
         if (s0 + j * kNT < B && key > best) {
           best = key;
           bslot = s0 + j * kNT;
         }
       }
     }
-    // wave maximum: DPP within each 16-lane row, then the four rows' values
-    uint32_t wm = best;
-    wm = max(wm, (uint32_t)__builtin_amdgcn_mov_dpp((int)wm, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
-    wm = max(wm, (uint32_t)__builtin_amdgcn_mov_dpp((int)wm, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
-    wm = max(wm, (uint32_t)__builtin_amdgcn_mov_dpp((int)wm, 0x141, 0xF, 0xF, false));   // row_half_mirror
-    wm = max(wm, (uint32_t)__builtin_amdgcn_mov_dpp((int)wm, 0x140, 0xF, 0xF, false));   // row_mirror
-    wm = max(max((uint32_t)__builtin_amdgcn_readlane((int)wm, 0), (uint32_t)__builtin_amdgcn_readlane((int)wm, 16)),
-             max((uint32_t)__builtin_amdgcn_readlane((int)wm, 32), (uint32_t)__builtin_amdgcn_readlane((int)wm, 48)));
-    const uint64_t won = __ballot(best == wm);  // exactly one lane
-    const int wl = __builtin_ctzll(won);
-    const int wslot = __builtin_amdgcn_readlane(bslot, wl);
+    const uint64_t wb = wave_best(best, bslot);
     // one barrier per step: the wave maxima alternate between two buffers,
     // every thread reduces them, and the replaced slot is rewritten by the
     // thread whose scan owns it (slot % NT), which alone reads it later
-    if (lane == 0) kscr[i & 1][tid / kWave] = ((uint64_t)wm << 32) | (uint32_t)wslot;
+    if (lane == 0) kscr[i & 1][tid / kWave] = wb;
     __syncthreads();
     uint64_t bb = kscr[i & 1][0];
 #pragma unroll
@@ -279,7 +292,8 @@ __global__ __launch_bounds__(kNT) void hash_evict_kernel(Shape sh, LayerCache c,
   int slot, ev;
   if (n >= B) {
     const SW qs = sk2[0];
-    uint64_t best = 0;
+    uint32_t best = 0;
+    int bslot = 0;
     // PER slots per 16-byte load of sketches (4 of 32 bits, 2 of 64) and the
     // matching load of positions when the unit's first slot is aligned
     // (slot0 % PER == 0); the remainder, or every slot otherwise, one at a time
@@ -302,28 +316,28 @@ __global__ __launch_bounds__(kNT) void hash_evict_kernel(Shape sh, LayerCache c,
       }
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
-        const uint64_t key = ((uint64_t)popcnt(qs ^ av[j]) << 48) | ((uint64_t)(0xFFFFFF - pv[j]) << 24) |
-                             (uint64_t)(sv + j);
-        best = key > best ? key : best;
+        const uint32_t key = evict_key(popcnt(qs ^ av[j]), pv[j]);
+        if (key > best) {
+          best = key;
+          bslot = sv + j;
+        }
       }
     }
     for (int s = nv + tid; s < n; s += kNT) {
-      const uint64_t key = ((uint64_t)popcnt(qs ^ skp[s]) << 48) | ((uint64_t)(0xFFFFFF - psp[s]) << 24) |
-                           (uint64_t)s;
-      best = key > best ? key : best;
+      const uint32_t key = evict_key(popcnt(qs ^ skp[s]), psp[s]);
+      if (key > best) {
+        best = key;
+        bslot = s;
+      }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint64_t ot = __shfl_xor(best, o);
-      best = ot > best ? ot : best;
-    }
-    if ((tid & (kWave - 1)) == 0) kscr[tid / kWave] = best;
+    const uint64_t wb = wave_best(best, bslot);
+    if ((tid & (kWave - 1)) == 0) kscr[tid / kWave] = wb;
     __syncthreads();
     uint64_t bb = kscr[0];
 #pragma unroll
     for (int w = 1; w < kNT / kWave; ++w) bb = kscr[w] > bb ? kscr[w] : bb;
-    slot = (int)(bb & 0xFFFFFF);
-    ev = 0xFFFFFF - (int)((bb >> 24) & 0xFFFFFF);
+    slot = (int)(bb & 0xFFFFFFFFu);
+    ev = key_position((uint32_t)(bb >> 32));
   } else {
     slot = n;
     ev = -1;
