@@ -346,7 +346,7 @@ __device__ inline void stash_groups(const float* acc, float* red) {
 // n kept slots (read for H2O and PERSIST heads only), e_new = exp(l_t - M),
 // L = the sum of every weight, invL = 1 / L.  Control flow is uniform over
 // the workgroup; contains barriers.
-template <int DT, int D, bool Q4>
+template <int DT, int D, bool Q4, int RND = 4>
 __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const DecodeIO& io, const HeadMeta& m,
                                    int u, int n, const float* wts, float e_new, double L, double invL,
                                    MinKey* kscr) {
@@ -364,19 +364,19 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
     const int lim = t - m.recent;              // candidates: position <= t - recent
     const bool prot_new = m.ids != IDS_NONE && id_protected(m.ids, io.sets, io.ids[u / sh.heads]);
     MinKey best{INFINITY, INT32_MAX, INT32_MAX};
-    // four slots per thread per round: their score/position loads are issued
-    // together, so a large cache costs n / (4 NT) load latencies, not n / NT
-    for (int r0 = tid; r0 < n; r0 += 4 * kNT) {
-      double sv[4];
-      int pv[4];
+    // RND slots per thread per round: their score/position loads are issued
+    // together, so a large cache costs n / (RND NT) load latencies, not n / NT
+    for (int r0 = tid; r0 < n; r0 += RND * kNT) {
+      double sv[RND];
+      int pv[RND];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < RND; ++i) {
         const int r = r0 + i * kNT;
         sv[i] = r < n ? c.S[slot0 + r] : 0.0;
         pv[i] = r < n ? c.pos[slot0 + r] : 0;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < RND; ++i) {
         const int r = r0 + i * kNT;
         if (r < n) {
           const double s = sv[i] + (double)wts[r] * invL;
@@ -416,17 +416,17 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
     const double nA = (double)(n + 1);
     unsigned long long* Hs = reinterpret_cast<unsigned long long*>(c.S) + slot0;
     MinKey best{INFINITY, INT32_MAX, INT32_MAX};
-    for (int r0 = tid; r0 < n; r0 += 4 * kNT) {
-      unsigned long long hv[4];
-      int pv[4];
+    for (int r0 = tid; r0 < n; r0 += RND * kNT) {
+      unsigned long long hv[RND];
+      int pv[RND];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < RND; ++i) {
         const int r = r0 + i * kNT;
         hv[i] = r < n ? Hs[r] : 0ull;
         pv[i] = r < n ? c.pos[slot0 + r] : 0;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < RND; ++i) {
         const int r = r0 + i * kNT;
         if (r < n) {
           const unsigned long long piv = (double)wts[r] * nA >= L ? 1ull : 0ull;
@@ -716,12 +716,13 @@ __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, De
   if (m.policy == H2O || m.policy == PERSIST) {
     // exact weights of every kept slot, recomputed from the stored logits
     const float* lgs = sp.logits + slot0;
-    for (int r0 = tid; r0 < n; r0 += 4 * kNT) {
-      float lv[4];
+    // eight slots per thread per round: a 2,048-slot cache in one load latency
+    for (int r0 = tid; r0 < n; r0 += 8 * kNT) {
+      float lv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lv[i] = r0 + i * kNT < n ? lgs[r0 + i * kNT] : 0.f;
+      for (int i = 0; i < 8; ++i) lv[i] = r0 + i * kNT < n ? lgs[r0 + i * kNT] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
         const int r = r0 + i * kNT;
         if (r < n) {
           const float w = expf(lv[i] - M);
@@ -746,7 +747,7 @@ __global__ KVE_DECODE_ATTR void decode_combine_kernel(Shape sh, LayerCache c, De
     }
     io.out[(size_t)u * D + i] = (float)((double)s * invL);
   }
-  policy_step<DT, D, Q4>(sh, c, io, m, u, n, wts, e_new, L, invL, kscr);
+  policy_step<DT, D, Q4, 8>(sh, c, io, m, u, n, wts, e_new, L, invL, kscr);
 }
 
 hipError_t set_lds(const void* fn, size_t lds) {
