@@ -473,10 +473,16 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
 #pragma unroll
     for (int r = 0; r < 4; ++r) cs[mb][r] = ms[mb][r] = 0.0;
 
-  // lse of one query, in log2 units as a float pair
-  auto lse2 = [&](int i, float& hi, float& lo) {
+  // lse of one query as loaded (natural-log float pair), then in log2 units
+  // as a float pair; the loads for the next tile are issued before the
+  // current tile is computed and converted only after it
+  auto lse_load = [&](int i, float& a, float& b) {
     const int qi = min(i, P - 1);
-    const double L2 = ((double)lse[((size_t)u * P + qi) * 2] + (double)lse[((size_t)u * P + qi) * 2 + 1]) * kLog2e;
+    a = lse[((size_t)u * P + qi) * 2];
+    b = lse[((size_t)u * P + qi) * 2 + 1];
+  };
+  auto lse2 = [&](float a, float b, float& hi, float& lo) {
+    const double L2 = ((double)a + (double)b) * kLog2e;
     hi = (float)L2;
     lo = (float)(L2 - (double)hi);
   };
@@ -486,11 +492,13 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
   auto thr = [&](int i) { return (float)(-log2((double)(i + 1))); };
   uint64_t bits[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
   TileRegs<D> nxt;
-  float nh = 0.f, nl = 0.f, nt = 0.f;
+  float la = 0.f, lb = 0.f;                     // the next tile's lse pair, as loaded
   load_tile<D>(nxt, qbase, i_first, P);
   store_tile<D>(nxt, Qs[0]);
   if (threadIdx.x < kTile) {
-    lse2(i_first + threadIdx.x, nh, nl);
+    float a, b, nh, nl;
+    lse_load(i_first + threadIdx.x, a, b);
+    lse2(a, b, nh, nl);
     Lh[0][threadIdx.x] = nh;
     Ll[0][threadIdx.x] = nl;
     Lf[0][threadIdx.x] = exp2f(-nl);
@@ -502,10 +510,7 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
     const bool more = i0 + kTile < P;
     if (more) {
       load_tile<D>(nxt, qbase, i0 + kTile, P);
-      if (threadIdx.x < kTile) {
-        lse2(i0 + kTile + threadIdx.x, nh, nl);
-        if (BITS) nt = thr(i0 + kTile + threadIdx.x);
-      }
+      if (threadIdx.x < kTile) lse_load(i0 + kTile + threadIdx.x, la, lb);   // in flight during the tile
     }
     if (i0 + kTile - 1 >= j0) {                 // some query of the tile follows a key of the wave
       const bool edge = i0 < j0 + 32 || i0 + kTile > P;
@@ -541,10 +546,12 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
     if (more) {
       store_tile<D>(nxt, Qs[buf ^ 1]);          // that buffer was last read before the previous barrier
       if (threadIdx.x < kTile) {
+        float nh, nl;
+        lse2(la, lb, nh, nl);
         Lh[buf ^ 1][threadIdx.x] = nh;
         Ll[buf ^ 1][threadIdx.x] = nl;
         Lf[buf ^ 1][threadIdx.x] = exp2f(-nl);
-        if (BITS) Th[buf ^ 1][threadIdx.x] = nt;
+        if (BITS) Th[buf ^ 1][threadIdx.x] = thr(i0 + kTile + threadIdx.x);
       }
     }
     __syncthreads();
