@@ -241,13 +241,13 @@ def decode_bytes_per_layer_step(w, ids=None) -> float:
     return total / T
 
 
-def counter_traffic(workload: str):
-    """HBM bytes per launch of the decode kernel from a committed counter record
-    (profiles/counters_*.txt whose `workload:` matches: FETCH_SIZE and
-    WRITE_SIZE passes scaled by a plain copy of known size), or None if there
-    is none or the kernel sources have changed since it was taken."""
+def _counter_records(workload: str):
+    """The committed counter records (profiles/counters_*.txt) whose
+    `workload:` matches and whose kernel sources still hash to the value
+    recorded with them, as dicts of their machine-readable lines."""
     import glob
     import hashlib
+    out = []
     for p in sorted(glob.glob(os.path.join(ROOT, "profiles", "counters_*.txt"))):
         rec = {}
         for line in open(p):
@@ -261,9 +261,29 @@ def counter_traffic(workload: str):
         for f in rec.get("kernel_sources", "").split():
             with open(os.path.join(ROOT, f), "rb") as fh:
                 h.update(fh.read())
-        if h.hexdigest()[:16] != rec.get("kernel_sources_sha256"):
-            return None
-        return float(rec["traffic_bytes_per_launch"])
+        if h.hexdigest()[:16] == rec.get("kernel_sources_sha256"):
+            out.append(rec)
+    return out
+
+
+def prefill_counters(workload: str):
+    """Matrix-core busy share (rocprofv3's MfmaUtil) and vector-ALU busy share
+    of the prefill scoring kernels from a committed counter record, or None."""
+    for rec in _counter_records(workload):
+        if "rowstats_mfma_util" in rec:
+            return {k: float(rec[k]) for k in ("rowstats_mfma_util", "colsum_mfma_util",
+                                                "rowstats_valu_busy", "colsum_valu_busy")}
+    return None
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per launch of the decode kernel from a committed counter record
+    (profiles/counters_*.txt whose `workload:` matches: FETCH_SIZE and
+    WRITE_SIZE passes scaled by a plain copy of known size), or None if there
+    is none or the kernel sources have changed since it was taken."""
+    for rec in _counter_records(workload):
+        if "traffic_bytes_per_launch" in rec:
+            return float(rec["traffic_bytes_per_launch"])
     return None
 
 
@@ -503,6 +523,7 @@ def main():
                                          if r["choice0"] is not None else None),
                    "prefill_algorithmic_tflops": pf_flops / (r["prefill_ms"] * 1e-3) / 1e12,
                    "prefill_frac_of_dense_16bit_mfma_peak": pf_flops / (r["prefill_ms"] * 1e-3) / 2.5e15,
+                   "prefill_counters": prefill_counters(w.name),
                    "input_generation_s": r["gen_s"], "outputs_finite": r["finite"],
                    "cold_kernel_us": r["cold_us"],
                    "cold_frac": (bytes_launch / (r["cold_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS) if r["cold_us"] else None},
