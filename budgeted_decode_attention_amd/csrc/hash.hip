@@ -184,13 +184,15 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
     const SW qs = qq[i];
     uint32_t best = 0;
     int bslot = 0;
-    // four slots per thread per round: their LDS reads are issued together
+    // four slots per thread per round: their LDS reads are issued together;
+    // past the budget a thread re-reads its own slot s0, so it reads only
+    // slots it owns (their owner alone rewrites them)
     for (int s0 = tid; s0 < B; s0 += 4 * kNT) {
       SW sk[4];
       int ps[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int s = min(s0 + j * kNT, B - 1);
+        const int s = s0 + j * kNT < B ? s0 + j * kNT : s0;
         sk[j] = ssk[s];
         ps[j] = spos[s];
       }
