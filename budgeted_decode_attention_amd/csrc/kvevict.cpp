@@ -83,12 +83,14 @@ int layer_chunk(const SplitPolicy& sp, int cap, int head_dim, bool uniform, bool
   int chunk = uniform ? std::max(512, (cap / (q4 ? 4 : 2) + 255) / 256 * 256) : kSplitChunkMixed;
   // grow it (256 slots at a time) until a unit's chunks fit the combine
   // kernel: at most kMaxChunks partials, and the partials plus one weight per
-  // slot within kMaxSplitLds.  A single chunk always fits (cap <= kMaxContext).
-  for (;;) {
-    const size_t nch = (size_t)(cap + chunk - 1) / chunk;
-    if (nch <= (size_t)kve::kMaxChunks && (nch * (head_dim + 2) + cap) * 4 <= kMaxSplitLds) return chunk;
-    chunk += 256;
-  }
+  // slot within kMaxSplitLds.  Growth stops at a single chunk, which fits
+  // every capacity up to kMaxContext; the caller rejects whatever does not fit.
+  auto fits = [&](int ch) {
+    const size_t nch = (size_t)(cap + ch - 1) / ch;
+    return nch <= (size_t)kve::kMaxChunks && (nch * (head_dim + 2) + cap) * 4 <= kMaxSplitLds;
+  };
+  while (chunk < cap && !fits(chunk)) chunk += 256;
+  return chunk;
 }
 
 
