@@ -1,0 +1,68 @@
+"""The committed hardware-counter records that bench.py reads (CPU only):
+each machine-readable section parses, its kernel sources exist, the decode
+traffic equals the record's own FETCH_SIZE / WRITE_SIZE arithmetic, and a
+record is ignored once its sources no longer hash to the recorded value."""
+
+import glob
+import os
+import re
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def records():
+    out = {}
+    for p in sorted(glob.glob(os.path.join(ROOT, "profiles", "counters_*.txt"))):
+        rec = {}
+        for line in open(p):
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+        out[os.path.basename(p)] = (rec, open(p).read())
+    return out
+
+
+def test_every_record_names_existing_sources_and_a_workload():
+    recs = records()
+    assert recs
+    for name, (rec, _) in recs.items():
+        assert rec.get("workload"), name
+        srcs = rec.get("kernel_sources", "").split()
+        assert srcs, name
+        for f in srcs:
+            assert os.path.exists(os.path.join(ROOT, f)), (name, f)
+        assert re.fullmatch(r"[0-9a-f]{16}", rec.get("kernel_sources_sha256", "")), name
+
+
+def test_decode_traffic_is_the_scaled_counter_sum():
+    for name, (rec, text) in records().items():
+        if "traffic_bytes_per_launch" not in rec:
+            continue
+        m = re.search(r"Traffic per launch = ([\d.]+) x ([\d.]+) KiB \+ ([\d.]+) x ([\d.]+) KiB = (\d+) KiB", text)
+        assert m, name
+        ff, fetch, wf, write, total = (float(x) for x in m.groups())
+        assert abs(ff * fetch + wf * write - total) <= 1.0, name
+        assert int(rec["traffic_bytes_per_launch"]) == int(total) * 1024, name
+
+
+def test_records_are_read_only_while_their_sources_match(monkeypatch):
+    live = bench._counter_records("opt30b_decode_h2o")
+    assert any("traffic_bytes_per_launch" in r for r in live)
+    assert any("rowstats_mfma_util" in r for r in live)
+    real_open = open
+
+    def changed_sources(path, mode="r", *a, **k):
+        f = real_open(path, mode, *a, **k)
+        if "b" in mode and path.endswith((".hip", ".hpp")):
+            data = f.read() + b"\n// changed\n"
+            f.close()
+            import io
+            return io.BytesIO(data)
+        return f
+
+    monkeypatch.setattr("builtins.open", changed_sources)
+    assert bench.counter_traffic("opt30b_decode_h2o") is None
+    assert bench.prefill_counters("opt30b_decode_h2o") is None
