@@ -57,3 +57,24 @@ def test_hash_at_max_budget(bits, budget):
                        hash_budget=budget, sketch_bits=bits)
     r = run_all_units(w)
     assert (r.final_cnt == budget).all()
+
+
+def test_q4_hash_at_max_budget():
+    """4-bit slots at the largest HashEvict budget: the replay's quantising
+    gather of 16,384 rows and the split decode over 4-bit chunks."""
+    w = configs.scaled("hashevict_lsh_q4", batch=1, heads=2, prompt=MAX_CONTEXT - STEPS, steps=STEPS,
+                       hash_budget=16384)
+    assert w.cache_bits == 4
+    r = run_all_units(w)
+    assert (r.final_cnt == 16384).all()
+
+
+def test_q4_h2o_at_max_context():
+    """4-bit slots on H2O heads with a 32,760-token prompt and a 2,048 + 2,048
+    slot budget (the split decode over 4-bit rows, the quantising gather of
+    the selected prompt rows)."""
+    w = configs.scaled("opt30b_decode_h2o_q4", layers=1, batch=1, heads=2, prompt=MAX_CONTEXT - STEPS,
+                       steps=STEPS, heavy=2048, recent=2048)
+    assert w.cache_bits == 4
+    r = run_all_units(w)
+    assert (r.final_cnt == 4096).all()
