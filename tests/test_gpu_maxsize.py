@@ -78,3 +78,22 @@ def test_q4_h2o_at_max_context():
     assert w.cache_bits == 4
     r = run_all_units(w)
     assert (r.final_cnt == 4096).all()
+
+
+def test_persist_at_max_context():
+    """Persistence counts with a 32,760-token prompt (pivotal bits of the
+    last 64 prompt rows, popcount ranking over 28,664 candidates) and
+    2,048 + 2,048 slots (split decode)."""
+    w = configs.scaled("opt30b_decode_persist", layers=1, batch=1, heads=2, prompt=MAX_CONTEXT - STEPS,
+                       steps=STEPS, heavy=2048, recent=2048)
+    r = run_all_units(w)
+    assert (r.final_cnt == 4096).all()
+
+
+def test_profiled_fastgen_at_max_context():
+    """FastGen profiling with a 32,760-token prompt: one head of each of the
+    five attention kinds, each unit's composite chosen from the last 64
+    prompt rows, caches whose stride is the whole 32,768-position context
+    (the grown split chunk)."""
+    w = configs.scaled("llama65b_fastgen_profiled", batch=1, heads=5, prompt=MAX_CONTEXT - STEPS, steps=STEPS)
+    run_all_units(w)
