@@ -39,9 +39,12 @@ def sketches(X: np.ndarray, W: np.ndarray) -> np.ndarray:
     The sign is that of the exact dot product.  Entries are exact float64
     values (bf16 inputs: every product is exact).  A float64 dot of n terms
     differs from the exact value by at most gamma_n * sum|terms| with
-    gamma_n = n u / (1 - n u), u = 2^-53, whatever the summation order; a
-    dot inside that bound is recomputed with math.fsum (correctly rounded, so
-    its sign is exact).
+    gamma_n = n u / (1 - n u), u = 2^-53, whatever the summation order.  The
+    sum of magnitudes is itself computed in float64, so it may fall short of
+    the exact one by a relative gamma_n, and the bound's product rounds once
+    more; gamma_{2n+2} exceeds gamma_n / ((1 - gamma_n)(1 - u)), so the test
+    below never misses a fragile dot.  A dot inside that bound is recomputed
+    with math.fsum (correctly rounded, so its sign is exact).
     """
     X = np.asarray(X, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
@@ -49,7 +52,8 @@ def sketches(X: np.ndarray, W: np.ndarray) -> np.ndarray:
     bits = W.shape[1]
     s = X @ W
     u = 2.0 ** -53
-    gamma = d * u / (1.0 - d * u)
+    m = 2 * d + 2
+    gamma = m * u / (1.0 - m * u)
     bound = gamma * (np.abs(X) @ np.abs(W))
     fragile = np.argwhere(np.abs(s) <= bound)
     for i, b in fragile:
