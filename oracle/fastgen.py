@@ -44,7 +44,7 @@ def run_full(Q_all, K_all, V_all, P, scale, steps=None, want_prompt_out=False) -
     T = Q_all.shape[0] - P if steps is None else steps
     outs = [attend(Q_all[t], K_all[:t + 1], V_all[:t + 1], scale)[1] for t in range(P, P + T)]
     po = causal_attention(Q_all[:P], K_all[:P], V_all[:P], scale)[1] if want_prompt_out else None
-    return Trajectory(np.arange(P), np.array(outs).reshape(T, -1), np.full(T, -1),
+    return Trajectory(np.arange(P), np.array(outs).reshape(T, V_all.shape[1]), np.full(T, -1),
                       np.arange(P + T), po)
 
 
@@ -62,7 +62,7 @@ def run_local(Q_all, K_all, V_all, P, W, scale, steps=None, want_prompt_out=Fals
         ev.append(t - W if t >= W else -1)
     po = causal_attention(Q_all[:P], K_all[:P], V_all[:P], scale)[1] if want_prompt_out else None
     end = P + T
-    return Trajectory(np.arange(max(0, P - W), P), np.array(outs).reshape(T, -1),
+    return Trajectory(np.arange(max(0, P - W), P), np.array(outs).reshape(T, V_all.shape[1]),
                       np.array(ev), np.arange(max(0, end - W), end), po)
 
 
@@ -87,7 +87,7 @@ def run_special(Q_all, K_all, V_all, ids, keep_ids: Sequence[int], P, scale, ste
         else:
             ev.append(t)
     po = causal_attention(Q_all[:P], K_all[:P], V_all[:P], scale)[1] if want_prompt_out else None
-    return Trajectory(kept0, np.array(outs).reshape(T, -1), np.array(ev),
+    return Trajectory(kept0, np.array(outs).reshape(T, V_all.shape[1]), np.array(ev),
                       np.array(kept, dtype=np.int64), po)
 
 

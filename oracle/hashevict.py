@@ -130,5 +130,5 @@ def run_unit(Q_all, K_all, V_all, W, P, B, scale, steps=None, want_prompt_out=Fa
         A = np.array(cache, dtype=np.int64)
         outs.append(attend(Q_all[t], Kc[A], Vc[A], scale)[1])
     po = causal_attention(Q_all[:P], K_all[:P], V_all[:P], scale)[1] if want_prompt_out else None
-    return Trajectory(kept0, np.array(outs).reshape(T, -1), np.array(ev, dtype=np.int64),
+    return Trajectory(kept0, np.array(outs).reshape(T, V_all.shape[1]), np.array(ev, dtype=np.int64),
                       np.sort(np.array(cache, dtype=np.int64)), qsk, ksk, po)

@@ -161,3 +161,22 @@ def test_hash_cache_invariants():
         assert e in seen
         seen.discard(int(e)); seen.add(P + s)
     assert seen == set(tr.final_kept.tolist())
+
+
+@pytest.mark.parametrize("policy", [fastgen.FULL, fastgen.LOCAL, fastgen.SPECIAL, fastgen.H2O, "hash"])
+def test_zero_decode_steps_is_the_prefill_alone(policy):
+    """steps=0 runs the prefill only: empty outputs and logs, the same prompt
+    cache as the full run."""
+    P, T, d = 24, 9, 8
+    Q, K, V = rand_qkv(31, P + T, d, heavy_pos=3)
+    ids = np.random.default_rng(2).integers(0, 20, P + T)
+    if policy == "hash":
+        W = np.random.default_rng(3).standard_normal((d, 32))
+        zero = hashevict.run_unit(Q, K, V, W, P, 10, 0.3, steps=0)
+        full = hashevict.run_unit(Q, K, V, W, P, 10, 0.3)
+    else:
+        kw = dict(heavy=4, recent=6, ids=ids, keep_ids=[0, 1, 5])
+        zero = fastgen.run_unit(policy, Q, K, V, P, 0.3, steps=0, **kw)
+        full = fastgen.run_unit(policy, Q, K, V, P, 0.3, **kw)
+    assert zero.out.shape == (0, d) and len(zero.evicted) == 0
+    assert zero.prefill_kept.tolist() == full.prefill_kept.tolist()
