@@ -27,7 +27,8 @@ CODE_DTYPES = {v: k for k, v in DTYPE_CODES.items()}
 
 EXPORTED = ("kvevict_workspace_size", "kvevict_create", "kvevict_destroy", "kvevict_prefill",
             "kvevict_decode_step", "kvevict_kept_indices", "kvevict_unit_policies", "kvevict_cache_rows",
-            "kvevict_capacity", "kvevict_position", "kvevict_status_string", "kvevict_last_error")
+            "kvevict_capacity", "kvevict_position", "kvevict_stream_read", "kvevict_status_string",
+            "kvevict_last_error")
 
 
 class KVEvictError(RuntimeError):
@@ -77,6 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvevict_cache_rows": (i32, [vp, i32, vp, vp, vp, vp, vp]),
         "kvevict_capacity": (i32, [vp, i32]),
         "kvevict_position": (i32, [vp, i32]),
+        "kvevict_stream_read": (i32, [vp, sz, vp, vp]),
         "kvevict_status_string": (ctypes.c_char_p, [i32]),
         "kvevict_last_error": (ctypes.c_char_p, []),
     }
@@ -217,6 +219,14 @@ def kvevict_capacity(h, layer: int) -> int:
 
 def kvevict_position(h, layer: int) -> int:
     return int(load_library().kvevict_position(h, layer))
+
+
+def kvevict_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Streaming read of the whole of `src` (measurement aid; see the header)."""
+    if not src.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < 1 or src.device != sink.device:
+        raise ValueError("src must be contiguous and sink an int32 tensor of >= 1 element on the same device")
+    _check(load_library().kvevict_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                              _stream(stream)), "kvevict_stream_read")
 
 
 # ---- convenience object ------------------------------------------------------------------------

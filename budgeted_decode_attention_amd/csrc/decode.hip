@@ -363,6 +363,9 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
     // against heavy + recent (npcount[u]).
     const int lim = t - m.recent;              // candidates: position <= t - recent
     const bool prot_new = m.ids != IDS_NONE && id_protected(m.ids, io.sets, io.ids[u / sh.heads]);
+    // unprotected tokens kept before t: read by every thread before the
+    // argmin's barriers, so thread 0's update below cannot race with it
+    const int held = m.ids == IDS_NONE ? n : c.npcount[u];
     MinKey best{INFINITY, INT32_MAX, INT32_MAX};
     // RND slots per thread per round: their score/position loads are issued
     // together, so a large cache costs n / (RND NT) load latencies, not n / NT
@@ -394,7 +397,6 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
       if (key_less(k, best)) best = k;
     }
     best = block_argmin<kNT>(best, kscr);      // barriers inside: S[] updates done
-    const int held = m.ids == IDS_NONE ? n : c.npcount[u];   // unprotected tokens kept before t
     if (prot_new) {
       wslot = n;
     } else if (held >= m.heavy + m.recent && best.s < INFINITY) {

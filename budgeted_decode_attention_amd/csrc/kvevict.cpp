@@ -281,7 +281,7 @@ struct kve_ctx {
   uint32_t* bitmap = nullptr;          // device keep set (SPECIAL heads)
   uint32_t* special = nullptr;         // device special / punctuation sets (ADAPTIVE heads)
   uint32_t* punct = nullptr;
-  double* mass = nullptr;              // device [U][max_context] (ADAPTIVE layers)
+  float* mass = nullptr;               // device [U][max_context] (ADAPTIVE layers): the profile
   uint16_t* proj = nullptr;            // device [layers][d][32]
   float* lse = nullptr;                // device [U][max_context][2]
   double* colsum = nullptr;            // device [U][max_context]
@@ -311,7 +311,7 @@ size_t layout(const kve_config* c, const std::vector<LayerInfo>& info, void* bas
   auto* bitmap = any_special ? pl.take<uint32_t>(words) : nullptr;
   auto* special = any_adaptive ? pl.take<uint32_t>(words) : nullptr;
   auto* punct = any_adaptive ? pl.take<uint32_t>(words) : nullptr;
-  auto* mass = any_adaptive ? pl.take<double>(U * N) : nullptr;
+  auto* mass = any_adaptive ? pl.take<float>(U * N) : nullptr;
   const size_t bits = c->sketch_bits, swb = sketch_word_bytes(c->sketch_bits);
   auto* proj = any_hash ? pl.take<uint16_t>((size_t)c->layers * d * bits) : nullptr;
   auto* lse = pl.take<float>(U * N * 2);
@@ -647,6 +647,20 @@ int32_t kvevict_capacity(kve_handle h, int32_t layer) {
 int32_t kvevict_position(kve_handle h, int32_t layer) {
   if (!h || layer < 0 || layer >= h->cfg.layers) return -1;
   return h->layers[layer].position;
+}
+
+kve_status kvevict_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return fail(KVE_EINVAL, "src and sink are required");
+  if (bytes < 16 || bytes % 16 || (uintptr_t)src % 16)
+    return fail(KVE_EINVAL, "bytes must be a positive multiple of 16 and src 16-byte aligned");
+  hipError_t e = kve::launch_stream_read(src, bytes, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return dev(e, "stream_read launch");
+  const char* env = std::getenv("KVEVICT_SYNC_CHECK");
+  if (env && env[0] == '1') {
+    kve_status s = dev(hipStreamSynchronize((hipStream_t)stream), "stream_read");
+    if (s != KVE_OK) return s;
+  }
+  return KVE_OK;
 }
 
 const char* kvevict_status_string(kve_status s) {

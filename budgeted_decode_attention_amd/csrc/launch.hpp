@@ -101,13 +101,14 @@ hipError_t launch_prefill_persist_valu(const Shape& sh, int P, UnitList units, c
                                        const void* k, const float* lse, const HeadMeta* meta,
                                        double* bits, hipStream_t st);
 // Column sums (as launch_prefill_colsum_mfma) plus, per key, the mass the last
-// `rows` prompt rows give it: mass[u][j] = sum_{i >= max(j, P - rows)} weight.
+// `rows` prompt rows give it: mass[u][j] = sum_{i >= max(j, P - rows)} weight,
+// summed in float64 and stored as float32 (one word per token: the profile).
 hipError_t launch_prefill_colsum_mass_mfma(const Shape& sh, int P, UnitList units, const void* q,
                                            const void* k, const float* lse, double* colsum,
-                                           double* mass, int rows, hipStream_t st);
+                                           float* mass, int rows, hipStream_t st);
 hipError_t launch_prefill_colsum_mass_valu(const Shape& sh, int P, UnitList units, const void* q,
                                            const void* k, const float* lse, double* colsum,
-                                           double* mass, int rows, hipStream_t st);
+                                           float* mass, int rows, hipStream_t st);
 // Chooses the kept prompt positions per the unit's policy and fills the cache.
 hipError_t launch_prefill_select(const Shape& sh, const LayerCache& c, int P, const double* colsum,
                                  const void* k, const void* v, const int32_t* ids, const IdSets& sets,
@@ -121,7 +122,7 @@ struct Profile {
   int32_t heavy, recent;     // frequent slots and local window of the composites
 };
 hipError_t launch_prefill_adaptive(const Shape& sh, const LayerCache& c, UnitList units, int P,
-                                   const double* colsum, const double* mass, const Profile& pf,
+                                   const double* colsum, const float* mass, const Profile& pf,
                                    const void* k, const void* v, const int32_t* ids, const IdSets& sets,
                                    hipStream_t st);
 
@@ -167,6 +168,12 @@ struct SplitScratch {
 // per-unit combine.
 hipError_t launch_decode(const Shape& sh, const LayerCache& c, const DecodeIO& io,
                          const SplitScratch* sp, hipStream_t st);
+
+// ---- measurement
+// Reads `bytes` (a multiple of 16, 16-byte aligned) of src with the decode
+// kernels' 16-byte non-temporal loads; writes nothing in practice (sink is
+// written only if the XOR of a workgroup's bytes equals a fixed constant).
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 
 
 }  // namespace kve

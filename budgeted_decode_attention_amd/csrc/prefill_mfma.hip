@@ -442,7 +442,7 @@ __device__ inline void persist_fold(const f32x4 (&acc)[2], int i0, int nb, int j
 template <int DT, int D, int MODE>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(KVE_PREFILL_WAVES_PER_EU)))
 void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void* k, const float* lse,
-                        double* colsum, const HeadMeta* meta, double* mass, int rows) {
+                        double* colsum, const HeadMeta* meta, float* mass, int rows) {
   constexpr bool BITS = MODE == 1;
   constexpr int KS = D / 32;
   __shared__ __attribute__((aligned(16))) char Qs[2][Tile<D>::kBytes];
@@ -581,7 +581,7 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
         double w = ms[mb][r];
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) w += __shfl_xor(w, o);
-        if (c16 == 0 && kj < P) mass[(size_t)u * P + kj] = w;
+        if (c16 == 0 && kj < P) mass[(size_t)u * P + kj] = (float)w;
       }
     }
 }
@@ -783,7 +783,7 @@ hipError_t rowstats_t(const Shape& sh, int P, UnitList ul, const void* q, const 
 
 template <int DT, int D, int MODE>
 hipError_t colsum_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, const float* lse,
-                    double* colsum, const HeadMeta* meta, double* mass, int rows, hipStream_t st) {
+                    double* colsum, const HeadMeta* meta, float* mass, int rows, hipStream_t st) {
   dim3 grid(ul.n, (P + kBlk - 1) / kBlk);
   hipLaunchKernelGGL((colsum_mfma_kernel<DT, D, MODE>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse, colsum,
                      meta, mass, rows);
@@ -847,7 +847,7 @@ hipError_t launch_prefill_persist_mfma(const Shape& sh, int P, UnitList ul, cons
 namespace kve {
 
 hipError_t launch_prefill_colsum_mass_mfma(const Shape& sh, int P, UnitList ul, const void* q, const void* k,
-                                           const float* lse, double* colsum, double* mass, int rows,
+                                           const float* lse, double* colsum, float* mass, int rows,
                                            hipStream_t st) {
   if (ul.n <= 0) return hipSuccess;
   if (!mass || rows < 1) return hipErrorInvalidValue;

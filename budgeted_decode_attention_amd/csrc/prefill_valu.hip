@@ -136,11 +136,12 @@ __global__ __launch_bounds__(kNT) void rowstats_valu_kernel(Shape sh, int P, Uni
   }
 }
 
-// With `mass` non-null also mass[u][j] = the part of the sum from rows >= P - rows.
+// With `mass` non-null also mass[u][j] = the part of the sum from rows >= P - rows
+// (stored as float32).
 template <int DT, int D>
 __global__ __launch_bounds__(kNT) void colsum_valu_kernel(Shape sh, int P, UnitList ul, const void* q,
                                                            const void* k, const float* lse, double* colsum,
-                                                           double* mass, int rows) {
+                                                           float* mass, int rows) {
   constexpr int ES = elem_bytes<DT>();
   __shared__ float Ks[kRB * (D + 1)];
   __shared__ float Qs[kKT * (D + 1)];
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(kNT) void colsum_valu_kernel(Shape sh, int P, UnitL
       m += mpart_s[g * kRB + tid];
     }
     colsum[(size_t)u * P + col0 + tid] = s;
-    if (mass) mass[(size_t)u * P + col0 + tid] = m;
+    if (mass) mass[(size_t)u * P + col0 + tid] = (float)m;
   }
 }
 
@@ -264,7 +265,7 @@ hipError_t rowstats_t(const Shape& sh, int P, UnitList ul, const void* q, const 
 
 template <int DT, int D>
 hipError_t colsum_t(const Shape& sh, int P, UnitList ul, const void* q, const void* k, const float* lse,
-                    double* colsum, double* mass, int rows, hipStream_t st) {
+                    double* colsum, float* mass, int rows, hipStream_t st) {
   dim3 grid((P + kRB - 1) / kRB, ul.n);
   hipLaunchKernelGGL((colsum_valu_kernel<DT, D>), grid, dim3(kNT), 0, st, sh, P, ul, q, k, lse, colsum, mass,
                      rows);
@@ -292,7 +293,7 @@ hipError_t launch_prefill_colsum_valu(const Shape& sh, int P, UnitList ul, const
 }
 
 hipError_t launch_prefill_colsum_mass_valu(const Shape& sh, int P, UnitList ul, const void* q, const void* k,
-                                           const float* lse, double* colsum, double* mass, int rows,
+                                           const float* lse, double* colsum, float* mass, int rows,
                                            hipStream_t st) {
   if (ul.n <= 0) return hipSuccess;
   switch (sh.dtype * 1000 + sh.d) {

@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kNT) void select_kernel(Shape sh, LayerCache c, int
 // carry score +inf in the frequent composites, so they are never evicted.
 template <int DT, int D>
 __global__ __launch_bounds__(kNT) void adaptive_kernel(Shape sh, LayerCache c, UnitList ul, int P,
-                                                       const double* colsum, const double* mass, Profile pf,
+                                                       const double* colsum, const float* mass, Profile pf,
                                                        const void* k, const void* v, const int32_t* ids,
                                                        IdSets sets) {
   extern __shared__ int32_t kept_pos[];     // [cap]
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kNT) void adaptive_kernel(Shape sh, LayerCache c, U
   const int tid = threadIdx.x;
   const size_t slot0 = (size_t)u * c.cap;
   const double* cu = colsum + (size_t)u * P;
-  const double* mu = mass + (size_t)u * P;
+  const float* mu = mass + (size_t)u * P;
   const int32_t* idu = ids + (size_t)(u / sh.heads) * P;
   const int R = min(pf.rows, P);
   const int hh = pf.heavy, W = pf.recent;
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kNT) void adaptive_kernel(Shape sh, LayerCache c, U
   // masses of the id sets, of the whole prompt and of the unprotected window
   double m1 = 0.0, m2 = 0.0, mall = 0.0, mwin = 0.0, nfree = 0.0, wfree = 0.0;
   for (int j = tid; j < P; j += kNT) {
-    const double x = mu[j];
+    const double x = (double)mu[j];
     const bool s1 = special(j), s2 = s1 || token_kept(sets.punct, sets.vocab, idu[j]);
     mall += x;
     if (s1) m1 += x;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kNT) void adaptive_kernel(Shape sh, LayerCache c, U
       if (hh > 0) radix_top(P, hh, 0, key, free_, rl, T3, cut3);
       double sel = 0.0;
       for (int j = tid; j < P; j += kNT)
-        if (hh > 0 && free_(j) && (key(j) > T3 || (key(j) == T3 && j >= cut3))) sel += mu[j];
+        if (hh > 0 && free_(j) && (key(j) > T3 || (key(j) == T3 && j >= cut3))) sel += (double)mu[j];
       rec3 = (m2 + block_sum<kNT>(sel, dscr)) * inv;
     }
     if (rec3 >= thr) {
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kNT) void adaptive_kernel(Shape sh, LayerCache c, U
         if (quota4 > 0) radix_top(nc, quota4, 0, key, free_, rl, T4, cut4);
         double sel = 0.0;
         for (int j = tid; j < nc; j += kNT)
-          if (quota4 > 0 && free_(j) && (key(j) > T4 || (key(j) == T4 && j >= cut4))) sel += mu[j];
+          if (quota4 > 0 && free_(j) && (key(j) > T4 || (key(j) == T4 && j >= cut4))) sel += (double)mu[j];
         rec4 = (m2 + mwin + block_sum<kNT>(sel, dscr)) * inv;
       }
       if (rec4 >= thr) choice = 4;
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kNT) void adaptive_kernel(Shape sh, LayerCache c, U
 
 template <int DT, int D>
 hipError_t adaptive_t(const Shape& sh, const LayerCache& c, UnitList ul, int P, const double* colsum,
-                      const double* mass, const Profile& pf, const void* k, const void* v, const int32_t* ids,
+                      const float* mass, const Profile& pf, const void* k, const void* v, const int32_t* ids,
                       const IdSets& sets, hipStream_t st) {
   const size_t lds = (size_t)c.cap * sizeof(int32_t);
   if (lds > 65536) {
@@ -412,7 +412,7 @@ hipError_t launch_prefill_select(const Shape& sh, const LayerCache& c, int P, co
 namespace kve {
 
 hipError_t launch_prefill_adaptive(const Shape& sh, const LayerCache& c, UnitList ul, int P, const double* colsum,
-                                   const double* mass, const Profile& pf, const void* k, const void* v,
+                                   const float* mass, const Profile& pf, const void* k, const void* v,
                                    const int32_t* ids, const IdSets& sets, hipStream_t st) {
   if (ul.n <= 0) return hipSuccess;
   if (!colsum || !mass || !ids || pf.rows < 1) return hipErrorInvalidValue;

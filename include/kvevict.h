@@ -245,6 +245,17 @@ int32_t kvevict_capacity(kve_handle h, int32_t layer);
  * for a bad handle/layer. */
 int32_t kvevict_position(kve_handle h, int32_t layer);
 
+/* Measurement aid, not part of the method: reads `bytes` bytes of device
+ * memory at `src` (16-byte aligned, a positive multiple of 16) with the same
+ * 16-byte non-temporal loads the decode kernels use for cached rows, and does
+ * nothing with them.  Timing it gives the streaming-read ceiling of the GPU
+ * for a given byte count, the reference a decode step's achieved bandwidth is
+ * compared with (a step's cost is the read of its kept rows: H2O review page,
+ * main findings).  `sink` is a device word that is written only in the
+ * (practically impossible) case that the bytes a workgroup read XOR to a fixed
+ * constant.  Stream-ordered; EINVAL on bad arguments. */
+kve_status kvevict_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Static text for a status code. */
 const char* kvevict_status_string(kve_status s);
 

@@ -22,7 +22,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     lib = binding.load_library()
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -200,3 +200,14 @@ def test_mixed_layer_at_max_context_is_accepted():
     s, n = status_of(c)
     assert s == binding.KVE_OK, binding.load_library().kvevict_last_error()
     assert n > 0
+
+
+def test_stream_read_validates_arguments():
+    lib = binding.load_library()
+    fake = ctypes.c_void_p((1 << 40))
+    sink = ctypes.c_void_p((1 << 40) + 4096)
+    assert lib.kvevict_stream_read(None, 64, sink, None) == binding.KVE_EINVAL
+    assert lib.kvevict_stream_read(fake, 64, None, None) == binding.KVE_EINVAL
+    assert lib.kvevict_stream_read(fake, 0, sink, None) == binding.KVE_EINVAL
+    assert lib.kvevict_stream_read(fake, 72, sink, None) == binding.KVE_EINVAL          # not a multiple of 16
+    assert lib.kvevict_stream_read(ctypes.c_void_p((1 << 40) + 8), 64, sink, None) == binding.KVE_EINVAL
