@@ -66,92 +66,148 @@ def _q4_output_error(tr_q4, Q, K, V, P: int, a: int, b: int, scale: float) -> fl
     return float(np.mean(np.linalg.norm(tr_q4.out - ref, axis=1) / np.linalg.norm(ref, axis=1)))
 
 
-def _oracle_unit(args):
-    """One unit through the float64 oracle (prefill + every decode step).
-    Returns (seconds, extra) -- extra: the HashEvict cache's recovered share,
-    or for 4-bit slots (on the units asked for) the output error against the
-    storage-dtype cache."""
+def _oracle_run(kind, Q, K, V, P, a, b, scale, extra, steps=None):
+    """One call of the oracle's own per-unit entry point for `kind`; with
+    steps=0 it runs the prefill only (scoring and selection of the prompt)."""
     import numpy as np
     from oracle import adaptive, fastgen, h2o, hashevict, persistence, quant
-    kind, Q, K, V, P, a, b, scale, extra = args
+    if kind == "h2o_q4":
+        return h2o.run_unit(Q, K, V, P, a, b, scale, steps=steps, Kc=quant.roundtrip(K), Vc=quant.roundtrip(V))
+    if kind == "h2o":
+        return h2o.run_unit(Q, K, V, P, a, b, scale, steps=steps)
+    if kind == "persist":
+        return persistence.run_unit(Q, K, V, P, a, b, extra, scale, steps=steps)
+    if kind == "adaptive":
+        ids, special, punct, rows, thr = extra
+        return adaptive.run_unit(Q, K, V, ids, P, special, punct, a, b, scale, rows, thr, steps=steps)
+    if kind in ("hash", "hash_q4"):
+        cc = dict(Kc=quant.roundtrip(K), Vc=quant.roundtrip(V)) if kind == "hash_q4" else {}
+        return hashevict.run_unit(Q, K, V, np.asarray(extra, dtype=np.float64), P, a, scale, steps=steps, **cc)
+    pol, ids, keep = extra
+    return fastgen.run_unit(pol, Q, K, V, P, scale, heavy=a, recent=b, ids=ids, keep_ids=keep, steps=steps)
+
+
+def _oracle_unit(args):
+    """One unit through the float64 oracle: the prefill alone (timed), then
+    prefill + every decode step (timed).  Returns (prefill s, whole-unit s,
+    extra) -- extra: the HashEvict cache's recovered share, or for 4-bit slots
+    (on the units asked for) the output error against the storage-dtype cache."""
+    import numpy as np
+    from oracle import adaptive, fastgen, h2o, hashevict, persistence, quant  # noqa: F401  (imported before timing)
+    kind, Q, K, V, P, a, b, scale, extra, want_extra = args
     Q, K, V = (np.asarray(x, dtype=np.float64) for x in (Q, K, V))
     t0 = time.perf_counter()
-    if kind == "h2o_q4":
-        tr = h2o.run_unit(Q, K, V, P, a, b, scale, Kc=quant.roundtrip(K), Vc=quant.roundtrip(V))
-        dt = time.perf_counter() - t0
-        return dt, (_q4_output_error(tr, Q, K, V, P, a, b, scale) if extra else None)
-    if kind == "h2o":
-        h2o.run_unit(Q, K, V, P, a, b, scale)
-    elif kind == "persist":
-        persistence.run_unit(Q, K, V, P, a, b, extra, scale)
-    elif kind == "adaptive":
-        ids, special, punct, rows, thr = extra
-        adaptive.run_unit(Q, K, V, ids, P, special, punct, a, b, scale, rows, thr)
-    elif kind in ("hash", "hash_q4"):
-        cc = dict(Kc=quant.roundtrip(K), Vc=quant.roundtrip(V)) if kind == "hash_q4" else {}
-        tr = hashevict.run_unit(Q, K, V, np.asarray(extra, dtype=np.float64), P, a, scale, **cc)
-        dt = time.perf_counter() - t0
-        return dt, _hash_recovered_share(tr, Q, K, P, scale)
-    else:
-        pol, ids, keep = extra
-        fastgen.run_unit(pol, Q, K, V, P, scale, heavy=a, recent=b, ids=ids, keep_ids=keep)
-    return time.perf_counter() - t0, None
+    _oracle_run(kind, Q, K, V, P, a, b, scale, extra, steps=0)
+    t1 = time.perf_counter()
+    tr = _oracle_run(kind, Q, K, V, P, a, b, scale, extra)
+    t2 = time.perf_counter()
+    out = None
+    if want_extra and kind == "h2o_q4":
+        out = _q4_output_error(tr, Q, K, V, P, a, b, scale)
+    elif want_extra and kind in ("hash", "hash_q4"):
+        out = _hash_recovered_share(tr, Q, K, P, scale)
+    return t1 - t0, t2 - t1, out
 
 
-def cpu_baseline(w, n_units: int, workers: int):
-    """Times the oracle on `n_units` units of workload `w` (inputs generated on the
-    CPU with the same recipe), with `workers` processes; returns the dict for
-    the JSON line.  Must run before anything initialises the GPU."""
+def _oracle_warmup(task):
+    """Pool initializer: the sample's first unit through the oracle's prefill
+    and one decode step, untimed, so each worker's one-time library start-up
+    (allocator, BLAS) stays out of the timed calls."""
     import numpy as np
-    from workloads import configs
+    from oracle import adaptive, fastgen, h2o, hashevict, persistence, quant  # noqa: F401
+    kind, Q, K, V, P, a, b, scale, extra, _ = task
+    Q, K, V = (np.asarray(x, dtype=np.float64) for x in (Q, K, V))
+    _oracle_run(kind, Q, K, V, P, a, b, scale, extra, steps=1)
+
+
+def sample_units(w, n_units: int):
+    """Seeded sample of units (layer, sequence, head): half from the first and
+    half from the last layer (one layer if the workload has one), drawn
+    without replacement over every (sequence, head) of that layer."""
+    import numpy as np
+    rng = np.random.default_rng([1000 + w.index, 47])
+    layers = [0, w.layers - 1] if w.layers > 1 else [0]
+    units = []
+    for i, layer in enumerate(layers):
+        m = min(n_units // len(layers) + (1 if i < n_units % len(layers) else 0), w.batch * w.heads)
+        for f in sorted(rng.choice(w.batch * w.heads, m, replace=False).tolist()):
+            units.append((layer, f // w.heads, f % w.heads))
+    return units
+
+
+def cpu_baseline(w, n_units: int, workers: int, one_core_units: int = 16):
+    """Times the oracle on a seeded sample of `n_units` units of workload `w`
+    (inputs generated on the CPU with the same recipe, the first and the last
+    layer, every sequence eligible) with `workers` processes, and the first
+    `one_core_units` of the sample again in one process.  Prefill and decode
+    are timed separately.  Returns the dict for the JSON line.  Must run
+    before anything initialises the GPU."""
+    import numpy as np
     from workloads.generate import generate_layer, unit_ids, unit_sequence
-    import dataclasses
-    sample_w = dataclasses.replace(w, batch=1)            # the workload's own shapes, one sequence
     pol, hv, rc = w.policy_table(0)
-    tasks = []
-    layer = 0
     scale = 1.0 / np.sqrt(w.head_dim)
-    while len(tasks) < n_units:
-        inp = generate_layer(sample_w, layer, "cpu", 1)
-        for h in range(w.heads):
-            if len(tasks) >= n_units:
-                break
-            Q, K, V = (x.astype(np.float32) for x in unit_sequence(inp, 0, h))
+    units = sample_units(w, n_units)
+    tasks = []
+    t_gen = time.perf_counter()
+    for layer in sorted(set(u[0] for u in units)):
+        inp = generate_layer(w, layer, "cpu", 1)
+        for (_, b, h) in [u for u in units if u[0] == layer]:
+            Q, K, V = (x.astype(np.float32) for x in unit_sequence(inp, b, h))
+            want = len(tasks) < 16
             if w.family == "h2o" and w.cache_bits == 4:
-                tasks.append(("h2o_q4", Q, K, V, w.prompt, hv[h], rc[h], scale, len(tasks) < 16))
+                tasks.append(("h2o_q4", Q, K, V, w.prompt, hv[h], rc[h], scale, None, want))
             elif w.family == "h2o":
-                tasks.append(("h2o", Q, K, V, w.prompt, hv[h], rc[h], scale, None))
+                tasks.append(("h2o", Q, K, V, w.prompt, hv[h], rc[h], scale, None, False))
             elif w.family == "persist":
-                tasks.append(("persist", Q, K, V, w.prompt, hv[h], rc[h], scale, w.window_table(0)[h]))
+                tasks.append(("persist", Q, K, V, w.prompt, hv[h], rc[h], scale, w.window_table(0)[h], False))
             elif w.family == "adaptive":
                 tasks.append(("adaptive", Q, K, V, w.prompt, hv[h], rc[h], scale,
-                              (unit_ids(inp, 0), list(w.special_ids), list(w.punct_ids), w.profile_rows,
-                               w.profile_threshold)))
+                              (unit_ids(inp, b), list(w.special_ids), list(w.punct_ids), w.profile_rows,
+                               w.profile_threshold), False))
             elif w.family == "hash":
                 tasks.append(("hash_q4" if w.cache_bits == 4 else "hash", Q, K, V, w.prompt, hv[h], 0, scale,
-                              inp.proj.float().numpy()))
+                              inp.proj.float().numpy(), True))
             else:
                 tasks.append(("fastgen", Q, K, V, w.prompt, hv[h], rc[h], scale,
-                              (pol[h], unit_ids(inp, 0), w.keep_ids())))
-        layer += 1
+                              (pol[h], unit_ids(inp, b), w.keep_ids()), False))
+        del inp
+    gen_s = time.perf_counter() - t_gen
     os.environ["OMP_NUM_THREADS"] = "1"
     os.environ["OPENBLAS_NUM_THREADS"] = "1"
     os.environ["MKL_NUM_THREADS"] = "1"
     ctx = mp.get_context("spawn")
     t0 = time.perf_counter()
-    with ctx.Pool(workers) as pool:
+    with ctx.Pool(workers, initializer=_oracle_warmup, initargs=(tasks[0],)) as pool:
         res = pool.map(_oracle_unit, tasks, chunksize=1)
     wall = time.perf_counter() - t0
-    per = [r[0] for r in res]
-    extra = [r[1] for r in res if r[1] is not None]
-    job_s = wall * w.units / len(tasks)
+    one = min(one_core_units, len(tasks))
+    t1 = time.perf_counter()
+    with ctx.Pool(1, initializer=_oracle_warmup, initargs=(tasks[0],)) as pool:
+        res1 = pool.map(_oracle_unit, [t[:-1] + (False,) for t in tasks[:one]], chunksize=1)
+    wall1 = time.perf_counter() - t1
+    pre = sum(r[0] for r in res)
+    tot = sum(r[1] for r in res)
+    extra = [r[2] for r in res if r[2] is not None]
+    # the parallel wall covers both timed calls of every unit; split it by the
+    # per-unit shares and scale it to the job's units
+    job_s = wall * (tot / (tot + pre)) * w.units / len(tasks)
+    job_pre_s = job_s * pre / tot
     tokens = w.batch * w.steps
+    layers = sorted(set(u[0] for u in units))
     return {
         "value": tokens / job_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-        "sample": f"{len(tasks)} of {w.units} units (full P={w.prompt}, T={w.steps}), float64 numpy, "
-                  f"{workers} processes x 1 BLAS thread, wall {wall:.2f} s "
-                  f"(mean {sum(per) / len(per):.3f} s per unit); job time scaled by units "
-                  f"({job_s:.0f} s for the whole job)",
+        "sample": f"{len(tasks)} of {w.units} units (full P={w.prompt}, T={w.steps}) drawn with a fixed seed "
+                  f"from layer{'s' if len(layers) > 1 else ''} {' and '.join(map(str, layers))} over all "
+                  f"{w.batch} sequences x {w.heads} heads; float64 numpy, {workers} processes x 1 BLAS thread, "
+                  f"wall {wall:.2f} s; job time scaled by units (extrapolated: {job_s:.0f} s for the whole job)",
+        "prefill_s_job": job_pre_s, "decode_s_job": job_s - job_pre_s,
+        "decode_only_tokens_per_s": tokens / (job_s - job_pre_s),
+        "per_unit_s": {"prefill": pre / len(tasks), "decode": (tot - pre) / len(tasks)},
+        "one_core": {"units": one, "wall_s": wall1, "prefill_s": sum(r[0] for r in res1),
+                     "decode_s": sum(r[1] - r[0] for r in res1),
+                     "tokens_per_s_extrapolated": tokens / (wall1 * (sum(r[1] for r in res1) /
+                                                             sum(r[0] + r[1] for r in res1)) * w.units / one)},
+        "input_generation_s": gen_s,
         "hash_recovered_share": float(np.mean(extra)) if extra and w.family == "hash" else None,
         "q4_output_rel_err": float(np.mean(extra)) if extra and w.cache_bits == 4 and w.family != "hash" else None,
         "q4_units": len(extra) if w.cache_bits == 4 and w.family != "hash" else 0,
@@ -287,26 +343,34 @@ def counter_traffic(workload: str):
     return None
 
 
-def prefill_flops_per_layer(w, prompt_out: bool) -> float:
-    """Algorithmic prefill flops of one layer: one causal Q K^T pass (2 d flops
-    per query-key pair with key <= query) for the row statistics and one for
-    the column sums of every heavy-hitter head, plus one P V pass per unit when
-    the prompt output is produced.  A persistence head needs its last `window`
-    rows twice (their row statistics, then their bits)."""
+def prefill_flops_per_layer(w, prompt_out: bool):
+    """Matrix flops of one layer's prefill, as (algorithmic, issued).
+
+    Algorithmic (what the method needs): one causal Q K^T (2 d flops per
+    query-key pair with key <= query) per unit whose policy scores the prompt
+    (H2O and profiled heads: every row; persistence heads: their last `window`
+    rows), and with the prompt output one causal Q K^T plus one P V for every
+    unit (the scores then come from that same softmax).  Issued (what the
+    kernels run): the column sums recompute Q K^T in a second pass, and the
+    prompt output's P V runs twice (each weight enters as a 16-bit (hi, lo)
+    pair); the difference is implementation overhead."""
     pairs = w.prompt * (w.prompt + 1) / 2
     pol = w.policy_table(0)[0]
-    h2o_units = w.batch * sum(1 for p in pol if p in (1, 6))      # profiled heads need both passes too
-    units = w.batch * w.heads
     per = 2.0 * w.head_dim * pairs
-    persist = 0.0
+    scored = w.batch * sum(1 for p in pol if p in (1, 6))
+    units = w.batch * w.heads
+    tail = 0.0
     for p, win in zip(pol, w.window_table(0)):
         if p == 5:
             rows = min(win, w.prompt)
-            tail_pairs = rows * w.prompt - rows * (rows - 1) / 2     # sum of (i + 1) over the last rows
-            persist += w.batch * 2.0 * w.head_dim * tail_pairs
+            tail += w.batch * 2.0 * w.head_dim * (rows * w.prompt - rows * (rows - 1) / 2)
     if prompt_out:
-        return per * (2 * units + h2o_units) + persist
-    return per * 2 * h2o_units + 2 * persist
+        algo = 2 * per * units
+        issued = 3 * per * units + per * scored + tail
+    else:
+        algo = per * scored + tail
+        issued = 2 * per * scored + 2 * tail
+    return algo, issued
 
 
 def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, cold: bool = False,
@@ -437,6 +501,33 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
             "split": kv.capacity(0) > 1024, "cold_us": cold_us, "choice0": choice0}
 
 
+def stream_read_ceiling(nbytes: float, reps: int = 24, regions: int = 4):
+    """Streaming-read reference on this GPU for one decode launch's bytes:
+    libkvevict's plain read (the decode kernels' 16-byte non-temporal loads)
+    of `nbytes` bytes, cycling over `regions` distinct buffers so that no
+    launch finds its bytes in the Infinity Cache (as the decode's launches
+    cycle over layers), timed with HIP events on the current stream.
+    Returns (GB/s, microseconds per launch)."""
+    import torch
+    from budgeted_decode_attention_amd import binding
+    n4 = (int(nbytes) + 15) // 16 * 4                      # int32 elements per region
+    buf = torch.ones(regions * n4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    views = [buf[i * n4:(i + 1) * n4] for i in range(regions)]
+    stream = torch.cuda.current_stream()
+    for v in views:
+        binding.kvevict_stream_read(v, sink, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(reps):
+        binding.kvevict_stream_read(views[r % regions], sink, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / reps
+    del buf
+    return n4 * 4 / (us * 1e-6) / 1e9, us
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,7 +571,7 @@ def main():
         print(f"[bench] cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
 
     r = run_gpu(w, a.steps, a.warmup, a.sample_every, a.calibration_copy_mib, a.cold, a.prompt_out)
-    pf_flops = prefill_flops_per_layer(w, a.prompt_out) * w.layers
+    pf_algo, pf_issued = (x * w.layers for x in prefill_flops_per_layer(w, a.prompt_out))
     ms = 1e3 * r["wall_s"] / a.steps
     tokens = w.batch * w.steps
     if w.family == "adaptive":
@@ -488,6 +579,7 @@ def main():
     else:
         bytes_launch = decode_bytes_per_layer_step(w, r["ids0"])
     achieved = bytes_launch / (r["kernel_us"] * 1e-6) / 1e9
+    ceiling_gbs, ceiling_us = stream_read_ceiling(bytes_launch)
     kernel = ("decode_partial_kernel + decode_combine_kernel" if r["split"] else "decode_fused_kernel")
     if w.family == "hash":
         kernel = "hash_evict_kernel + " + kernel
@@ -510,7 +602,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(w.name),
                      "kernel": kernel, "bytes_per_launch": bytes_launch,
-                     "kernel_us": r["kernel_us"], "launches_timed": r["n_samples"]},
+                     "kernel_us": r["kernel_us"], "launches_timed": r["n_samples"],
+                     "read_ceiling_gbs": ceiling_gbs, "read_ceiling_us": ceiling_us,
+                     "frac_of_read_ceiling": achieved / ceiling_gbs},
         "cpu_baseline": cpu,
         "detail": {"prefill_ms_per_step": r["prefill_ms"], "decode_ms_per_step": r["decode_ms"],
                    "decode_only_tokens_per_s": tokens / (r["decode_ms"] * 1e-3),
@@ -521,8 +615,17 @@ def main():
                    "q4_error_units": cpu.get("q4_units") if cpu else None,
                    "composites_chosen": ({str(k): int((r["choice0"] == k).sum()) for k in range(1, 6)}
                                          if r["choice0"] is not None else None),
-                   "prefill_algorithmic_tflops": pf_flops / (r["prefill_ms"] * 1e-3) / 1e12,
-                   "prefill_frac_of_dense_16bit_mfma_peak": pf_flops / (r["prefill_ms"] * 1e-3) / 2.5e15,
+                   # FastGen's profile: one float32 per (unit, token) against the
+                   # layer's uncompressed K/V bytes (the page reports 0.78 %)
+                   "profile_memory": ({"bytes_per_layer": w.units_per_layer * w.context * 4,
+                                       "kv_bytes_per_layer": w.units_per_layer * w.context * w.head_dim * 2 *
+                                       {"f32": 4, "f16": 2, "bf16": 2}[w.dtype],
+                                       "frac_of_kv": 4.0 / (2 * w.head_dim * {"f32": 4, "f16": 2, "bf16": 2}[w.dtype])}
+                                      if w.family == "adaptive" else None),
+                   "prefill_algorithmic_tflops": pf_algo / (r["prefill_ms"] * 1e-3) / 1e12,
+                   "prefill_frac_of_dense_16bit_mfma_peak": pf_algo / (r["prefill_ms"] * 1e-3) / 2.5e15,
+                   "prefill_issued_matrix_tflops": pf_issued / (r["prefill_ms"] * 1e-3) / 1e12,
+                   "prefill_recompute_overhead": pf_issued / pf_algo - 1.0 if pf_algo else None,
                    "prefill_counters": prefill_counters(w.name),
                    "input_generation_s": r["gen_s"], "outputs_finite": r["finite"],
                    "cold_kernel_us": r["cold_us"],

@@ -4,6 +4,7 @@ traffic equals the record's own FETCH_SIZE / WRITE_SIZE arithmetic, and a
 record is ignored once its sources no longer hash to the recorded value."""
 
 import glob
+import hashlib
 import os
 import re
 
@@ -48,10 +49,18 @@ def test_decode_traffic_is_the_scaled_counter_sum():
         assert int(rec["traffic_bytes_per_launch"]) == int(total) * 1024, name
 
 
+def _source_hash(rec):
+    h = hashlib.sha256()
+    for f in rec["kernel_sources"].split():
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def test_records_are_read_only_while_their_sources_match(monkeypatch):
-    live = bench._counter_records("opt30b_decode_h2o")
-    assert any("traffic_bytes_per_launch" in r for r in live)
-    assert any("rowstats_mfma_util" in r for r in live)
+    for name, (rec, _) in records().items():
+        live = bench._counter_records(rec["workload"])
+        assert (rec in live) == (_source_hash(rec) == rec["kernel_sources_sha256"]), name
     real_open = open
 
     def changed_sources(path, mode="r", *a, **k):
