@@ -26,7 +26,7 @@ DTYPE_CODES = {torch.float32: KVE_F32, torch.float16: KVE_F16, torch.bfloat16: K
 CODE_DTYPES = {v: k for k, v in DTYPE_CODES.items()}
 
 EXPORTED = ("kvevict_workspace_size", "kvevict_create", "kvevict_destroy", "kvevict_prefill",
-            "kvevict_decode_step", "kvevict_kept_indices", "kvevict_unit_policies", "kvevict_cache_rows",
+            "kvevict_decode_step", "kvevict_decode_step_noalloc", "kvevict_kept_indices", "kvevict_unit_policies", "kvevict_cache_rows",
             "kvevict_capacity", "kvevict_position", "kvevict_stream_read", "kvevict_status_string",
             "kvevict_last_error")
 
@@ -73,6 +73,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvevict_destroy": (i32, [vp]),
         "kvevict_prefill": (i32, [vp, i32, i32, vp, vp, vp, vp, vp, vp]),
         "kvevict_decode_step": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "kvevict_decode_step_noalloc": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
         "kvevict_kept_indices": (i32, [vp, i32, vp, vp, vp, vp]),
         "kvevict_unit_policies": (i32, [vp, i32, vp, vp]),
         "kvevict_cache_rows": (i32, [vp, i32, vp, vp, vp, vp, vp]),
@@ -198,6 +199,13 @@ def kvevict_decode_step(h, layer: int, q, k, v, token_ids=None, out=None, evicte
                                               _ptr(evicted_pos), _stream(stream)), "kvevict_decode_step")
 
 
+def kvevict_decode_step_noalloc(h, layer: int, q, k, v, token_ids=None, out=None, evicted_pos=None,
+                                stream=None) -> None:
+    _check(load_library().kvevict_decode_step_noalloc(h, layer, _ptr(q), _ptr(k), _ptr(v), _ptr(token_ids),
+                                                      _ptr(out), _ptr(evicted_pos), _stream(stream)),
+           "kvevict_decode_step_noalloc")
+
+
 def kvevict_kept_indices(h, layer: int, pos_out, count_out, scores_out=None, stream=None) -> None:
     _check(load_library().kvevict_kept_indices(h, layer, _ptr(pos_out), _ptr(count_out), _ptr(scores_out),
                                                _stream(stream)), "kvevict_kept_indices")
@@ -289,7 +297,10 @@ class KVCache:
         out = self._tensor(out, shp, torch.float32, "out")
         kvevict_prefill(self.handle, layer, P, q, k, v, token_ids, out, stream)
 
-    def decode_step(self, layer: int, q, k, v, token_ids=None, out=None, evicted=None, stream=None):
+    def decode_step(self, layer: int, q, k, v, token_ids=None, out=None, evicted=None, stream=None,
+                    noalloc: bool = False):
+        """One decode step; noalloc=True calls kvevict_decode_step_noalloc (no
+        workspace scratch: the library's static per-GPU array instead)."""
         shp = (self.batch, self.heads, self.head_dim)
         q, k, v = (self._tensor(x, shp, self.dtype, n) for x, n in ((q, "q"), (k, "k"), (v, "v")))
         token_ids = self._tensor(token_ids, (self.batch,), torch.int32, "token_ids")
@@ -297,7 +308,8 @@ class KVCache:
             out = torch.empty(shp, dtype=torch.float32, device=self.device)
         out = self._tensor(out, shp, torch.float32, "out")
         evicted = self._tensor(evicted, (self.batch, self.heads), torch.int32, "evicted")
-        kvevict_decode_step(self.handle, layer, q, k, v, token_ids, out, evicted, stream)
+        fn = kvevict_decode_step_noalloc if noalloc else kvevict_decode_step
+        fn(self.handle, layer, q, k, v, token_ids, out, evicted, stream)
         return out
 
     def unit_policies(self, layer: int, stream=None) -> torch.Tensor:

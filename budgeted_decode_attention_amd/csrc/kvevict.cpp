@@ -287,6 +287,7 @@ struct kve_ctx {
   double* colsum = nullptr;            // device [U][max_context]
   void* qsk = nullptr;                 // device [U][max_context] sketch words
   void* ksk = nullptr;
+  void* static_scratch = nullptr;      // device address of the per-GPU static scratch (null: unavailable)
   bool sync_check = false;
 
   kve::IdSets sets() const { return {bitmap, special, punct, cfg.vocab}; }
@@ -399,6 +400,35 @@ kve_status finish(kve_handle h, hipStream_t st, const char* what) {
   return s;
 }
 
+// One decode step; `scratch` overrides where the split decode keeps its
+// partials and logits (null: the workspace's region).
+kve_status decode_step_impl(kve_handle h, int32_t layer, const void* q, const void* k, const void* v,
+                            const int32_t* token_ids, float* out, int32_t* evicted_pos, void* stream,
+                            const kve::SplitScratch* scratch, const char* what) {
+  kve_status s = check_layer(h, layer);
+  if (s != KVE_OK) return s;
+  Layer& L = h->layers[layer];
+  if (L.position < 0) return fail(KVE_ESTATE, "layer %d: decode before prefill", layer);
+  if (L.position >= h->cfg.max_context)
+    return fail(KVE_ESTATE, "layer %d: position %d reached max_context", layer, L.position);
+  if (!q || !k || !v || !out) return fail(KVE_EINVAL, "q, k, v and out are required");
+  if ((L.info.any_special || L.info.any_adaptive) && !token_ids)
+    return fail(KVE_EINVAL, "token_ids required (layer has SPECIAL or ADAPTIVE heads)");
+  hipStream_t st = (hipStream_t)stream;
+  const kve::Shape& sh = h->shape;
+  hipError_t e = hipSuccess;
+  if (L.hash.n) e = kve::launch_hash_evict(sh, L.cache, L.hash, L.position, q, k, v, evicted_pos, st);
+  if (e == hipSuccess) {
+    const kve::DecodeIO io{q, k, v, token_ids, h->sets(), out, evicted_pos, L.position};
+    const kve::SplitScratch* sp = L.split.chunk ? (scratch ? scratch : &L.split) : nullptr;
+    e = kve::launch_decode(sh, L.cache, io, sp, st);
+  }
+  if (e != hipSuccess) return dev(e, "decode launch");
+  s = finish(h, st, what);
+  if (s == KVE_OK) L.position += 1;
+  return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -484,6 +514,14 @@ kve_status kvevict_create(const kve_config* cfg, void* d_workspace, size_t bytes
     delete ctx;
     return s;
   }
+  // the static scratch of the allocation-free decode entry point, on the
+  // device current at create (where the workspace lives); looked up once per
+  // device.  A failure only disables that entry point, so the error state it
+  // leaves is cleared here rather than reported by a later call.
+  if (kve::static_scratch_address(&ctx->static_scratch) != hipSuccess) {
+    ctx->static_scratch = nullptr;
+    (void)hipGetLastError();
+  }
   *out = ctx;
   return KVE_OK;
 }
@@ -562,27 +600,30 @@ kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t P, const void* q
 
 kve_status kvevict_decode_step(kve_handle h, int32_t layer, const void* q, const void* k, const void* v,
                                const int32_t* token_ids, float* out, int32_t* evicted_pos, void* stream) {
+  return decode_step_impl(h, layer, q, k, v, token_ids, out, evicted_pos, stream, nullptr, "decode_step");
+}
+
+kve_status kvevict_decode_step_noalloc(kve_handle h, int32_t layer, const void* q, const void* k, const void* v,
+                                       const int32_t* token_ids, float* out, int32_t* evicted_pos,
+                                       void* stream) {
   kve_status s = check_layer(h, layer);
   if (s != KVE_OK) return s;
-  Layer& L = h->layers[layer];
-  if (L.position < 0) return fail(KVE_ESTATE, "layer %d: decode before prefill", layer);
-  if (L.position >= h->cfg.max_context)
-    return fail(KVE_ESTATE, "layer %d: position %d reached max_context", layer, L.position);
-  if (!q || !k || !v || !out) return fail(KVE_EINVAL, "q, k, v and out are required");
-  if ((L.info.any_special || L.info.any_adaptive) && !token_ids)
-    return fail(KVE_EINVAL, "token_ids required (layer has SPECIAL or ADAPTIVE heads)");
-  hipStream_t st = (hipStream_t)stream;
-  const kve::Shape& sh = h->shape;
-  hipError_t e = hipSuccess;
-  if (L.hash.n) e = kve::launch_hash_evict(sh, L.cache, L.hash, L.position, q, k, v, evicted_pos, st);
-  if (e == hipSuccess) {
-    const kve::DecodeIO io{q, k, v, token_ids, h->sets(), out, evicted_pos, L.position};
-    e = kve::launch_decode(sh, L.cache, io, L.split.chunk ? &L.split : nullptr, st);
-  }
-  if (e != hipSuccess) return dev(e, "decode launch");
-  s = finish(h, st, "decode_step");
-  if (s == KVE_OK) L.position += 1;
-  return s;
+  const Layer& L = h->layers[layer];
+  if (!L.split.chunk)          // fused layers use no scratch at all
+    return decode_step_impl(h, layer, q, k, v, token_ids, out, evicted_pos, stream, nullptr, "decode_step_noalloc");
+  // partials [U][nch][d + 2] float, then logits [U][cap] float, 256-byte aligned
+  const size_t U = h->shape.units(), d = h->shape.d;
+  const size_t part_bytes = align_up(U * (size_t)L.split.max_chunks * (d + 2) * sizeof(float));
+  const size_t need = part_bytes + align_up(U * (size_t)L.cache.cap * sizeof(float));
+  if (need > kve::static_scratch_bytes())
+    return fail(KVE_EUNSUPPORTED, "layer %d: the split decode needs %zu bytes of scratch; the static scratch holds %zu",
+                layer, need, kve::static_scratch_bytes());
+  if (!h->static_scratch)
+    return fail(KVE_EDEVICE, "the static scratch's device address could not be looked up at create");
+  char* base = static_cast<char*>(h->static_scratch);
+  const kve::SplitScratch sp{reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + part_bytes),
+                             L.split.chunk, L.split.max_chunks};
+  return decode_step_impl(h, layer, q, k, v, token_ids, out, evicted_pos, stream, &sp, "decode_step_noalloc");
 }
 
 kve_status kvevict_kept_indices(kve_handle h, int32_t layer, int32_t* pos_out, int32_t* count_out,

@@ -169,6 +169,12 @@ struct SplitScratch {
 hipError_t launch_decode(const Shape& sh, const LayerCache& c, const DecodeIO& io,
                          const SplitScratch* sp, hipStream_t st);
 
+// ---- static scratch (the allocation-free decode entry point)
+// Size of the per-GPU static scratch array, and its device address on the
+// current device (looked up once per device; thread-safe).
+size_t static_scratch_bytes();
+hipError_t static_scratch_address(void** out);
+
 // ---- measurement
 // Reads `bytes` (a multiple of 16, 16-byte aligned) of src with the decode
 // kernels' 16-byte non-temporal loads; writes nothing in practice (sink is

@@ -207,6 +207,25 @@ kve_status kvevict_decode_step(kve_handle h, int32_t layer,
                                const int32_t* token_ids, float* out, int32_t* evicted_pos,
                                void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as kvevict_decode_step, with the same arguments, results and errors,
+ * except that layers using the split decode (slot stride above 1,024) keep
+ * its per-chunk partials and logits in a static device array of the library
+ * (32 MiB per GPU, held from the library's load on that GPU until the process
+ * ends) instead of the workspace.  Nothing is allocated and no scratch needs
+ * clearing: every partial and logit a step reads is written earlier in the
+ * same step.  KVE_EUNSUPPORTED if the layer needs more than the array holds
+ * (batch * heads * (chunks * (head_dim + 2) + capacity) * 4 bytes, each part
+ * rounded up to 256), KVE_EDEVICE if the array's address could not be looked
+ * up when the handle was created.  Every call on one GPU, from any handle,
+ * shares the array: calls that overlap on one GPU (different streams or host
+ * threads) race and must be serialised by the caller. */
+kve_status kvevict_decode_step_noalloc(kve_handle h, int32_t layer,
+                                       const void* q, const void* k, const void* v,
+                                       const int32_t* token_ids, float* out, int32_t* evicted_pos,
+                                       void* stream);
+
 /* Exports one layer's cache in slot order.
  * pos_out: [batch][heads][capacity] int32 position held by each slot, -1 for
  * an empty slot.  count_out: [batch][heads] int32 number of occupied slots.

@@ -22,7 +22,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     lib = binding.load_library()
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert set(names) == set(binding.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -211,3 +211,8 @@ def test_stream_read_validates_arguments():
     assert lib.kvevict_stream_read(fake, 0, sink, None) == binding.KVE_EINVAL
     assert lib.kvevict_stream_read(fake, 72, sink, None) == binding.KVE_EINVAL          # not a multiple of 16
     assert lib.kvevict_stream_read(ctypes.c_void_p((1 << 40) + 8), 64, sink, None) == binding.KVE_EINVAL
+
+
+def test_decode_step_noalloc_validates_on_the_host():
+    lib = binding.load_library()
+    assert lib.kvevict_decode_step_noalloc(None, 0, None, None, None, None, None, None, None) == binding.KVE_EINVAL
