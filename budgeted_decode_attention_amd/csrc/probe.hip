@@ -9,8 +9,8 @@ namespace kve {
 namespace {
 
 constexpr int kNT = 256;
-constexpr int kInFlight = 8;                    // 16-byte loads per thread per round
-constexpr size_t kBlockBytes = (size_t)kNT * 16 * kInFlight * 4;   // 128 KiB per workgroup
+constexpr int kInFlight = 4;                    // 16-byte loads per thread per round
+constexpr size_t kBlockBytes = (size_t)kNT * 16 * kInFlight * 2;   // 32 KiB per workgroup
 
 __device__ inline uint4 ld_stream(const uint4* p) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
