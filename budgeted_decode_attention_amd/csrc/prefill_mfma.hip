@@ -95,15 +95,28 @@ template <int D> struct TileRegs {
   uint4 v[kChunks];
 };
 
+// Buffer resource over rows [r0, P) of a unit's [P][D] 16-bit matrix: raw
+// buffer loads check their (per-lane) offset against the byte count, so
+// rows at or past P read as zero with no compare, select or 64-bit address
+// arithmetic per load.  The third descriptor word is the gfx9-family raw
+// buffer format (32-bit data, no swizzle).
+template <int D>
+__device__ inline __amdgpu_buffer_rsrc_t rows_rsrc(const char* src, int r0, int P) {
+  const uint32_t bytes = r0 < P ? (uint32_t)(P - r0) * D * 2 : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src) + (size_t)r0 * D * 2, (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // Rows at or past P read as zero.
 template <int D>
 __device__ inline void load_tile(TileRegs<D>& t, const char* src, int r0, int P) {
   constexpr int CPR = TileRegs<D>::CPR;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc<D>(src, r0, P);
 #pragma unroll
   for (int j = 0; j < TileRegs<D>::kChunks; ++j) {
     const int i = threadIdx.x + j * kNT;
     const int r = i / CPR, c = i % CPR;
-    t.v[j] = r0 + r < P ? ld16(src + ((size_t)(r0 + r) * D) * 2 + c * 16) : make_uint4(0, 0, 0, 0);
+    t.v[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, r * D * 2 + c * 16, 0, 0));
   }
 }
 
@@ -227,24 +240,37 @@ __device__ inline Scale2 make_scale2(float scale) {
   return {hi, (float)(c - (double)hi)};
 }
 
+// Logit given to masked pairs: its weight exp2(x c - m) underflows to 0 and
+// it never sets a maximum; x c stays finite for any positive scale.
+__device__ inline float masked_logit(const Scale2& c2) { return -1e30f / fmaxf(c2.hi, 1.f); }
+
 // ------------------------------------------------------------------ rowstats
-// Folds one 64-key tile (already in acc) into the online statistics of this
-// lane's two queries.  EDGE: some keys follow a query or lie past P.
-template <bool EDGE>
-__device__ inline void rowstats_fold(const f32x4 (&acc)[4][2], int k0, int q0, int P, int g, int c16,
-                                     const Scale2& c2, float (&mc)[2], double (&l)[2]) {
+// Diagonal and last tiles: pairs whose key follows the query or lies at or
+// past P get the masked logit.  Every query of a processed tile keeps at
+// least its first key (a tile starts at or before the wave's first query).
+__device__ inline void rowstats_mask(f32x4 (&acc)[4][2], int k0, int q0, int P, int g, int c16, float msk) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int qi = q0 + nb * 16 + c16;
+    const int lim = min(q0 + nb * 16 + c16, P - 1) - k0 - 4 * g;   // largest valid mb 16 + r
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (mb * 16 + r > lim) acc[mb][nb][r] = msk;
+  }
+}
+
+// Folds one 64-key tile (already in acc, edge tiles masked) into the online
+// statistics of this lane's two queries: raises the offset to the tile's
+// maximum where it is larger, then adds the tile's weights.
+__device__ inline void rowstats_fold(const f32x4 (&acc)[4][2], const Scale2& c2, float (&mc)[2], double (&l)[2]) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
     float tmax = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kj = k0 + mb * 16 + g * 4 + r;
-        const bool ok = !EDGE || (kj <= qi && kj < P);
-        tmax = fmaxf(tmax, ok ? acc[mb][nb][r] : -INFINITY);
-      }
+      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, acc[mb][nb][r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float mn = fmaxf(mc[nb], tmax * c2.hi);
@@ -258,13 +284,7 @@ __device__ inline void rowstats_fold(const f32x4 (&acc)[4][2], int k0, int q0, i
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float s = acc[mb][nb][r];
-        const float p = exp2_fast(fmaf(s, c2.lo, fmaf(s, c2.hi, -mn)));
-        if (EDGE) {
-          const int kj = k0 + mb * 16 + g * 4 + r;
-          sum += (kj <= qi && kj < P) ? p : 0.f;
-        } else {
-          sum += p;
-        }
+        sum += exp2_fast(fmaf(s, c2.lo, fmaf(s, c2.hi, -mn)));
       }
     l[nb] += (double)sum;
   }
@@ -313,6 +333,7 @@ void rowstats_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const voi
   const char* kbase = (const char*)k + base;
   const int q0 = qb * kBlk + w * 32;            // this wave's first query
   const Scale2 c2 = make_scale2(sh.scale);
+  const float msk = masked_logit(c2);
 
   // B fragments: the wave's 32 queries
   uint4 qf[2][KS];
@@ -349,8 +370,12 @@ void rowstats_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const voi
           for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = Mfma<DT>::run(a, qf[nb][ks], acc[mb][nb]);
         }
       }
-      if (k0 + kTile > q0 || k0 + kTile > P) rowstats_fold<true>(acc, k0, q0, P, g, c16, c2, mc, l);
-      else if (k0 == 0 || !rowstats_fold_lazy(acc, c2, mc, l)) rowstats_fold<false>(acc, k0, q0, P, g, c16, c2, mc, l);
+      if (k0 + kTile > q0 || k0 + kTile > P) {
+        rowstats_mask(acc, k0, q0, P, g, c16, msk);
+        rowstats_fold(acc, c2, mc, l);
+      } else if (k0 == 0 || !rowstats_fold_lazy(acc, c2, mc, l)) {
+        rowstats_fold(acc, c2, mc, l);
+      }
     }
     if (more) store_tile<D>(nxt, Ks[(it + 1) & 1]);   // that buffer was last read before the previous barrier
     __syncthreads();
@@ -372,26 +397,30 @@ void rowstats_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const voi
 
 // ------------------------------------------------------------------ colsum
 // Adds one 64-query tile's weights exp2(s * c2 - lse2) into part (this lane's
-// keys).  EDGE: some query precedes a key of the wave or lies past P.
-// The low word of lse2 enters as the factor fl = 2^-ll on the weight, taken
-// by the accumulating fused multiply-add.
-template <bool EDGE>
-__device__ inline void colsum_fold(const f32x4 (&acc)[2], int i0, int nb, int j0, int P, int g, int c16,
-                                   const Scale2& c2, float lh, float fl, float (&part)[2][4]) {
-  const int qi = i0 + nb * 16 + c16;
+// keys; edge tiles masked).  The low word of lse2 enters as the factor
+// fl = 2^-ll on the weight, taken by the accumulating fused multiply-add.
+__device__ inline void colsum_fold(const f32x4 (&acc)[2], const Scale2& c2, float lh, float fl,
+                                   float (&part)[2][4]) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float s = acc[mb][r];
       const float p = exp2_fast(fmaf(s, c2.lo, fmaf(s, c2.hi, -lh)));
-      if (EDGE) {
-        const int kj = j0 + mb * 16 + g * 4 + r;
-        part[mb][r] = (qi < P && qi >= kj) ? fmaf(p, fl, part[mb][r]) : part[mb][r];
-      } else {
-        part[mb][r] = fmaf(p, fl, part[mb][r]);
-      }
+      part[mb][r] = fmaf(p, fl, part[mb][r]);
     }
+}
+
+// Diagonal and last tiles: pairs whose query precedes the key or lies at or
+// past P get the masked logit (weight 0).
+__device__ inline void colsum_mask(f32x4 (&acc)[2], int i0, int nb, int j0, int P, int g, int c16, float msk) {
+  const int qi = i0 + nb * 16 + c16;
+  const int lim = qi < P ? qi - j0 - 4 * g : -1;   // largest valid mb 16 + r
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (mb * 16 + r > lim) acc[mb][r] = msk;
 }
 
 // colsum_fold with masks, also adding the weights of rows >= wlo into pm.
@@ -458,6 +487,7 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
   const char* kbase = (const char*)k + base;
   const int j0 = kb * kBlk + w * 32;            // this wave's first key
   const Scale2 c2 = make_scale2(sh.scale);
+  const float msk = masked_logit(c2);
 
   uint4 kf[2][KS];                              // A fragments: the wave's 32 keys
 #pragma unroll
@@ -532,8 +562,10 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
         const float lh = Lh[buf][nb * 16 + c16];
         if (BITS) persist_fold(acc, i0, nb, j0, P, wlo, g, c16, c2, lh, Ll[buf][nb * 16 + c16], Th[buf][nb * 16 + c16], bits);
         else if (in_rows) mass_fold(acc, i0, nb, j0, P, wlo, g, c16, c2, lh, Lf[buf][nb * 16 + c16], part, pm);
-        else if (edge) colsum_fold<true>(acc, i0, nb, j0, P, g, c16, c2, lh, Lf[buf][nb * 16 + c16], part);
-        else colsum_fold<false>(acc, i0, nb, j0, P, g, c16, c2, lh, Lf[buf][nb * 16 + c16], part);
+        else {
+          if (edge) colsum_mask(acc, i0, nb, j0, P, g, c16, msk);
+          colsum_fold(acc, c2, lh, Lf[buf][nb * 16 + c16], part);
+        }
       }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
