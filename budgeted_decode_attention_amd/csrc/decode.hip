@@ -30,6 +30,7 @@
 // accumulates w * scale * (c + 8) and subtracts 8 * sum(w * scale) at the end.  Token t's own key and
 // value are read from the inputs at full precision and quantised into its slot.
 #include "common.hpp"
+#include "hash.hpp"
 #include "q4.hpp"
 
 namespace kve {
@@ -505,11 +506,19 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
 }
 
 // ------------------------------------------------------------------ fused
+// Dynamic LDS of the fused kernel: the [cap + 1] weights, then (layers with
+// HASH units) the replacement's projection and rows.
+__host__ __device__ constexpr size_t fused_wts_bytes(int cap) { return ((size_t)cap + 1 + 3) / 4 * 16; }
+
+// One workgroup per unit.  HASH units first run HashEvict's pre-attention
+// replacement in the same workgroup (token t takes the farthest key's slot,
+// or is appended), so a step is one launch and the passes below read token t
+// from its slot like every kept token.
 template <int DT, int D, bool Q4>
 __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, DecodeIO io) {
   using R = Rows<DT, D>;
   using Y = Lay<DT, D, Q4>;
-  extern __shared__ float wts[];                 // [cap + 1]
+  extern __shared__ __attribute__((aligned(16))) float wts[];   // [cap + 1], then the replacement's LDS
   __shared__ float red[Y::NRED * D];
   __shared__ float fscr[kNT / kWave];
   __shared__ double dscr[kNT / kWave];
@@ -520,8 +529,16 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
   const int col = tid % Y::LPR;
   const int rg = tid / Y::LPR;
   const HeadMeta m = c.meta[u];
-  const int n = c.count[u];
-  const int with_new = m.policy == HASH ? 0 : 1;  // HASH: token t is already in a slot
+  int n = c.count[u];
+  if (m.policy == HASH) {                        // uniform over the workgroup
+    char* hl = reinterpret_cast<char*>(wts) + fused_wts_bytes(c.cap);
+    switch (c.sk_bits) {
+      case 16: n = hash_replace<DT, D, 16>(c, u, io.t, m.heavy, n, io.q, io.k, io.v, io.evicted, hl); break;
+      case 64: n = hash_replace<DT, D, 64>(c, u, io.t, m.heavy, n, io.q, io.k, io.v, io.evicted, hl); break;
+      default: n = hash_replace<DT, D, 32>(c, u, io.t, m.heavy, n, io.q, io.k, io.v, io.evicted, hl); break;
+    }
+  }
+  const int with_new = m.policy == HASH ? 0 : 1;  // HASH: token t is now in a slot
   const size_t slot0 = (size_t)u * c.cap;
   const char* Kb = (const char*)c.K + slot0 * (Q4 ? D / 2 : D * R::ES);
   const char* Vb = (const char*)c.V + slot0 * (Q4 ? D / 2 : D * R::ES);
@@ -761,7 +778,8 @@ template <int DT, int D, bool Q4>
 hipError_t launch_f(const Shape& sh, const LayerCache& c, const DecodeIO& io, const SplitScratch* sp,
                     hipStream_t st) {
   if (!sp) {
-    const size_t lds = (size_t)(c.cap + 1) * sizeof(float);
+    size_t lds = fused_wts_bytes(c.cap);
+    if (c.sk) lds += c.sk_bits == 64 ? hash_replace_lds<D, 64>() : hash_replace_lds<D, 32>();
     hipError_t e = set_lds((const void*)decode_fused_kernel<DT, D, Q4>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_fused_kernel<DT, D, Q4>), dim3(sh.units()), dim3(kNT), lds, st, sh, c, io);

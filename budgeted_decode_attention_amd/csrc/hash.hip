@@ -21,79 +21,12 @@
 // With 4-bit slots the rows entering the cache (the replay's gather, the
 // replacement at each step) are quantised; sketches always come from the
 // inputs.
-#include "common.hpp"
-#include "q4.hpp"
+#include "hash.hpp"
 
 namespace kve {
 namespace {
 
 constexpr int kNT = 256;
-
-template <int BITS> struct SkWord { using T = uint32_t; };
-template <> struct SkWord<64> { using T = uint64_t; };
-__device__ inline int popcnt(uint32_t x) { return __popc(x); }
-__device__ inline int popcnt(uint64_t x) { return __popcll(x); }
-
-// The BITS-bit field of a wave ballot that starts at lane `first`.
-template <int BITS> __device__ inline typename SkWord<BITS>::T ballot_field(uint64_t m, int first) {
-  if constexpr (BITS == 64) return m;
-  else return (typename SkWord<BITS>::T)((m >> first) & ((1ull << BITS) - 1ull));
-}
-
-__device__ inline double bf16_to_double(uint16_t w) { return (double)__uint_as_float((uint32_t)w << 16); }
-
-// Exact sign of sum_i a_i b_i (each product exact in float64), by growing a
-// zero-free non-overlapping expansion with two-sum.  Rarely taken.
-template <int DT, int D>
-__device__ __attribute__((noinline)) int exact_sign(const char* row, const uint16_t* W, int bits, int b) {
-  double e[D + 1];
-  int len = 0;
-  for (int i = 0; i < D; ++i) {
-    double q = (double)load_elem<DT>(row, i) * bf16_to_double(W[i * bits + b]);
-    int k = 0;
-    for (int j = 0; j < len; ++j) {
-      const double s = q + e[j];
-      const double bv = s - q;
-      const double av = s - bv;
-      const double err = (q - av) + (e[j] - bv);
-      q = s;
-      if (err != 0.0) e[k++] = err;
-    }
-    if (q != 0.0) e[k++] = q;
-    len = k;
-  }
-  if (len == 0) return 0;
-  return e[len - 1] > 0.0 ? 1 : 0;   // the largest component carries the sign
-}
-
-// Sign bit b of a row: float64 dot with the error bound, exact fallback.
-// xs: the row as floats (LDS), Ws: the projection as bf16 bits (LDS); the
-// exact fallback re-reads the row and projection from global memory.
-template <int DT, int D>
-__device__ inline int sketch_bit(const float* xs, const uint16_t* Ws, const char* row, const uint16_t* W,
-                                 int bits, int b) {
-  double s = 0.0, a = 0.0;
-#pragma unroll 8
-  for (int i = 0; i < D; ++i) {
-    const double x = (double)xs[i];
-    const double w = bf16_to_double(Ws[i * bits + b]);
-    s = fma(x, w, s);
-    a = fma(fabs(x), fabs(w), a);
-  }
-  // |s - exact| <= gamma_D * sum|terms|; sum|terms| itself is computed with a
-  // relative error below gamma_D, so gamma_{2D+2} bounds the comparison.
-  constexpr double u = 1.1102230246251565e-16;
-  constexpr double g = (2 * D + 2) * u / (1.0 - (2 * D + 2) * u);
-  if (fabs(s) > g * a) return s > 0.0 ? 1 : 0;
-  return exact_sign<DT, D>(row, W, bits, b);
-}
-
-// Copies the [D][BITS] bf16 projection into LDS (all threads of the workgroup).
-template <int D, int BITS>
-__device__ inline void stage_proj(uint16_t* Ws, const uint16_t* W) {
-  for (int i = threadIdx.x; i < D * BITS / 8; i += kNT)
-    reinterpret_cast<uint4*>(Ws)[i] = reinterpret_cast<const uint4*>(W)[i];
-}
 
 constexpr int kSketchRows = 64;   // rows per workgroup in sketch_rows_kernel
 
@@ -107,6 +40,7 @@ __global__ __launch_bounds__(kNT) void sketch_rows_kernel(Shape sh, UnitList ul,
   constexpr int RPP = kNT / BITS;                            // rows per pass
   __shared__ __attribute__((aligned(16))) uint16_t Ws[D * BITS];
   __shared__ float xs[RPP][D];
+  __shared__ double ebuf[kNT / kWave][D + 1];                // the exact fallback, per wave
   constexpr int ES = elem_bytes<DT>();
   const int u = ul.ids ? ul.ids[blockIdx.y] : blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
@@ -120,36 +54,10 @@ __global__ __launch_bounds__(kNT) void sketch_rows_kernel(Shape sh, UnitList ul,
     __syncthreads();                                        // previous pass done with xs; Ws staged
     for (int i = b; i < D; i += BITS) xs[slot][i] = ok ? load_elem<DT>(row, i) : 0.f;
     __syncthreads();
-    const int bit = ok ? sketch_bit<DT, D>(xs[slot], Ws, row, proj, BITS, b) : 0;
+    const int bit = sketch_bit<DT, D>(ok, xs[slot], Ws, row, proj, BITS, b, ebuf[threadIdx.x / kWave]);
     const uint64_t m = __ballot(bit != 0);
     if (ok && b == 0) out[(size_t)u * P + row0 + r] = ballot_field<BITS>(m, lane);
   }
-}
-
-// Eviction keys: distance << 16 | (65535 - position).  The maximum is the
-// farthest key, then the oldest position; positions in a cache are distinct
-// and below 65536, so a non-zero maximum is unique.  Lanes without a
-// candidate hold 0.
-__device__ inline uint32_t evict_key(uint32_t dist, int pos) { return (dist << 16) | (uint32_t)(0xFFFF - pos); }
-__device__ inline int key_position(uint32_t key) { return 0xFFFF - (int)(key & 0xFFFF); }
-
-// The wave's largest key (every lane receives it): DPP within each 16-lane
-// row, then the four rows' values.
-__device__ inline uint32_t wave_max_key(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
-  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
-             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
-}
-
-// (wave maximum << 32 | the slot of the lane that holds it); a wave with no
-// candidate reports key 0.
-__device__ inline uint64_t wave_best(uint32_t best, int bslot) {
-  const uint32_t wm = wave_max_key(best);
-  const int wl = __builtin_ctzll(__ballot(best == wm));
-  return ((uint64_t)wm << 32) | (uint32_t)__builtin_amdgcn_readlane(bslot, wl);
 }
 
 // Prompt replay for one HASH unit per workgroup; slot state in LDS.
@@ -259,117 +167,16 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
   }
 }
 
-// Decode-time replacement for one HASH unit per workgroup.
+// Decode-time replacement for one HASH unit per workgroup (layers that take
+// the split decode; the fused decode runs the same replacement itself).
 template <int DT, int D, int BITS>
 __global__ __launch_bounds__(kNT) void hash_evict_kernel(Shape sh, LayerCache c, UnitList ul, int t,
                                                          const void* q, const void* k, const void* v,
                                                          int32_t* evicted) {
-  using SW = typename SkWord<BITS>::T;
-  constexpr int EPL = St<DT>::EPL;
-  constexpr int ES = elem_bytes<DT>();
-  constexpr int LPR = D / EPL;
-  __shared__ SW sk2[2];
-  __shared__ uint64_t kscr[kNT / kWave];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[D * BITS];
-  __shared__ float xs[2][D];
+  static_assert(kNT == kHashNT, "workgroup size");
+  __shared__ __attribute__((aligned(16))) char lds[hash_replace_lds<D, BITS>()];
   const int u = ul.ids[blockIdx.x];
-  const int tid = threadIdx.x;
-  const HeadMeta m = c.meta[u];
-  const int B = m.heavy;
-  stage_proj<D, BITS>(Ws, c.proj);
-  for (int i = tid; i < 2 * D; i += kNT)
-    xs[i / D][i % D] = load_elem<DT>((const char*)(i < D ? q : k) + (size_t)u * D * ES, i % D);
-  __syncthreads();
-  // threads [0, BITS) sketch q, [BITS, 2 BITS) sketch k; one bit per lane
-  if (tid < 2 * BITS) {
-    const int r = tid / BITS, b = tid % BITS;
-    const char* row = (const char*)(r ? k : q) + (size_t)u * D * ES;
-    const int bit = sketch_bit<DT, D>(xs[r], Ws, row, c.proj, BITS, b);
-    const uint64_t msk = __ballot(bit != 0);
-    if (b == 0) sk2[r] = ballot_field<BITS>(msk, tid & (kWave - 1));
-  }
-  __syncthreads();
-  const size_t slot0 = (size_t)u * c.cap;
-  const int n = c.count[u];
-  int slot, ev;
-  if (n >= B) {
-    const SW qs = sk2[0];
-    uint32_t best = 0;
-    int bslot = 0;
-    // PER slots per 16-byte load of sketches (4 of 32 bits, 2 of 64) and the
-    // matching load of positions when the unit's first slot is aligned
-    // (slot0 % PER == 0); the remainder, or every slot otherwise, one at a time
-    constexpr int PER = 16 / (int)sizeof(SW);
-    const SW* skp = reinterpret_cast<const SW*>(c.sk) + slot0;
-    const int32_t* psp = c.pos + slot0;
-    const bool vec = (slot0 % PER) == 0;
-    const int nv = vec ? (n / PER) * PER : 0;
-    for (int sv = tid * PER; sv < nv; sv += kNT * PER) {
-      const uint4 a = *reinterpret_cast<const uint4*>(skp + sv);
-      SW av[PER];
-      int32_t pv[PER];
-      __builtin_memcpy(av, &a, 16);
-      if constexpr (PER == 4) {
-        const int4 p = *reinterpret_cast<const int4*>(psp + sv);
-        pv[0] = p.x; pv[1] = p.y; pv[2] = p.z; pv[3] = p.w;
-      } else {
-        const int2 p = *reinterpret_cast<const int2*>(psp + sv);
-        pv[0] = p.x; pv[1] = p.y;
-      }
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const uint32_t key = evict_key(popcnt(qs ^ av[j]), pv[j]);
-        if (key > best) {
-          best = key;
-          bslot = sv + j;
-        }
-      }
-    }
-    for (int s = nv + tid; s < n; s += kNT) {
-      const uint32_t key = evict_key(popcnt(qs ^ skp[s]), psp[s]);
-      if (key > best) {
-        best = key;
-        bslot = s;
-      }
-    }
-    const uint64_t wb = wave_best(best, bslot);
-    if ((tid & (kWave - 1)) == 0) kscr[tid / kWave] = wb;
-    __syncthreads();
-    uint64_t bb = kscr[0];
-#pragma unroll
-    for (int w = 1; w < kNT / kWave; ++w) bb = kscr[w] > bb ? kscr[w] : bb;
-    slot = (int)(bb & 0xFFFFFFFFu);
-    ev = key_position((uint32_t)(bb >> 32));
-  } else {
-    slot = n;
-    ev = -1;
-  }
-  __syncthreads();
-  if (c.q4) {
-    // one element per thread: threads [0, D) the key row, [D, 2D) the value row
-    constexpr int G = D / kQGroup;
-    if (tid < 2 * D) {
-      const bool val = tid >= D;
-      const int e = tid - (val ? D : 0);
-      const size_t row = slot0 + slot;
-      const float x = load_elem<DT>((const char*)(val ? v : k) + (size_t)u * D * ES, e);
-      q4_quantize_lane(x, e, (char*)(val ? c.V : c.K) + row * (D / 2), (val ? c.Vsc : c.Ksc) + row * G);
-    }
-  } else {
-    char* Kd = (char*)c.K + (slot0 + slot) * D * ES;
-    char* Vd = (char*)c.V + (slot0 + slot) * D * ES;
-    if (tid < LPR) {
-      st16(Kd + tid * EPL * ES, ld16((const char*)k + ((size_t)u * D + tid * EPL) * ES));
-      st16(Vd + tid * EPL * ES, ld16((const char*)v + ((size_t)u * D + tid * EPL) * ES));
-    }
-  }
-  if (tid == 0) {
-    c.pos[slot0 + slot] = t;
-    reinterpret_cast<SW*>(c.sk)[slot0 + slot] = sk2[1];
-    c.S[slot0 + slot] = 0.0;
-    if (slot == n) c.count[u] = n + 1;
-    if (evicted) evicted[u] = ev;
-  }
+  hash_replace<DT, D, BITS>(c, u, t, c.meta[u].heavy, c.count[u], q, k, v, evicted, lds);
 }
 
 #define KVE_DISPATCH_D(FN, BITS, ...)                                           \

@@ -417,7 +417,9 @@ kve_status decode_step_impl(kve_handle h, int32_t layer, const void* q, const vo
   hipStream_t st = (hipStream_t)stream;
   const kve::Shape& sh = h->shape;
   hipError_t e = hipSuccess;
-  if (L.hash.n) e = kve::launch_hash_evict(sh, L.cache, L.hash, L.position, q, k, v, evicted_pos, st);
+  // HASH units: the pre-attention replacement runs as its own launch before
+  // the split decode; the fused decode runs it inside each unit's workgroup
+  if (L.hash.n && L.split.chunk) e = kve::launch_hash_evict(sh, L.cache, L.hash, L.position, q, k, v, evicted_pos, st);
   if (e == hipSuccess) {
     const kve::DecodeIO io{q, k, v, token_ids, h->sets(), out, evicted_pos, L.position};
     const kve::SplitScratch* sp = L.split.chunk ? (scratch ? scratch : &L.split) : nullptr;
