@@ -115,6 +115,7 @@ struct LayerInfo {
   int nch = 0;           // chunks per unit
   bool any_h2o = false, any_hash = false, any_special = false, any_persist = false, any_adaptive = false;
   int max_hash_budget = 0;
+  int min_hash_budget = 0;   // smallest HASH budget of the layer (0: none)
   int max_window = 0;    // largest history window of the layer's PERSIST heads
   int ad_heavy = -1, ad_recent = -1;   // the layer's ADAPTIVE heads' frequent slots and local window
   std::vector<int32_t> h2o_units, hash_units, persist_units, adaptive_units;
@@ -175,6 +176,7 @@ kve_status validate(const kve_config* c, std::vector<LayerInfo>* info) {
                         std::min(c->max_context, c->sketch_bits == 64 ? kMaxHashBudget64 : kMaxHashBudget));
           li.any_hash = true;
           li.max_hash_budget = std::max(li.max_hash_budget, hv);
+          li.min_hash_budget = li.min_hash_budget ? std::min(li.min_hash_budget, hv) : hv;
           need_proj = true;
           break;
         case KVE_ADAPTIVE:
@@ -589,7 +591,10 @@ kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t P, const void* q
     e = kve::launch_prefill_select(sh, L.cache, P, h->colsum, k, v, token_ids, h->sets(), st);
   if (e == hipSuccess && L.hash.n) {
     const int bits = h->cfg.sketch_bits;
-    e = kve::launch_sketch_rows(sh, L.hash, q, P, 0, P, L.cache.proj, bits, h->qsk, st);
+    // the replay ranks with the queries of positions [B, P) only (B the
+    // unit's budget), and every prompt key's sketch
+    const int q0 = std::min(P, L.info.min_hash_budget);
+    e = kve::launch_sketch_rows(sh, L.hash, q, P, q0, P - q0, L.cache.proj, bits, h->qsk, st);
     if (e == hipSuccess) e = kve::launch_sketch_rows(sh, L.hash, k, P, 0, P, L.cache.proj, bits, h->ksk, st);
     if (e == hipSuccess)
       e = kve::launch_hash_prefill(sh, L.cache, L.hash, P, L.info.max_hash_budget, h->qsk, h->ksk, k, v, st);
