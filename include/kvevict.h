@@ -195,7 +195,16 @@ kve_status kvevict_prefill(kve_handle h, int32_t layer, int32_t prompt_len,
                            const void* q, const void* k, const void* v,
                            const int32_t* token_ids, float* out, void* stream);
 
-/* One decode step of one layer at its current position t (then t + 1).
+/* One decode step of one layer at its current position t (then t + 1): per
+ * unit, attention of the step's query over the kept slots and token t, each
+ * kept slot's score raised by its softmax weight, then the head's policy
+ * frees a slot for token t (H2O review page, proposed method: each decode
+ * step's attention statistics drive a greedy eviction of the token expected
+ * to matter least, with the recent tokens kept; Scissorhands summary page,
+ * Abstract: the cache stays at a fixed budget; FastGen review page, proposed
+ * method: the per-head positional and id-based policies; HashEvict summary
+ * page, original abstract: HASH heads replace the farthest key by sketch
+ * before attention).
  * q, k, v: [batch][heads][d] storage dtype, the new token's projections.
  * token_ids: [batch] int32 (required if the layer has a SPECIAL or ADAPTIVE head).
  * out: [batch][heads][d] fp32 attention output of the step.
@@ -226,7 +235,11 @@ kve_status kvevict_decode_step_noalloc(kve_handle h, int32_t layer,
                                        const int32_t* token_ids, float* out, int32_t* evicted_pos,
                                        void* stream);
 
-/* Exports one layer's cache in slot order.
+/* Exports one layer's cache in slot order: which prompt and generated
+ * tokens each unit still keeps, and their accumulated scores (the kept set
+ * the eviction policies maintain -- H2O review page, proposed method:
+ * heavy hitters plus recent tokens; Scissorhands summary page, Abstract: the
+ * pivotal tokens kept under a fixed budget).
  * pos_out: [batch][heads][capacity] int32 position held by each slot, -1 for
  * an empty slot.  count_out: [batch][heads] int32 number of occupied slots.
  * scores_out: [batch][heads][capacity] float64 accumulated score per slot
