@@ -466,9 +466,11 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
     cold_us = None
     if cold:
         # one more pass in which every sampled step group starts after a 1 GiB
-        # read-modify-write of another buffer (outside the timed group), so
-        # neither the L2 nor the 256 MB Infinity Cache holds the cache's rows
+        # read of another buffer (outside the timed group), so neither the L2
+        # nor the 256 MB Infinity Cache holds the cache's rows; a read leaves
+        # no dirty lines whose write-back would compete with the timed launch
         fl = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
         cold_samples = []
         for l in range(w.layers):
             x = inputs[l]
@@ -476,7 +478,7 @@ def run_gpu(w, steps: int, warmup: int, sample_every: int, calib_mib: int = 0, c
         for s in range(w.steps):
             sample = s % sample_every == 0
             if sample:
-                fl.mul_(1.0)
+                torch.sum(fl, dim=None, out=sink)
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)

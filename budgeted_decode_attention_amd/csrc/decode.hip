@@ -51,6 +51,14 @@ namespace {
 
 constexpr int kNT = 256;
 constexpr int kUnroll = KVE_DECODE_UNROLL;
+// Caches of at most kSmallCache slots load kUnrollSmall rows per thread at a
+// time (4 x 16 rows of 16-bit elements per round trip: a 102-slot unit in
+// two), still within the register budget of 8 waves per SIMD.
+#ifndef KVE_DECODE_SMALL_CACHE
+#define KVE_DECODE_SMALL_CACHE 256
+#endif
+constexpr int kSmallCache = KVE_DECODE_SMALL_CACHE;
+constexpr int kUnrollSmall = 4;
 
 #ifndef KVE_DECODE_WAVES_PER_EU_Q4
 #define KVE_DECODE_WAVES_PER_EU_Q4 8
@@ -103,20 +111,20 @@ template <int DT, int D, bool Q4> struct Lay {
 
 // Logits scale * q.k_r for rows [r0, r1) into lg[r - r0] (LDS) and, when
 // lgg is non-null, lgg[r] (global).  qf holds this lane's q elements.
-template <int DT, int D>
+template <int DT, int D, int UNR = kUnroll>
 __device__ inline void row_logits(const char* Kb, const float* qf, float scale, int r0, int r1, float* lg,
                                   float* lgg) {
   using R = Rows<DT, D>;
   const int col = threadIdx.x % R::LPR, rg = threadIdx.x / R::LPR;
-  for (int b = r0; b < r1; b += R::RPI * kUnroll) {
-    uint4 raw[kUnroll];
+  for (int b = r0; b < r1; b += R::RPI * UNR) {
+    uint4 raw[UNR];
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
+    for (int i = 0; i < UNR; ++i) {
       const int r = b + i * R::RPI + rg;
       raw[i] = r < r1 ? ld_kv(Kb + ((size_t)r * D + col * R::EPL) * R::ES) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
+    for (int i = 0; i < UNR; ++i) {
       const int r = b + i * R::RPI + rg;
       float f[R::EPL];
       St<DT>::unpack(raw[i], f);
@@ -133,19 +141,19 @@ __device__ inline void row_logits(const char* Kb, const float* qf, float scale, 
 }
 
 // acc (this lane's EPL columns) += sum over rows [r0, r1) of w[r - r0] * v_r.
-template <int DT, int D>
+template <int DT, int D, int UNR = kUnroll>
 __device__ inline void row_values(const char* Vb, const float* w, int r0, int r1, float* acc) {
   using R = Rows<DT, D>;
   const int col = threadIdx.x % R::LPR, rg = threadIdx.x / R::LPR;
-  for (int b = r0; b < r1; b += R::RPI * kUnroll) {
-    uint4 raw[kUnroll];
+  for (int b = r0; b < r1; b += R::RPI * UNR) {
+    uint4 raw[UNR];
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
+    for (int i = 0; i < UNR; ++i) {
       const int r = b + i * R::RPI + rg;
       raw[i] = r < r1 ? ld_kv(Vb + ((size_t)r * D + col * R::EPL) * R::ES) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < kUnroll; ++i) {
+    for (int i = 0; i < UNR; ++i) {
       const int r = b + i * R::RPI + rg;
       const float wr = r < r1 ? w[r - r0] : 0.f;
       float f[R::EPL];
@@ -514,7 +522,7 @@ __host__ __device__ constexpr size_t fused_wts_bytes(int cap) { return ((size_t)
 // replacement in the same workgroup (token t takes the farthest key's slot,
 // or is appended), so a step is one launch and the passes below read token t
 // from its slot like every kept token.
-template <int DT, int D, bool Q4>
+template <int DT, int D, bool Q4, int UNR = kUnroll>
 __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, DecodeIO io) {
   using R = Rows<DT, D>;
   using Y = Lay<DT, D, Q4>;
@@ -552,7 +560,7 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
     for (int j = 0; j < Y::EPL; ++j) qsum += qf[j];
     row_logits_q4<D>(Kb, c.Ksc + slot0 * Q4Rows<D>::G, qf, qsum, sh.scale, 0, n, wts, nullptr);
   } else {
-    row_logits<DT, D>(Kb, qf, sh.scale, 0, n, wts, nullptr);
+    row_logits<DT, D, UNR>(Kb, qf, sh.scale, 0, n, wts, nullptr);
   }
   if (with_new && rg == 0) {
     const float s = group0_dot<DT, D, Y::EPL>(qf, io.k, u) * sh.scale;
@@ -589,7 +597,7 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
 #pragma unroll
     for (int j = 0; j < Y::EPL; ++j) acc[j] = fmaf(-8.f, off, acc[j]);
   } else {
-    row_values<DT, D>(Vb, wts, 0, n, acc);
+    row_values<DT, D, UNR>(Vb, wts, 0, n, acc);
   }
   if (with_new && rg == 0) {
     const float w = wts[n];
@@ -780,6 +788,14 @@ hipError_t launch_f(const Shape& sh, const LayerCache& c, const DecodeIO& io, co
   if (!sp) {
     size_t lds = fused_wts_bytes(c.cap);
     if (c.sk) lds += c.sk_bits == 64 ? hash_replace_lds<D, 64>() : hash_replace_lds<D, 32>();
+    // small caches: a unit's rows in fewer dependent round trips
+    if (!Q4 && c.cap <= kSmallCache) {
+      hipError_t e = set_lds((const void*)decode_fused_kernel<DT, D, Q4, kUnrollSmall>, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((decode_fused_kernel<DT, D, Q4, kUnrollSmall>), dim3(sh.units()), dim3(kNT), lds, st, sh,
+                         c, io);
+      return hipGetLastError();
+    }
     hipError_t e = set_lds((const void*)decode_fused_kernel<DT, D, Q4>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_fused_kernel<DT, D, Q4>), dim3(sh.units()), dim3(kNT), lds, st, sh, c, io);
