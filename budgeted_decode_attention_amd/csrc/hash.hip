@@ -60,6 +60,41 @@ __global__ __launch_bounds__(kNT) void sketch_rows_kernel(Shape sh, UnitList ul,
   }
 }
 
+// Copies the kept prompt rows (positions spos[0, n0)) into the unit's slots,
+// quantised with 4-bit slots.  All threads of the workgroup.
+template <int DT, int D>
+__device__ inline void replay_gather(const LayerCache& c, int u, int P, int n0, const int32_t* spos,
+                                     const void* k, const void* v) {
+  constexpr int EPL = St<DT>::EPL;
+  constexpr int ES = elem_bytes<DT>();
+  constexpr int LPR = D / EPL;
+  constexpr int RPI = kNT / LPR;
+  const int tid = threadIdx.x;
+  const size_t slot0 = (size_t)u * c.cap;
+  const size_t src0 = (size_t)u * P * D * ES;
+  if (c.q4) {
+    constexpr int G = D / kQGroup;
+    char* Kq = (char*)c.K + slot0 * (D / 2);
+    char* Vq = (char*)c.V + slot0 * (D / 2);
+    const int g = tid % G;
+    for (int s = tid / G; s < n0; s += kNT / G) {
+      const size_t so = src0 + (size_t)spos[s] * D * ES;
+      q4_store_group<DT, D>((const char*)k + so, Kq + (size_t)s * (D / 2), c.Ksc + (slot0 + s) * G, g);
+      q4_store_group<DT, D>((const char*)v + so, Vq + (size_t)s * (D / 2), c.Vsc + (slot0 + s) * G, g);
+    }
+    return;
+  }
+  char* Kd = (char*)c.K + slot0 * D * ES;
+  char* Vd = (char*)c.V + slot0 * D * ES;
+  const int col = tid % LPR;
+  for (int s = tid / LPR; s < n0; s += RPI) {
+    const size_t so = ((size_t)spos[s] * D + col * EPL) * ES;
+    const size_t dof = ((size_t)s * D + col * EPL) * ES;
+    st16(Kd + dof, ld16((const char*)k + src0 + so));
+    st16(Vd + dof, ld16((const char*)v + src0 + so));
+  }
+}
+
 // Prompt replay for one HASH unit per workgroup; slot state in LDS.
 template <int DT, int D, int BITS>
 __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c, UnitList ul, int P,
@@ -67,10 +102,6 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
                                                           const typename SkWord<BITS>::T* ksk,
                                                           const void* k, const void* v) {
   using SW = typename SkWord<BITS>::T;
-  constexpr int EPL = St<DT>::EPL;
-  constexpr int ES = elem_bytes<DT>();
-  constexpr int LPR = D / EPL;
-  constexpr int RPI = kNT / LPR;
   extern __shared__ __attribute__((aligned(16))) char lds[];   // sk[B] then pos[B]
   __shared__ uint64_t kscr[2][kNT / kWave];
   const int u = ul.ids[blockIdx.x];
@@ -142,29 +173,117 @@ __global__ __launch_bounds__(kNT) void hash_replay_kernel(Shape sh, LayerCache c
     c.S[slot0 + s] = 0.0;
   }
   if (tid == 0) c.count[u] = n0;
-  // gather
-  const size_t src0 = (size_t)u * P * D * ES;
-  if (c.q4) {
-    constexpr int G = D / kQGroup;
-    char* Kq = (char*)c.K + slot0 * (D / 2);
-    char* Vq = (char*)c.V + slot0 * (D / 2);
-    const int g = tid % G;
-    for (int s = tid / G; s < n0; s += kNT / G) {
-      const size_t so = src0 + (size_t)spos[s] * D * ES;
-      q4_store_group<DT, D>((const char*)k + so, Kq + (size_t)s * (D / 2), c.Ksc + (slot0 + s) * G, g);
-      q4_store_group<DT, D>((const char*)v + so, Vq + (size_t)s * (D / 2), c.Vsc + (slot0 + s) * G, g);
+  replay_gather<DT, D>(c, u, P, n0, spos, k, v);
+}
+
+// Lane d's value of x, as a wave-uniform value.
+__device__ inline uint32_t lane_read(uint32_t x, int d) { return (uint32_t)__builtin_amdgcn_readlane((int)x, d); }
+__device__ inline uint64_t lane_read(uint64_t x, int d) {
+  return ((uint64_t)lane_read((uint32_t)(x >> 32), d) << 32) | lane_read((uint32_t)x, d);
+}
+
+// Prompt replay with every slot's state in registers, for budgets up to
+// JR * kNT slots: thread tid owns slots j * kNT + tid (j < JR), keeping each
+// one's sketch and its eviction key's low part, ((65535 - position) << 7) | j,
+// so a decision costs four vector operations per slot (xor, population count,
+// shift-or, signed maximum) and no LDS traffic.  Slots at or past the budget
+// carry a low part with the sign bit set, so their keys are negative and never
+// win: the scan needs no masks.  The workgroup's maximum key names the
+// winner's position and j; the winning lane's thread index travels with it,
+// and the owner rewrites its registers j.  Positions below 65,536 are
+// distinct, so the maximum is unique.
+template <int DT, int D, int BITS, int JR>
+__global__ __launch_bounds__(kNT) void hash_replay_reg_kernel(Shape sh, LayerCache c, UnitList ul, int P,
+                                                              const typename SkWord<BITS>::T* qsk,
+                                                              const typename SkWord<BITS>::T* ksk,
+                                                              const void* k, const void* v) {
+  using SW = typename SkWord<BITS>::T;
+  static_assert(JR <= 128, "j takes 7 bits of the key");
+  constexpr uint32_t kDead = 0x80000000u;
+  extern __shared__ __attribute__((aligned(16))) char lds[];   // pos[B] for the gather
+  __shared__ uint64_t kscr[2][kNT / kWave];
+  const int u = ul.ids[blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int B = c.meta[u].heavy;
+  const int n0 = min(P, B);
+  const SW* kq = ksk + (size_t)u * P;
+  const SW* qq = qsk + (size_t)u * P;
+  SW sk[JR];
+  uint32_t lo[JR];
+#pragma unroll
+  for (int j = 0; j < JR; ++j) {
+    const int s = j * kNT + tid;
+    sk[j] = s < n0 ? kq[s] : (SW)0;
+    lo[j] = s < B ? ((uint32_t)(0xFFFF - s) << 7) | (uint32_t)j : kDead;
+  }
+  // the decisions' query and key sketches come in windows of 64, lane l of
+  // every wave holding decision w0 + l's, in two register pairs used in turn:
+  // each window is loaded while the one before it is decided, and a decision
+  // reads its own with two lane reads
+  const int nd = P - B;                         // decisions (none if P <= B)
+  auto window = [&](const SW* x, int w0) -> SW { return x[min(B + w0 + lane, P - 1)]; };
+  auto decide = [&](SW qw, SW kw, int w0) {
+    const int m = min(kWave, nd - w0);
+    for (int d = 0; d < m; ++d) {
+      const int i = B + w0 + d;
+      const SW qs = lane_read(qw, d), ks = lane_read(kw, d);
+      int best = INT32_MIN;
+#pragma unroll
+      for (int j = 0; j < JR; ++j)
+        best = max(best, (int)(((uint32_t)popcnt(qs ^ sk[j]) << 23) | lo[j]));
+      const uint32_t kb = (uint32_t)max(best, 0);   // a thread with no slot offers 0
+      const uint32_t wm = wave_max_key(kb);
+      const int wl = __builtin_ctzll(__ballot(kb == wm));
+      if (lane == 0) kscr[i & 1][tid / kWave] = ((uint64_t)wm << 32) | (uint32_t)(tid + wl);
+      __syncthreads();
+      uint64_t bb = kscr[i & 1][0];
+#pragma unroll
+      for (int w = 1; w < kNT / kWave; ++w) bb = kscr[i & 1][w] > bb ? kscr[i & 1][w] : bb;
+      const int owner = __builtin_amdgcn_readfirstlane((int)(bb & 0xFFFFFFFFu));
+      const int jw = __builtin_amdgcn_readfirstlane((int)((bb >> 32) & 0x7F));
+      if (tid == owner) {                         // jw is uniform: an indexed register write
+        sk[jw] = ks;
+        lo[jw] = ((uint32_t)(0xFFFF - i) << 7) | (uint32_t)jw;
+      }
     }
-    return;
+  };
+  if (nd > 0) {
+    SW qa = window(qq, 0), ka = window(kq, 0);
+    SW qb = window(qq, kWave), kb = window(kq, kWave);
+    for (int w0 = 0;; w0 += 2 * kWave) {
+      decide(qa, ka, w0);
+      if (w0 + kWave >= nd) break;
+      qa = window(qq, w0 + 2 * kWave);
+      ka = window(kq, w0 + 2 * kWave);
+      decide(qb, kb, w0 + kWave);
+      if (w0 + 2 * kWave >= nd) break;
+      qb = window(qq, w0 + 3 * kWave);
+      kb = window(kq, w0 + 3 * kWave);
+    }
   }
-  char* Kd = (char*)c.K + slot0 * D * ES;
-  char* Vd = (char*)c.V + slot0 * D * ES;
-  const int col = tid % LPR;
-  for (int s = tid / LPR; s < n0; s += RPI) {
-    const size_t so = ((size_t)spos[s] * D + col * EPL) * ES;
-    const size_t dof = ((size_t)s * D + col * EPL) * ES;
-    st16(Kd + dof, ld16((const char*)k + src0 + so));
-    st16(Vd + dof, ld16((const char*)v + src0 + so));
+  int32_t* spos = reinterpret_cast<int32_t*>(lds);
+  const size_t slot0 = (size_t)u * c.cap;
+#pragma unroll
+  for (int j = 0; j < JR; ++j) {
+    const int s = j * kNT + tid;
+    if (s < B) {
+      const bool full = s < n0;
+      const int p = 0xFFFF - (int)(lo[j] >> 7);
+      if (full) spos[s] = p;
+      c.pos[slot0 + s] = full ? p : -1;
+      reinterpret_cast<SW*>(c.sk)[slot0 + s] = full ? sk[j] : (SW)0;
+      c.S[slot0 + s] = 0.0;
+    }
   }
+  for (int s = B + tid; s < c.cap; s += kNT) {
+    c.pos[slot0 + s] = -1;
+    reinterpret_cast<SW*>(c.sk)[slot0 + s] = 0;
+    c.S[slot0 + s] = 0.0;
+  }
+  if (tid == 0) c.count[u] = n0;
+  __syncthreads();                              // spos complete
+  replay_gather<DT, D>(c, u, P, n0, spos, k, v);
 }
 
 // Decode-time replacement for one HASH unit per workgroup (layers that take
@@ -213,6 +332,12 @@ hipError_t replay_t(const Shape& sh, const LayerCache& c, UnitList ul, int P, co
                     const void* k, const void* v, int B, hipStream_t st) {
   using SW = typename SkWord<BITS>::T;
   if (ul.n <= 0) return hipSuccess;
+  if (B <= 16 * kNT) {
+    auto fn = B <= 4 * kNT ? hash_replay_reg_kernel<DT, D, BITS, 4> : hash_replay_reg_kernel<DT, D, BITS, 16>;
+    hipLaunchKernelGGL(fn, dim3(ul.n), dim3(kNT), (size_t)B * 4, st, sh, c, ul, P,
+                       reinterpret_cast<const SW*>(qsk), reinterpret_cast<const SW*>(ksk), k, v);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)B * (sizeof(SW) + 4);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)hash_replay_kernel<DT, D, BITS>,
