@@ -60,6 +60,172 @@ __global__ __launch_bounds__(kNT) void sketch_rows_kernel(Shape sh, UnitList ul,
   }
 }
 
+// ---------------------------------------------------------------- matrix-core sketches (bf16 rows)
+//
+// For bf16 rows the projections run on the matrix cores: v_mfma_f32_16x16x32_bf16
+// with A = 16 rows x 32 features and B = 32 features x 16 sketch bits gives
+// every (row, bit) sum s in float32, and a second product of |rows| and |W|
+// gives a = sum |x_i w_ib|.  Products of two bf16 values are exact in float32;
+// the accumulation of D of them errs by at most gamma_D = D u / (1 - D u)
+// times a with u = 2^-23 (one unit in the last place per addition: this also
+// covers truncating or multi-operand adders), plus an absolute D 2^-126
+// (max|W| + 2) for products, inputs and partial sums flushed below the
+// float32 normal range.  The sign of s is the exact sign when |s| exceeds
+// twice that relative bound times a plus twice the absolute one; every other
+// (row, bit) -- tiny or cancelling sums, non-finite or overflowing rows -- is
+// settled as before (float64 with its own bound, then the exact expansion).
+
+typedef __bf16 sk_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float sk_f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaTiles = 4;                                 // 16-row tiles per wave and pass
+constexpr int kMfmaPasses = 2;                                // passes per workgroup
+constexpr int kMfmaRows = kNT / kWave * kMfmaTiles * 16 * kMfmaPasses;   // 512 rows per workgroup
+
+__device__ inline sk_f32x4 mfma_bf16(const uint4& a, const uint4& b, sk_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sk_bf16x8, a), __builtin_bit_cast(sk_bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+__device__ inline uint4 abs_bf16x8(uint4 v) {
+  return make_uint4(v.x & 0x7fff7fffu, v.y & 0x7fff7fffu, v.z & 0x7fff7fffu, v.w & 0x7fff7fffu);
+}
+
+// Relative threshold factor 2 gamma_D / (1 - gamma_D) with u = 2^-23, rounded up.
+template <int D> __host__ __device__ constexpr float mfma_sign_threshold() {
+  constexpr double u = 1.0 / 8388608.0;
+  constexpr double g = D * u / (1.0 - D * u);
+  return (float)(2.0 * g / (1.0 - g) * 1.0001);
+}
+
+// Sketches of rows [row0, row0 + nrows) of each listed unit from bf16 rows.
+// Wave w of a workgroup takes kMfmaTiles tiles of 16 consecutive rows per
+// pass; lane l supplies row l % 16 of a tile and features 8 (l / 16) + 0..7
+// of each 32-feature step, and receives rows 4 (l / 16) + 0..3, bit l % 16
+// of each 16-bit block of the sketch.
+template <int D, int BITS>
+__global__ __launch_bounds__(kNT) void sketch_rows_mfma_kernel(UnitList ul, const void* x, int P, int row0,
+                                                               int nrows, const uint16_t* proj,
+                                                               typename SkWord<BITS>::T* out) {
+  using SW = typename SkWord<BITS>::T;
+  constexpr int NB = BITS / 16;                              // 16-bit blocks of a sketch
+  constexpr int KS = D / 32;                                 // 32-feature steps
+  static_assert(NB * 4 <= 32, "one flag bit per (block, row) of a lane");
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[D * BITS];
+  __shared__ double ebuf[kNT / kWave][D + 1];                // the exact fallback, per wave
+  __shared__ float wred[kNT / kWave];
+  const int u = ul.ids ? ul.ids[blockIdx.y] : blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int g = lane >> 4, c16 = lane & 15;
+  const char* base = (const char*)x + ((size_t)u * P + row0) * D * 2;
+
+  stage_proj<D, BITS>(Ws, proj);
+  __syncthreads();
+  float wm = 0.f;
+  for (int i = tid; i < D * BITS; i += kNT) wm = fmaxf(wm, fabsf(__uint_as_float((uint32_t)Ws[i] << 16)));
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
+  if (lane == 0) wred[wv] = wm;
+  // B fragments: lane (g, c16) holds W[32 kk + 8 g + 0..7][16 nb + c16]
+  uint4 wf[KS][NB], wa[KS][NB];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      uint32_t h[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int i0 = kk * 32 + 8 * g + 2 * t;
+        h[t] = (uint32_t)Ws[i0 * BITS + nb * 16 + c16] | ((uint32_t)Ws[(i0 + 1) * BITS + nb * 16 + c16] << 16);
+      }
+      wf[kk][nb] = make_uint4(h[0], h[1], h[2], h[3]);
+      wa[kk][nb] = abs_bf16x8(wf[kk][nb]);
+    }
+  __syncthreads();
+  float wmax = wred[0];
+#pragma unroll
+  for (int i = 1; i < kNT / kWave; ++i) wmax = fmaxf(wmax, wred[i]);
+  const float thr = mfma_sign_threshold<D>();
+  const float tau = 2.f * (float)D * 0x1p-126f * (wmax + 2.f);   // inf (everything falls back) if W is huge
+
+  for (int pass = 0; pass < kMfmaPasses; ++pass) {
+    const int rw = blockIdx.x * kMfmaRows + (pass * (kNT / kWave) + wv) * (kMfmaTiles * 16);
+    // rows at or past nrows read as zero (range-checked buffer loads)
+    const uint32_t bytes = rw < nrows ? (uint32_t)(nrows - rw) * D * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base) + (size_t)rw * D * 2, (short)0, (int)bytes,
+                                          0x00020000);
+    uint4 xt[kMfmaTiles][KS];
+#pragma unroll
+    for (int t = 0; t < kMfmaTiles; ++t)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        xt[t][kk] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (t * 16 + c16) * D * 2 + kk * 64 + g * 16, 0, 0));
+#pragma unroll
+    for (int t = 0; t < kMfmaTiles; ++t) {
+      const int rt = rw + t * 16;                            // the tile's first row
+      if (rt >= nrows) break;                                // uniform
+      sk_f32x4 sv[NB], av[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        sv[nb] = sk_f32x4{0.f, 0.f, 0.f, 0.f};
+        av[nb] = sk_f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint4 xa = abs_bf16x8(xt[t][kk]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          sv[nb] = mfma_bf16(xt[t][kk], wf[kk][nb], sv[nb]);
+          av[nb] = mfma_bf16(xa, wa[kk][nb], av[nb]);
+        }
+      }
+      // flag bit nb * 4 + r: row rt + 4 g + r, sketch bit 16 nb + c16
+      uint32_t bitm = 0, ambm = 0;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float s = sv[nb][r], a = av[nb][r];
+          if (s > 0.f) bitm |= 1u << (nb * 4 + r);
+          if (rt + 4 * g + r < nrows && !(fabsf(s) > fmaf(thr, a, tau))) ambm |= 1u << (nb * 4 + r);
+        }
+      if (__ballot(ambm != 0)) {                             // rare: float64, then exact
+#pragma unroll
+        for (int f = 0; f < NB * 4; ++f) {
+          const bool mine = (ambm >> f) & 1u;
+          if (!__ballot(mine)) continue;
+          const int r = f & 3, b = (f >> 2) * 16 + c16;
+          const char* row = base + (size_t)(rt + 4 * g + r) * D * 2;
+          int v = mine ? sketch_bit_fast<D>([&](int i) { return load_elem<BF16>(row, i); }, Ws, BITS, b) : 0;
+          uint64_t fr = __ballot(v < 0);
+          while (fr) {                                       // uniform over the wave
+            if (lane == __builtin_ctzll(fr)) v = exact_sign<BF16, D>(row, proj, BITS, b, ebuf[wv]);
+            fr &= fr - 1;
+          }
+          if (mine) bitm = (bitm & ~(1u << f)) | ((uint32_t)v << f);
+        }
+      }
+      uint64_t m[NB][4];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m[nb][r] = __ballot((bitm >> (nb * 4 + r)) & 1u);
+      // lane L < 16 assembles row rt + L = rt + 4 (L / 4) + (L % 4)
+      if (lane < 16 && rt + lane < nrows) {
+        const int gg = lane >> 2, rr = lane & 3;
+        SW word = 0;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint64_t mm = rr == 0 ? m[nb][0] : rr == 1 ? m[nb][1] : rr == 2 ? m[nb][2] : m[nb][3];
+          word |= (SW)((mm >> (16 * gg)) & 0xFFFFu) << (16 * nb);
+        }
+        out[(size_t)u * P + row0 + rt + lane] = word;
+      }
+    }
+  }
+}
+
 // Copies the kept prompt rows (positions spos[0, n0)) into the unit's slots,
 // quantised with 4-bit slots.  All threads of the workgroup.
 template <int DT, int D>
@@ -321,6 +487,12 @@ template <int DT, int D, int BITS>
 hipError_t sketch_t(const Shape& sh, UnitList ul, const void* x, int P, int row0, int nrows,
                     const uint16_t* proj, void* out, hipStream_t st) {
   if (nrows <= 0 || ul.n <= 0) return hipSuccess;
+  if constexpr (DT == BF16) {
+    dim3 grid((nrows + kMfmaRows - 1) / kMfmaRows, ul.n);
+    hipLaunchKernelGGL((sketch_rows_mfma_kernel<D, BITS>), grid, dim3(kNT), 0, st, ul, x, P, row0, nrows, proj,
+                       reinterpret_cast<typename SkWord<BITS>::T*>(out));
+    return hipGetLastError();
+  }
   dim3 grid((nrows + kSketchRows - 1) / kSketchRows, ul.n);
   hipLaunchKernelGGL((sketch_rows_kernel<DT, D, BITS>), grid, dim3(kNT), 0, st, sh, ul, x, P, row0, nrows, proj,
                      reinterpret_cast<typename SkWord<BITS>::T*>(out));

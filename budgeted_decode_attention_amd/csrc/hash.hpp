@@ -52,13 +52,14 @@ __device__ inline int exact_sign(const char* row, const uint16_t* W, int bits, i
 template <int D> __host__ __device__ constexpr size_t exact_lds() { return (size_t)(D + 1) * 8; }
 
 // Sign bit b of a row: float64 dot with the error bound; -1 if the bound does
-// not settle the sign.  xs: the row as floats, Ws: the projection as bf16 bits.
-template <int D>
-__device__ inline int sketch_bit_fast(const float* xs, const uint16_t* Ws, int bits, int b) {
+// not settle the sign.  xs(i): element i of the row as a float (from LDS or
+// global memory), Ws: the projection as bf16 bits.
+template <int D, typename X>
+__device__ inline int sketch_bit_fast(X xs, const uint16_t* Ws, int bits, int b) {
   double s = 0.0, a = 0.0;
 #pragma unroll 8
   for (int i = 0; i < D; ++i) {
-    const double x = (double)xs[i];
+    const double x = (double)xs(i);
     const double w = bf16_to_double(Ws[i * bits + b]);
     s = fma(x, w, s);
     a = fma(fabs(x), fabs(w), a);
@@ -80,7 +81,7 @@ __device__ inline int sketch_bit_fast(const float* xs, const uint16_t* Ws, int b
 template <int DT, int D>
 __device__ inline int sketch_bit(bool active, const float* xs, const uint16_t* Ws, const char* row,
                                  const uint16_t* W, int bits, int b, double* ebuf) {
-  int bit = active ? sketch_bit_fast<D>(xs, Ws, bits, b) : 0;
+  int bit = active ? sketch_bit_fast<D>([&](int i) { return xs[i]; }, Ws, bits, b) : 0;
   uint64_t fr = __ballot(bit < 0);
   const int lane = threadIdx.x & (kWave - 1);
   while (fr) {                                   // uniform over the wave

@@ -90,3 +90,45 @@ def test_cancelling_projections_take_the_exact_sign(bits):
         assert np.array_equal(g0, np.sort(tr.prefill_kept)), h
         assert np.array_equal(r.evicted[:, 0, h], tr.evicted), h
         assert np.array_equal(g1, tr.final_kept), h
+
+
+def scaled_inputs(seed, bits):
+    """Prompt and step rows of both heads scaled by 2^e, e drawn from
+    {-133, -126, -120, -100, 100, 110, 124}: bf16 subnormals, sums of
+    magnitudes that overflow float32 (e = 124: 128 products near 2^124), and
+    everything between.  The sign of a projection does not depend on the scale, so the
+    exact sketches -- and the replay's decisions -- stay well defined."""
+    w = dataclasses.replace(configs.scaled("hashevict_lsh", batch=1, heads=2, prompt=P, steps=T), sketch_bits=bits)
+    inp = generate_layer(w, 0, "cpu", seed)
+    rng = np.random.default_rng(seed + 100)
+    exps = np.array([-133, -126, -120, -100, 100, 110, 124])
+    for h in range(2):
+        for tensor_p, tensor_d in ((inp.prompt_k, inp.dec_k), (inp.prompt_q, inp.dec_q)):
+            for p in rng.choice(P + T, 60, replace=False):
+                f = float(2.0 ** int(rng.choice(exps)))
+                if p < P:
+                    tensor_p[0, h, p] = (tensor_p[0, h, p].float() * f).to(torch.bfloat16)
+                else:
+                    tensor_d[p - P, 0, h] = (tensor_d[p - P, 0, h].float() * f).to(torch.bfloat16)
+    return w, inp
+
+
+@pytest.mark.parametrize("bits", [16, 32, 64])
+def test_extreme_row_scales_take_the_exact_sign(bits):
+    """bf16 rows are sketched on the matrix cores, in float32; rows whose
+    sums overflow or underflow float32 must fall back to the exact sign."""
+    w, inp = scaled_inputs(seed=7, bits=bits)
+    Wp = inp.proj.float().double().numpy()
+    assert inp.prompt_k.dtype == torch.bfloat16
+    kv = harness.make_cache(w, inp, policy=[4, 4], heavy=[BUDGET, BUDGET], recent=[0, 0])
+    r = harness.run_layer(kv, inp.to("cuda"))
+    kv.close()
+    for h in range(2):
+        Q, K, V = unit_sequence(inp, 0, h)
+        assert np.isfinite(K).all() and np.isfinite(Q).all()
+        tr = hashevict.run_unit(Q, K, V, Wp, P, BUDGET, 1 / np.sqrt(128), steps=T)
+        g0 = np.sort(r.prefill_pos[0, h, :int(r.prefill_cnt[0, h])])
+        g1 = np.sort(r.final_pos[0, h, :int(r.final_cnt[0, h])])
+        assert np.array_equal(g0, np.sort(tr.prefill_kept)), h
+        assert np.array_equal(r.evicted[:, 0, h], tr.evicted), h
+        assert np.array_equal(g1, tr.final_kept), h
