@@ -140,27 +140,48 @@ __device__ inline void row_logits(const char* Kb, const float* qf, float scale, 
   }
 }
 
-// acc (this lane's EPL columns) += sum over rows [r0, r1) of w[r - r0] * v_r.
-template <int DT, int D, int UNR = kUnroll>
-__device__ inline void row_values(const char* Vb, const float* w, int r0, int r1, float* acc) {
+// One tile of value rows b + i RPI + rg (i < UNR), zero past r1.
+template <int DT, int D, int UNR>
+__device__ inline void value_tile_load(const char* Vb, int b, int r1, uint4 (&raw)[UNR]) {
   using R = Rows<DT, D>;
   const int col = threadIdx.x % R::LPR, rg = threadIdx.x / R::LPR;
-  for (int b = r0; b < r1; b += R::RPI * UNR) {
+#pragma unroll
+  for (int i = 0; i < UNR; ++i) {
+    const int r = b + i * R::RPI + rg;
+    raw[i] = r < r1 ? ld_kv(Vb + ((size_t)r * D + col * R::EPL) * R::ES) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int DT, int D, int UNR>
+__device__ inline void value_tile_fma(const uint4 (&raw)[UNR], const float* w, int b, int r0, int r1, float* acc) {
+  using R = Rows<DT, D>;
+  const int rg = threadIdx.x / R::LPR;
+#pragma unroll
+  for (int i = 0; i < UNR; ++i) {
+    const int r = b + i * R::RPI + rg;
+    const float wr = r < r1 ? w[r - r0] : 0.f;
+    float f[R::EPL];
+    St<DT>::unpack(raw[i], f);
+#pragma unroll
+    for (int j = 0; j < R::EPL; ++j) acc[j] = fmaf(wr, f[j], acc[j]);
+  }
+}
+
+// acc (this lane's EPL columns) += sum over rows [r0, r1) of w[r - r0] * v_r.
+// With `first`, the tile of rows from r0 is already in registers.
+template <int DT, int D, int UNR = kUnroll>
+__device__ inline void row_values(const char* Vb, const float* w, int r0, int r1, float* acc,
+                                  const uint4 (*first)[UNR] = nullptr) {
+  using R = Rows<DT, D>;
+  int b = r0;
+  if (first && b < r1) {
+    value_tile_fma<DT, D, UNR>(*first, w, b, r0, r1, acc);
+    b += R::RPI * UNR;
+  }
+  for (; b < r1; b += R::RPI * UNR) {
     uint4 raw[UNR];
-#pragma unroll
-    for (int i = 0; i < UNR; ++i) {
-      const int r = b + i * R::RPI + rg;
-      raw[i] = r < r1 ? ld_kv(Vb + ((size_t)r * D + col * R::EPL) * R::ES) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < UNR; ++i) {
-      const int r = b + i * R::RPI + rg;
-      const float wr = r < r1 ? w[r - r0] : 0.f;
-      float f[R::EPL];
-      St<DT>::unpack(raw[i], f);
-#pragma unroll
-      for (int j = 0; j < R::EPL; ++j) acc[j] = fmaf(wr, f[j], acc[j]);
-    }
+    value_tile_load<DT, D, UNR>(Vb, b, r1, raw);
+    value_tile_fma<DT, D, UNR>(raw, w, b, r0, r1, acc);
   }
 }
 
@@ -566,10 +587,16 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
     const float s = group0_dot<DT, D, Y::EPL>(qf, io.k, u) * sh.scale;
     if (col == 0) wts[n] = s;
   }
-  // 4-bit rows: the value pass's first tile loads while the softmax runs
+  // 4-bit rows and small caches: the value pass's first tile loads while
+  // the softmax runs (a small cache's unit streams in one or two tiles, so
+  // this takes a whole round trip off its chain)
+  constexpr bool kVFirst = !Q4 && UNR == kUnrollSmall;
   Q4Tile vfirst;
+  uint4 vraw[UNR];
   if constexpr (Q4) {
     q4_load<D>(Vb, c.Vsc + slot0 * Q4Rows<D>::G, 0, max(n - 1, 0), vfirst);
+  } else if constexpr (kVFirst) {
+    value_tile_load<DT, D, UNR>(Vb, 0, n, vraw);
   }
   __syncthreads();
 
@@ -597,7 +624,7 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
 #pragma unroll
     for (int j = 0; j < Y::EPL; ++j) acc[j] = fmaf(-8.f, off, acc[j]);
   } else {
-    row_values<DT, D, UNR>(Vb, wts, 0, n, acc);
+    row_values<DT, D, UNR>(Vb, wts, 0, n, acc, kVFirst ? &vraw : nullptr);
   }
   if (with_new && rg == 0) {
     const float w = wts[n];
