@@ -75,3 +75,18 @@ def test_records_are_read_only_while_their_sources_match(monkeypatch):
     monkeypatch.setattr("builtins.open", changed_sources)
     assert bench.counter_traffic("opt30b_decode_h2o") is None
     assert bench.prefill_counters("opt30b_decode_h2o") is None
+
+
+def test_every_kernel_trace_names_its_sources_and_their_hash():
+    """Each kernel-trace summary carries the sources it was taken with and
+    their hash, so a reader can tell whether it still describes the code."""
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "kernels_*.md")))
+    assert paths
+    for p in paths:
+        text = open(p).read()
+        m = re.search(r"^kernel_sources: (.+)$", text, re.M)
+        assert m, p
+        for f in m.group(1).split():
+            assert os.path.exists(os.path.join(ROOT, f)), (p, f)
+        assert re.search(r"^kernel_sources_sha256: [0-9a-f]{16}$", text, re.M), p
+        assert "rocprofv3 --kernel-trace --stats" in text, p
