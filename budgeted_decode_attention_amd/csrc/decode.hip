@@ -225,24 +225,32 @@ __device__ inline uint2 ld_codes(const void* p) {
 }
 
 // One load tile of 4-bit rows: kUnrollQ4 rows per thread (rows b + i RPI +
-// rg), their 8 code bytes and group scale.  Rows past rlast re-read row rlast
-// (the last row of the range, or row 0 of an empty one), so every load is
-// issued unconditionally and the compiler waits only for the tile being
-// used, not for the one in flight behind it; callers mask those rows.
+// rg), their 8 code bytes and group scale, by raw buffer loads whose range
+// check covers rows [0, rlast]: rows past it read as zero, so every load is
+// issued unconditionally with a 32-bit offset and the compiler waits only
+// for the tile being used, not for the one in flight behind it; callers
+// mask those rows.  Loads carry the non-temporal hint, as the 16-bit rows'.
 struct Q4Tile {
   uint2 raw[kUnrollQ4];
   float sc[kUnrollQ4];
 };
 
+__device__ inline __amdgpu_buffer_rsrc_t q4_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int D>
 __device__ inline void q4_load(const char* Xq, const float* Xs, int b, int rlast, Q4Tile& t) {
   using Q = Q4Rows<D>;
+  constexpr int kNtAux = 2;                     // cache policy: non-temporal
   const int col = threadIdx.x % Q::LPR, rg = threadIdx.x / Q::LPR;
+  const __amdgpu_buffer_rsrc_t rq = q4_rsrc(Xq, (uint32_t)(rlast + 1) * Q::CB);
+  const __amdgpu_buffer_rsrc_t rs = q4_rsrc(Xs, (uint32_t)(rlast + 1) * Q::G * 4);
 #pragma unroll
   for (int i = 0; i < kUnrollQ4; ++i) {
-    const int r = min(b + i * Q::RPI + rg, rlast);
-    t.raw[i] = ld_codes(Xq + (size_t)r * Q::CB + col * 8);
-    t.sc[i] = ld_scale(Xs + (size_t)r * Q::G + col / 2);
+    const int r = b + i * Q::RPI + rg;
+    t.raw[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, r * Q::CB + col * 8, 0, kNtAux));
+    t.sc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (r * Q::G + col / 2) * 4, 0, kNtAux));
   }
 }
 
