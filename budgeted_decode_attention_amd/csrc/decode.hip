@@ -298,7 +298,7 @@ __device__ inline void row_logits_q4(const char* Kq, const float* Ks, const floa
     const int b = r0 + k * STEP;
     q4_load<D>(Kq, Ks, b + STEP, rlast, tb);
     q4_tile_logits<D>(ta, qf, qsum, scale, b, r0, r1, lg, lgg);
-    q4_load<D>(Kq, Ks, b + 2 * STEP, rlast, ta);   // past the range: re-reads row rlast
+    q4_load<D>(Kq, Ks, b + 2 * STEP, rlast, ta);   // past the range: reads as zero
     q4_tile_logits<D>(tb, qf, qsum, scale, b + STEP, r0, r1, lg, lgg);
   }
   if (k < ntile) q4_tile_logits<D>(ta, qf, qsum, scale, r0 + k * STEP, r0, r1, lg, lgg);
@@ -342,7 +342,7 @@ __device__ inline void row_values_q4(const char* Vq, const float* Vs, const floa
     const int b = r0 + k * STEP;
     q4_load<D>(Vq, Vs, b + STEP, rlast, tb);
     q4_tile_values<D>(ta, w, b, r0, r1, acc, off);
-    q4_load<D>(Vq, Vs, b + 2 * STEP, rlast, ta);   // past the range: re-reads row rlast
+    q4_load<D>(Vq, Vs, b + 2 * STEP, rlast, ta);   // past the range: reads as zero
     q4_tile_values<D>(tb, w, b + STEP, r0, r1, acc, off);
   }
   if (k < ntile) q4_tile_values<D>(ta, w, r0 + k * STEP, r0, r1, acc, off);
