@@ -123,6 +123,16 @@ def test_special_without_kept_prompt_tokens(decode_path):
     run_and_check(w, policy=[SPECIAL, FULL, LOCAL, SPECIAL], heavy=[0] * 4, recent=[0, 0, 7, 0])
 
 
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_hash_fp16_fp32_rows(dtype, decode_path):
+    """HashEvict with fp16 and fp32 rows: their sketches take the float64
+    path (bf16 rows take the matrix cores), then the register replay."""
+    w = dataclasses.replace(configs.scaled("hashevict_lsh", batch=1, heads=3, prompt=400, steps=40), dtype=dtype)
+    assert w.hash_budget == 200
+    rep, _ = run_and_check(w)
+    assert rep.decisions == 3 * 40
+
+
 def test_hash_prompt_shorter_than_budget(decode_path):
     w = configs.scaled("hashevict_lsh", batch=1, heads=2, prompt=50, steps=40)
     run_and_check(w, policy=[HASH] * 2, heavy=[70] * 2, recent=[0] * 2)
