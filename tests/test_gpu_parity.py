@@ -275,13 +275,15 @@ def test_hash_sketch_widths(bits, decode_path):
     assert rep.decisions == 6 * 70
 
 
-@pytest.mark.parametrize("budget", [1, 3, 64, 255, 257, 1027])
+@pytest.mark.parametrize("budget", [1, 3, 64, 255, 257, 1024, 1027, 4096, 4097])
 def test_hash_replay_budgets(budget):
     """Prompt replay and decode replacement at budgets that leave whole waves
     of the workgroup without a slot (1, 3, 64), that are not a multiple of the
-    four-slot scan rounds or of the 256 threads (255, 257, 1027): bit-exact
-    decisions against the oracle, every prompt position past the budget
-    replayed."""
+    four-slot scan rounds or of the 256 threads (255, 257, 1027), and at the
+    edges of the register replay's two sizes (1,024 and 4,096 slots: every
+    register group full; 4,097: the replay with slot state in LDS):
+    bit-exact decisions against the oracle, every prompt position past the
+    budget replayed."""
     w = configs.scaled("hashevict_lsh", batch=1, heads=2, prompt=budget + 300, steps=30)
     rep, r = run_and_check(w, policy=[HASH] * 2, heavy=[budget] * 2, recent=[0] * 2)
     assert (r.final_cnt == budget).all()
