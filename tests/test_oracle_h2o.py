@@ -207,3 +207,39 @@ def test_decode_eviction_maximises_retained_score_brute_force():
             winners = [j for j in admissible if retained[j] == best]
             assert A[i] == min(A[j] for j in winners)
             cache = h2o.remove(A, S_A, i)
+
+
+def test_worked_example_with_distinct_keys():
+    """A trajectory worked by hand on distinct keys (H2O review page,
+    proposed method: accumulated attention decides which tokens stay).
+
+    d = 1, scale 1, keys k = (0, 1, 2 | 1, 0), queries e^q = (2, 2, 2 | 27, 2),
+    values v = (1, 2, 3 | 4, 5); prompt P = 3, one heavy and one recent slot.
+    Every weight is a ratio of powers of the query's base, so each number
+    below is an exact fraction:
+
+      prompt rows   [1], [1, 2]/3, [1, 2, 4]/7
+      column sums   c = (31/21, 20/21, 4/7); keep {2} (recent) + {0} (top c)
+      step 3        attends {0, 2, 3}: e = (1, 729, 27)/757, o = 2296/757;
+                    S0 = 31/21 + 1/757 < S2 = 4/7 + 729/757, so 0 goes
+                    (without this step's weights 2 would go: the step adds
+                    its weights before it evicts), token 3 keeps 27/757
+      step 4        attends {2, 3, 4}: e = (4, 2, 1)/7, o = 25/7;
+                    S3 = 27/757 + 2/7 < S2, so 3 goes; S4 = 1/7
+      final         {2, 4} with S = (4/7 + 729/757 + 4/7, 1/7)
+    """
+    ln = np.log
+    K = np.array([[0.0], [1.0], [2.0], [1.0], [0.0]])
+    Q = np.array([[ln(2.0)], [ln(2.0)], [ln(2.0)], [ln(27.0)], [ln(2.0)]])
+    V = np.array([[1.0], [2.0], [3.0], [4.0], [5.0]])
+    tr = h2o.run_unit(Q, K, V, 3, 1, 1, 1.0)
+    F = Fraction
+    close = lambda a, b: np.allclose(np.asarray(a, dtype=float), [float(x) for x in b], rtol=1e-13, atol=0)
+    assert close(tr.column_scores, [F(31, 21), F(20, 21), F(4, 7)])
+    assert list(tr.prefill_kept) == [0, 2]
+    assert close(tr.prefill_scores, [F(31, 21), F(4, 7)])
+    assert close(tr.out[:, 0], [F(2296, 757), F(25, 7)])
+    assert list(tr.evicted) == [0, 3]
+    assert close(tr.evicted_score, [F(31, 21) + F(1, 757), F(27, 757) + F(2, 7)])
+    assert list(tr.final.pos) == [2, 4]
+    assert close(tr.final.S, [F(4, 7) + F(729, 757) + F(4, 7), F(1, 7)])
