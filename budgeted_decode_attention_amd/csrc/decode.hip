@@ -206,24 +206,6 @@ __device__ inline float group0_dot(const float* qf, const void* rows, int u) {
 #endif
 constexpr int kUnrollQ4 = KVE_DECODE_UNROLL_Q4;
 
-__device__ inline float ld_scale(const float* p) {
-#if KVE_DECODE_NT_LOADS
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
-
-__device__ inline uint2 ld_codes(const void* p) {
-#if KVE_DECODE_NT_LOADS
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-  return make_uint2(v.x, v.y);
-#else
-  return *reinterpret_cast<const uint2*>(p);
-#endif
-}
-
 // One load tile of 4-bit rows: kUnrollQ4 rows per thread (rows b + i RPI +
 // rg), their 8 code bytes and group scale, by raw buffer loads whose range
 // check covers rows [0, rlast]: rows past it read as zero, so every load is
@@ -242,7 +224,7 @@ __device__ inline __amdgpu_buffer_rsrc_t q4_rsrc(const void* p, uint32_t bytes) 
 template <int D>
 __device__ inline void q4_load(const char* Xq, const float* Xs, int b, int rlast, Q4Tile& t) {
   using Q = Q4Rows<D>;
-  constexpr int kNtAux = 2;                     // cache policy: non-temporal
+  constexpr int kNtAux = KVE_DECODE_NT_LOADS ? 2 : 0;   // cache policy: non-temporal
   const int col = threadIdx.x % Q::LPR, rg = threadIdx.x / Q::LPR;
   const __amdgpu_buffer_rsrc_t rq = q4_rsrc(Xq, (uint32_t)(rlast + 1) * Q::CB);
   const __amdgpu_buffer_rsrc_t rs = q4_rsrc(Xs, (uint32_t)(rlast + 1) * Q::G * 4);
