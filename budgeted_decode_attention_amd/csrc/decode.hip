@@ -59,6 +59,10 @@ constexpr int kUnroll = KVE_DECODE_UNROLL;
 #endif
 constexpr int kSmallCache = KVE_DECODE_SMALL_CACHE;
 constexpr int kUnrollSmall = 4;
+// Small caches take the policy's decision before the value pass.
+#ifndef KVE_DECODE_DECIDE_EARLY
+#define KVE_DECODE_DECIDE_EARLY 1
+#endif
 
 #ifndef KVE_DECODE_WAVES_PER_EU_Q4
 #define KVE_DECODE_WAVES_PER_EU_Q4 8
@@ -360,17 +364,23 @@ __device__ inline void stash_groups(const float* acc, float* red) {
   for (int j = 0; j < R::EPL; ++j) red[rg * D + col * R::EPL + j] = acc[j];
 }
 
-// The head's policy after attention: H2O score update and victim, the
-// persistence-count update and victim, or the positional rule; writes token
-// t's key/value/score/position into its slot.  wts[r] = exp(l_r - M) for the
-// n kept slots (read for H2O and PERSIST heads only), e_new = exp(l_t - M),
-// L = the sum of every weight, invL = 1 / L.  Control flow is uniform over
-// the workgroup; contains barriers.
+// What a policy step decided: the slot that receives token t (-1: none), the
+// position it evicts (-1: none) and token t's score word.
+struct PolicyDecision {
+  int wslot;
+  int evicted;
+  double s_new;
+};
+
+// The policy's decision for one unit (every thread of the workgroup calls
+// it): the kept slots' scores (or histories) are updated in place and the
+// victim chosen.  It reads the step's weights and the slots' metadata, never
+// their key or value rows, so it may run while the value pass is still to
+// come; policy_write then moves token t into the chosen slot.
 template <int DT, int D, bool Q4, int RND = 4>
-__device__ inline void policy_step(const Shape& sh, const LayerCache& c, const DecodeIO& io, const HeadMeta& m,
-                                   int u, int n, const float* wts, float e_new, double L, double invL,
-                                   MinKey* kscr) {
-  using R = Rows<DT, D>;
+__device__ inline PolicyDecision policy_decide(const Shape& sh, const LayerCache& c, const DecodeIO& io,
+                                               const HeadMeta& m, int u, int n, const float* wts, float e_new,
+                                               double L, double invL, MinKey* kscr) {
   const int tid = threadIdx.x;
   const int t = io.t;
   const size_t slot0 = (size_t)u * c.cap;
@@ -491,6 +501,19 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
     if (id_protected(m.ids, io.sets, io.ids[u / sh.heads])) wslot = n;
     else evicted = t;
   }
+  return PolicyDecision{wslot, evicted, s_new};
+}
+
+// Token t's key and value rows written into the decided slot with its score
+// word, position and the unit's count; the eviction log.  Ends the step.
+template <int DT, int D, bool Q4>
+__device__ inline void policy_write(const Shape& sh, const LayerCache& c, const DecodeIO& io, const HeadMeta& m,
+                                    int u, int n, const PolicyDecision& pd) {
+  using R = Rows<DT, D>;
+  const int tid = threadIdx.x;
+  const int t = io.t;
+  const size_t slot0 = (size_t)u * c.cap;
+  const int wslot = pd.wslot;
   if (wslot >= 0) {
     __syncthreads();                           // every read of the slot is done
     if constexpr (Q4) {
@@ -515,13 +538,27 @@ __device__ inline void policy_step(const Shape& sh, const LayerCache& c, const D
       }
     }
     if (tid == 0) {
-      c.S[slot0 + wslot] = s_new;
+      c.S[slot0 + wslot] = pd.s_new;
       c.pos[slot0 + wslot] = t;
       if (wslot == n) c.count[u] = n + 1;
     }
   }
   // HASH units log their replacement in the pre-attention kernel
-  if (tid == 0 && io.evicted && m.policy != HASH) io.evicted[u] = evicted;
+  if (tid == 0 && io.evicted && m.policy != HASH) io.evicted[u] = pd.evicted;
+}
+
+// The head's policy after attention: H2O score update and victim, the
+// persistence-count update and victim, or the positional rule; writes token
+// t's key/value/score/position into its slot.  wts[r] = exp(l_r - M) for the
+// n kept slots (read for H2O and PERSIST heads only), e_new = exp(l_t - M),
+// L = the sum of every weight, invL = 1 / L.  Control flow is uniform over
+// the workgroup; contains barriers.
+template <int DT, int D, bool Q4, int RND = 4>
+__device__ inline void policy_step(const Shape& sh, const LayerCache& c, const DecodeIO& io, const HeadMeta& m,
+                                   int u, int n, const float* wts, float e_new, double L, double invL,
+                                   MinKey* kscr) {
+  const PolicyDecision pd = policy_decide<DT, D, Q4, RND>(sh, c, io, m, u, n, wts, e_new, L, invL, kscr);
+  policy_write<DT, D, Q4>(sh, c, io, m, u, n, pd);
 }
 
 // ------------------------------------------------------------------ fused
@@ -604,6 +641,17 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
   const double L = block_sum<kNT>(ls, dscr);     // barriers inside: wts[] complete
   const double invL = 1.0 / L;
 
+  // The policy's decision needs only the weights and the slots' metadata.
+  // A small cache takes it here, while its first value tile is still in
+  // flight (at most one slot per thread: one score per round); token t's
+  // rows go into their slot once the output is formed.  Larger caches
+  // decide after the value pass, which measured faster for them.
+  constexpr bool kDecideEarly = kVFirst && KVE_DECODE_DECIDE_EARLY;
+  constexpr int kRnd = kVFirst && kSmallCache <= kNT ? 1 : 4;
+  PolicyDecision pd{-1, -1, 0.0};
+  if constexpr (kDecideEarly)
+    pd = policy_decide<DT, D, Q4, kRnd>(sh, c, io, m, u, n, wts, with_new ? wts[n] : 0.f, L, invL, kscr);
+
   // output o = sum_j w_j v_j / L
   float acc[Y::EPL];
 #pragma unroll
@@ -632,7 +680,9 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
     for (int g = 0; g < Y::NRED; ++g) s += red[g * D + i];
     io.out[(size_t)u * D + i] = (float)((double)s * invL);
   }
-  policy_step<DT, D, Q4>(sh, c, io, m, u, n, wts, with_new ? wts[n] : 0.f, L, invL, kscr);
+  if constexpr (!kDecideEarly)
+    pd = policy_decide<DT, D, Q4, kRnd>(sh, c, io, m, u, n, wts, with_new ? wts[n] : 0.f, L, invL, kscr);
+  policy_write<DT, D, Q4>(sh, c, io, m, u, n, pd);
 }
 
 // ------------------------------------------------------------------ split
