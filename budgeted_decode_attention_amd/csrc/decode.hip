@@ -63,6 +63,13 @@ constexpr int kUnrollSmall = 4;
 #ifndef KVE_DECODE_DECIDE_EARLY
 #define KVE_DECODE_DECIDE_EARLY 1
 #endif
+// Wave priority by phase for small caches: a workgroup starts at the
+// highest and lowers it after the key pass and after the value pass, so waves
+// still streaming keys win issue over those further on (the youngest
+// workgroups on a CU otherwise finish their key pass last).
+#ifndef KVE_DECODE_PRIO
+#define KVE_DECODE_PRIO 1
+#endif
 
 #ifndef KVE_DECODE_WAVES_PER_EU_Q4
 #define KVE_DECODE_WAVES_PER_EU_Q4 8
@@ -580,6 +587,8 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
   __shared__ double dscr[kNT / kWave];
   __shared__ MinKey kscr[kNT / kWave];
 
+  constexpr bool kPrio = KVE_DECODE_PRIO && !Q4 && UNR == kUnrollSmall;
+  if constexpr (kPrio) __builtin_amdgcn_s_setprio(3);
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
   const int col = tid % Y::LPR;
@@ -626,6 +635,7 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
     value_tile_load<DT, D, UNR>(Vb, 0, n, vraw);
   }
   __syncthreads();
+  if constexpr (kPrio) __builtin_amdgcn_s_setprio(2);
 
   // softmax over the n kept slots (+ the new token)
   const int nt = n + with_new;
@@ -671,6 +681,7 @@ __global__ KVE_DECODE_ATTR void decode_fused_kernel(Shape sh, LayerCache c, Deco
 #pragma unroll
     for (int j = 0; j < Y::EPL; ++j) acc[j] = fmaf(w, f[j], acc[j]);
   }
+  if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
   if constexpr (Q4) stash_q4<D>(acc, red);
   else stash_groups<DT, D>(acc, red);
   __syncthreads();
