@@ -155,7 +155,7 @@ def generate_layer(w: Workload, layer: int = 0, device="cpu", seed: int = 0) -> 
         elif w.structure == "zipf_dir":
             dirs = _unit_dirs(gen, H, d, device)            # one per head
             weights = (torch.arange(N, device=device, dtype=torch.float64) + 1.0) ** -1.1
-            for b in range(Bt):
+            for b in range(Bt if n_pos > 0 else 0):         # sequences too short to carry one
                 pos = torch.multinomial(weights, n_pos, replacement=False, generator=gen)
                 k[b, :, pos, :] += 3.0 * dirs.unsqueeze(1)
         elif w.structure == "head_kinds":
