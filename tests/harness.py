@@ -40,7 +40,7 @@ def make_cache(w: Workload, inp: LayerInputs, policy=None, heavy=None, recent=No
 
 
 @dataclass
-class GpuRun:
+class GpuLayerRun:
     prefill_pos: np.ndarray      # [B, H, cap]
     prefill_cnt: np.ndarray
     prefill_S: np.ndarray
@@ -54,7 +54,7 @@ class GpuRun:
 
 
 def run_layer(kv: KVCache, inp: LayerInputs, layer: int = 0, steps: Optional[int] = None,
-              want_prompt_out: bool = False) -> GpuRun:
+              want_prompt_out: bool = False) -> GpuLayerRun:
     """Prefill + `steps` decode steps on the GPU; logs copied to the host."""
     P = inp.prompt_q.shape[2]
     T = inp.dec_q.shape[0] if steps is None else steps
@@ -74,11 +74,11 @@ def run_layer(kv: KVCache, inp: LayerInputs, layer: int = 0, steps: Optional[int
         kv.decode_step(layer, inp.dec_q[s], inp.dec_k[s], inp.dec_v[s], tid, out[s], ev[s])
     p1, c1, s1 = kv.kept_indices(layer)
     torch.cuda.synchronize()
-    return GpuRun(p0.numpy(), c0.numpy(), s0.numpy(), p1.cpu().numpy(), c1.cpu().numpy(), s1.cpu().numpy(),
+    return GpuLayerRun(p0.numpy(), c0.numpy(), s0.numpy(), p1.cpu().numpy(), c1.cpu().numpy(), s1.cpu().numpy(),
                   out.cpu().numpy(), ev.cpu().numpy(), po.cpu().numpy() if po is not None else None, choice)
 
 
-def gpu_unit(r: GpuRun, b: int, h: int) -> lockstep.GpuUnit:
+def gpu_unit(r: GpuLayerRun, b: int, h: int) -> lockstep.GpuUnit:
     n0, n1 = int(r.prefill_cnt[b, h]), int(r.final_cnt[b, h])
     return lockstep.GpuUnit(
         prefill_pos=r.prefill_pos[b, h, :n0].astype(np.int64), evicted=r.evicted[:, b, h].astype(np.int64),
@@ -87,7 +87,7 @@ def gpu_unit(r: GpuRun, b: int, h: int) -> lockstep.GpuUnit:
         prompt_out=r.prompt_out[b, h] if r.prompt_out is not None else None)
 
 
-def check_unit(w: Workload, inp_cpu: LayerInputs, r: GpuRun, b: int, h: int, policy=None, heavy=None,
+def check_unit(w: Workload, inp_cpu: LayerInputs, r: GpuLayerRun, b: int, h: int, policy=None, heavy=None,
                recent=None, scale=None, history=None) -> lockstep.UnitReport:
     pol, hv, rc = w.policy_table(0)
     p = pol[h] if policy is None else policy[h]
@@ -118,7 +118,7 @@ def check_unit(w: Workload, inp_cpu: LayerInputs, r: GpuRun, b: int, h: int, pol
     return rep
 
 
-def check_all(w: Workload, inp_cpu: LayerInputs, r: GpuRun, units: Optional[Iterable[Tuple[int, int]]] = None,
+def check_all(w: Workload, inp_cpu: LayerInputs, r: GpuLayerRun, units: Optional[Iterable[Tuple[int, int]]] = None,
               **kw) -> lockstep.UnitReport:
     total = lockstep.UnitReport()
     if units is None:
@@ -128,7 +128,7 @@ def check_all(w: Workload, inp_cpu: LayerInputs, r: GpuRun, units: Optional[Iter
     return total
 
 
-def check_invariants(w: Workload, r: GpuRun, P: int, policy=None, heavy=None, recent=None,
+def check_invariants(w: Workload, r: GpuLayerRun, P: int, policy=None, heavy=None, recent=None,
                      history=None) -> List[str]:
     """Properties that hold at any size: budgets, recent windows, unique in-range positions."""
     pol, hv, rc = w.policy_table(0)
