@@ -31,19 +31,25 @@ BASE = {"h2o": "opt30b_decode_h2o", "h2o16": "opt6.7b_layer_h2o", "persist": "op
 FAMILIES = ["h2o", "h2o16", "persist", "fastgen", "adaptive", "hash", "mixed"]
 
 
-def draw(rng):
-    """One random configuration: (family, workload, policy, heavy, recent, history, path, chunk)."""
+def draw(rng, medium=False):
+    """One random configuration: (family, workload, policy, heavy, recent, history, path, chunk).
+    medium: prompts of 700 to 3,999 tokens, budgets up to 6,000 slots, few steps."""
     fam = str(rng.choice(FAMILIES))
     q4 = bool(rng.random() < 0.3) and fam in ("h2o", "h2o16", "persist", "hash", "mixed")
-    P, T = int(rng.integers(1, 700)), int(rng.integers(1, 70))
-    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 5))
+    if medium:
+        P, T = int(rng.integers(700, 4000)), int(rng.integers(1, 20))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    else:
+        P, T = int(rng.integers(1, 700)), int(rng.integers(1, 70))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 5))
+    hmax, rmax, bmax = (1500, 700, 6000) if medium else (90, 70, 1300)
     w = configs.scaled(BASE["h2o" if fam == "mixed" else fam], batch=B, heads=H, prompt=P, steps=T)
     w = dataclasses.replace(w, head_dim=int(rng.choice([64, 128])), dtype=str(rng.choice(["f32", "f16", "bf16"])),
                             cache_bits=4 if q4 else 0)
     ctx = P + T
 
     def hr():
-        h, r = int(rng.integers(0, 90)), int(rng.integers(0, 70))
+        h, r = int(rng.integers(0, hmax)), int(rng.integers(0, rmax))
         while h + r > ctx:
             h, r = h // 2, r // 2
         return h, r
@@ -68,7 +74,7 @@ def draw(rng):
                                 profile_rows=int(rng.integers(1, 64)))
     elif fam == "hash":
         pol = [HASH] * H
-        hv = [int(rng.integers(1, min(ctx, 1300) + 1)) for _ in range(H)]
+        hv = [int(rng.integers(1, min(ctx, bmax) + 1)) for _ in range(H)]
         rc = [0] * H
         w = dataclasses.replace(w, sketch_bits=int(rng.choice([16, 32, 64])))
     else:
@@ -77,7 +83,7 @@ def draw(rng):
         for p in pol:
             h, r = hr()
             if p == HASH:
-                hv.append(int(rng.integers(1, min(ctx, 900) + 1))); rc.append(0)
+                hv.append(int(rng.integers(1, min(ctx, bmax) + 1))); rc.append(0)
             elif p in (H2O, PERSIST):
                 hv.append(h); rc.append(r)
             elif p == LOCAL:
@@ -90,13 +96,14 @@ def draw(rng):
     return fam, w, pol, hv, rc, hist, path, chunk
 
 
-def test_random_configurations():
-    rng = np.random.default_rng(20261203)
+def run_random(seed, cases, medium):
+    """Runs `cases` draws in lockstep with the oracle; returns (checked, rejected)."""
+    rng = np.random.default_rng(seed)
     ran = rejected = 0
     saved = {k: os.environ.get(k) for k in ("KVEVICT_SPLIT_ABOVE", "KVEVICT_SPLIT_CHUNK")}
     try:
-        for i in range(160):
-            fam, w, pol, hv, rc, hist, path, chunk = draw(rng)
+        for i in range(cases):
+            fam, w, pol, hv, rc, hist, path, chunk = draw(rng, medium)
             seed = int(rng.integers(0, 1 << 30))
             if path == "split":
                 os.environ["KVEVICT_SPLIT_ABOVE"] = "0"
@@ -133,4 +140,17 @@ def test_random_configurations():
             else:
                 os.environ[k] = v
     print(f"\n[random] {ran} configurations checked, {rejected} rejected by the library", flush=True)
+    return ran, rejected
+
+
+def test_random_configurations():
+    ran, _ = run_random(20261203, 160, medium=False)
     assert ran >= 120
+
+
+def test_random_configurations_medium():
+    """Longer prompts and larger budgets: HashEvict budgets past the register
+    replay's 1,024-slot step, split layers of many chunks, FastGen FULL heads
+    holding thousands of positions."""
+    ran, _ = run_random(4031, 24, medium=True)
+    assert ran >= 16
