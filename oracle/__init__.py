@@ -47,7 +47,8 @@ Sources (cited per function):
 Parity pins: every function is pinned by a CPU test against a textbook
 routine, a closed form, an invariant or brute force (tests/test_oracle_*.py).
 Parity unpinned: the H2O score trajectory for generic inputs beyond those
-invariants and brute-force checks -- the pages print no worked example; the
+invariants, the brute-force checks and one trajectory worked by hand in exact
+fractions (distinct keys, two evictions) -- the pages print no worked example; the
 persistence rule itself is a reading of a one-sentence hypothesis, so its
 pins (closed forms on constructed inputs, invariants, a replay of recorded
 weights) check the oracle against that reading, not against the page; the
