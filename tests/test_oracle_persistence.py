@@ -1,9 +1,10 @@
 """Pins of the persistence-count oracle (CPU only).
 
 Closed forms on constructed inputs (identical keys reduce the rule to a
-sliding window; one dominant key is kept forever), invariants on random
-inputs, and a replay of the recorded per-step weights that rebuilds every
-history from the definition of a pivotal step.
+sliding window; one dominant key is kept forever), two trajectories worked by
+hand in exact fractions, invariants on random inputs, and a replay of the
+recorded per-step weights that rebuilds every history from the definition of
+a pivotal step.
 """
 
 import numpy as np
@@ -156,3 +157,50 @@ def test_pivotal_band_and_window_checks():
     with pytest.raises(ValueError):
         persistence.window_mask(65)
     assert persistence.window_mask(64) == (1 << 64) - 1
+
+
+@pytest.mark.parametrize("window", [4, 1])
+def test_trajectory_worked_by_hand(window):
+    """Two trajectories worked by hand (Scissorhands page, Abstract: pivotal
+    tokens are the ones kept; the reading: pivotal = weight at least 1 / |A|,
+    count over the last `window` steps, lowest count evicted, oldest first).
+
+    d = 1, scale 1, keys k = (0, 1, 0, 2 | 0, 1), values v_j = j + 1, prompt
+    P = 4, one heavy slot and one recent slot.  Query i has e^q = 2 except
+    row 3 (e^q = 3), so every weight is a ratio of powers of that base:
+
+      prompt rows   [1], (1, 2)/3, (1, 2, 1)/4, (1, 3, 1, 9)/14
+      pivotal       row 0: token 0; row 1: token 1; row 2: token 1; row 3: token 3
+
+    window 4: histories 1000, 0110, 0000, 0001 (bit 3 = row 0); counts
+      (1, 2, 0, 1); keep {3} (recent) + {1}.  Step 4 attends {1, 3, 4} with
+      (2, 4, 1)/7: token 3 pivotal; histories 1100, 0011, 0000, so 1 and 3
+      tie at 2 and the older, 1, leaves; out = (2*2 + 4*4 + 1*5)/7 = 25/7.
+      Step 5 attends {3, 4, 5} with (4, 1, 2)/7: 3 pivotal; counts 3, 0 (4
+      is the only other candidate) so 4 leaves; out = (16 + 5 + 12)/7 = 33/7.
+    window 1: only row 3 counts, so every earlier token has count 0 and the
+      newer-first order keeps 2: {2, 3}.  Step 4 attends {2, 3, 4} with
+      (1, 4, 1)/6: counts 0, 1 among the candidates 2, 3, so 2 leaves;
+      out = (3 + 16 + 5)/6 = 4.  Step 5 as above: 4 leaves, out = 33/7.
+
+    A misread tie order (newest first on equal counts at decode), window
+    (counting all steps) or prefill tie order changes a kept set or a victim.
+    """
+    lnb = np.log([2.0, 2.0, 2.0, 3.0, 2.0, 2.0])
+    k = np.array([0.0, 1.0, 0.0, 2.0, 0.0, 1.0])
+    Q, K, V = lnb[:, None], k[:, None], (np.arange(6) + 1.0)[:, None]
+    tr = persistence.run_unit(Q, K, V, P=4, heavy=1, recent=1, window=window, scale=1.0)
+    if window == 4:
+        assert [int(h) for h in tr.prompt_hist] == [0b1000, 0b0110, 0b0000, 0b0001]
+        assert sorted(tr.prefill_kept.tolist()) == [1, 3]
+        assert tr.evicted.tolist() == [1, 4]
+        np.testing.assert_allclose(tr.out[:, 0], [25 / 7, 33 / 7], rtol=1e-13)
+        final = dict(zip(tr.final.pos.tolist(), (int(h) for h in tr.final.hist)))
+        assert final == {3: 0b0111, 5: 0b0000}
+    else:
+        assert [int(h) for h in tr.prompt_hist] == [0, 0, 0, 1]
+        assert sorted(tr.prefill_kept.tolist()) == [2, 3]
+        assert tr.evicted.tolist() == [2, 4]
+        np.testing.assert_allclose(tr.out[:, 0], [4.0, 33 / 7], rtol=1e-13)
+        final = dict(zip(tr.final.pos.tolist(), (int(h) for h in tr.final.hist)))
+        assert final == {3: 1, 5: 0}
