@@ -517,6 +517,25 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
   const int i_first = BITS ? max(kb * kBlk, wlo) & ~(kTile - 1) : kb * kBlk;
   auto thr = [&](int i) { return (float)(-log2((double)(i + 1))); };
   uint64_t bits[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  // float32 sums of this lane's weights over two tiles at a time (8 terms),
+  // then added into the float64 column sums
+  float part[2][4], pm[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[mb][r] = pm[mb][r] = 0.f;
+  int held = 0;                                 // tiles summed in part since the last flush
+  auto flush = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        cs[mb][r] += (double)part[mb][r];
+        if (MODE == 2) ms[mb][r] += (double)pm[mb][r];
+        part[mb][r] = pm[mb][r] = 0.f;
+      }
+    held = 0;
+  };
   TileRegs<D> nxt;
   float la = 0.f, lb = 0.f;                     // the next tile's lse pair, as loaded
   load_tile<D>(nxt, qbase, i_first, P);
@@ -540,11 +559,6 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
     }
     if (i0 + kTile - 1 >= j0) {                 // some query of the tile follows a key of the wave
       const bool edge = i0 < j0 + 32 || i0 + kTile > P;
-      float part[2][4], pm[2][4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part[mb][r] = pm[mb][r] = 0.f;
       const bool in_rows = MODE == 2 && i0 + kTile > wlo;   // the tile reaches the profiled rows
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
@@ -563,13 +577,10 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
           colsum_fold(acc, c2, lh, Lf[buf][nb * 16 + c16], part);
         }
       }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          cs[mb][r] += (double)part[mb][r];
-          if (MODE == 2) ms[mb][r] += (double)pm[mb][r];
-        }
+      if constexpr (!BITS) {
+        held = __builtin_amdgcn_readfirstlane(held + 1);   // the same in every lane of the wave
+        if (held == 2) flush();
+      }
     }
     if (more) {
       store_tile<D>(nxt, Qs[buf ^ 1]);          // that buffer was last read before the previous barrier
@@ -584,6 +595,7 @@ void colsum_mfma_kernel(Shape sh, int P, UnitList ul, const void* q, const void*
     }
     __syncthreads();
   }
+  if (!BITS && held) flush();
   if (BITS) {
     // the 16 lanes that share a key hold the same bits
 #pragma unroll
